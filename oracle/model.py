@@ -1,0 +1,268 @@
+"""Plain float64 forward pass of the looped weight-shared transformer.
+
+Structure ("TinyLoop Framework" intro page, opening list): embed tokens, run a
+small number of pre-blocks, reuse ONE shared loop block L times, then
+normalise and project to the output head. L is a runtime argument ("What
+Makes It Different": loop count is a runtime knob; weight memory is tied to
+unique blocks, not effective depth). Every pre-block and every loop iteration
+is an effective layer with its own KV cache ("Performance and Memory" page,
+INT8-KV table: max_seq 2048 over 10 layers at 2 pre-blocks and L=8).
+
+Block ("Current Status" page, model-architecture table): pre-norm RMSNorm,
+rotary position embedding on q and k, full multi-head causal attention, and a
+gated SiLU MLP (GeLU and post-norm are opt-in there, so not used); the
+residual stream is FP32 by default (core-inference table, FP16 residual is
+opt-in) and is carried here in float64.
+
+Float16 activation cast points (a reading: FP16 activations with FP32
+residual and accumulation): the normed block inputs, Q/K/V after RoPE, the
+attention output and the gated-MLP product, and the final normed vector before
+the head. With casts=False every cast is the identity (the pure high-precision
+variant used to compare against a library transformer).
+
+Readings where the pages are silent: RMSNorm eps 1e-5; rotate-half RoPE
+pairing dimension i with i + hd/2, theta_i = base^(-2i/hd), 0-based absolute
+positions; attention scale 1/sqrt(hd) with the causal mask including the
+diagonal; cache layer of pre-block b is b and of loop iteration i is
+n_pre + i; logits are float64 and argmax ties go to the lowest index.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .int4 import dequantize
+from .kvquant import kv_quantize, kv_dequantize
+
+_LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def fp16(a):
+    """Round to nearest-even binary16 and return float64 (direct, no float32 step)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _identity(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def rmsnorm(x, gamma, eps):
+    """gamma_i * x_i / sqrt(mean(x^2) + eps) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def rope_cos_sin(positions, head_dim, base):
+    """cos/sin [n][hd/2] of angle pos * base^(-2i/hd), in float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * i / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x, cos, sin):
+    """Rotate each pair (x_i, x_{i+hd/2}) of x [n][H][hd] by its angle."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attention(Q, K, V, q_pos):
+    """Causal softmax attention per head.
+
+    Q [n][H][hd]; K, V [S][H][hd] hold cache rows 0..S-1; query m sees keys
+    j <= q_pos[m]. Scores are scaled by 1/sqrt(hd); softmax subtracts the row
+    maximum. Returns [n][H][hd].
+    """
+    n, H, hd = Q.shape
+    S = K.shape[0]
+    Qh = np.ascontiguousarray(Q.transpose(1, 0, 2))          # H n hd
+    Kh = np.ascontiguousarray(K.transpose(1, 2, 0))          # H hd S
+    Vh = np.ascontiguousarray(V.transpose(1, 0, 2))          # H S hd
+    scores = np.matmul(Qh, Kh) / math.sqrt(hd)               # H n S
+    masked = np.arange(S)[None, :] > np.asarray(q_pos)[:, None]
+    scores[:, masked] = -np.inf
+    scores -= scores.max(axis=-1, keepdims=True)
+    p = np.exp(scores)
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.matmul(p, Vh).transpose(1, 0, 2)               # n H hd
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+class OracleModel:
+    """Dequantized float64 weights of the pre-blocks, the loop block, embed and head."""
+
+    def __init__(self, weights: dict):
+        s = weights["shape"]
+        self.shape = s
+        self.embed = np.asarray(weights["embed"], dtype=np.float16)
+        self.pre = [self._block(b) for b in weights["pre"]]
+        self.loop = self._block(weights["loop"])
+        self.final_norm = np.asarray(weights["final_norm"], dtype=np.float16).astype(np.float64)
+        self.head16 = np.asarray(weights["head"], dtype=np.float16)
+        self._head64 = None
+
+    def _block(self, b):
+        g = self.shape.group_size
+        out = {name: dequantize(b[name]["qweight"], b[name]["scales"], g) for name in _LINEARS}
+        out["attn_norm"] = np.asarray(b["attn_norm"], dtype=np.float16).astype(np.float64)
+        out["mlp_norm"] = np.asarray(b["mlp_norm"], dtype=np.float16).astype(np.float64)
+        return out
+
+    @property
+    def head64(self):
+        if self._head64 is None:
+            self._head64 = self.head16.astype(np.float64)
+        return self._head64
+
+
+class Cache:
+    """KV cache of one lane: one K and one V store per effective layer.
+
+    Rows hold the values attention reads: the FP16 K/V, or in INT8 mode the
+    dequantized f32(q) * f32(s); the raw codes and scales are kept as well.
+    depth[t] is the number of effective layers token t was computed through.
+    """
+
+    def __init__(self, shape, max_seq, kv_int8=False):
+        self.shape = shape
+        self.max_seq = max_seq
+        self.kv_int8 = kv_int8
+        self.length = 0
+        self.k, self.v = {}, {}
+        self.kq, self.ks, self.vq, self.vs = {}, {}, {}, {}
+        self.depth = np.zeros(max_seq, dtype=np.int64)
+
+    def _store(self, d, layer, dtype, tail=()):
+        if layer not in d:
+            s = self.shape
+            d[layer] = np.zeros((self.max_seq, s.n_heads) + tail, dtype=dtype)
+        return d[layer]
+
+    def write(self, layer, pos, K, V, raw=None):
+        s = self.shape
+        self._store(self.k, layer, np.float64, (s.head_dim,))[pos] = K
+        self._store(self.v, layer, np.float64, (s.head_dim,))[pos] = V
+        if raw is not None:
+            kq, ks, vq, vs = raw
+            self._store(self.kq, layer, np.int8, (s.head_dim,))[pos] = kq
+            self._store(self.ks, layer, np.float16)[pos] = ks
+            self._store(self.vq, layer, np.int8, (s.head_dim,))[pos] = vq
+            self._store(self.vs, layer, np.float16)[pos] = vs
+
+    def read(self, layer, upto):
+        return self.k[layer][:upto], self.v[layer][:upto]
+
+
+def _block_forward(x, B, cache, layer, positions, s, casts):
+    """One pre-norm block on residual rows x [n][d] at absolute positions."""
+    c = fp16 if casts else _identity
+    n = x.shape[0]
+    H, hd = s.n_heads, s.head_dim
+    h = c(rmsnorm(x, B["attn_norm"], s.rms_eps))
+    q = (h @ B["wq"].T).reshape(n, H, hd)
+    k = (h @ B["wk"].T).reshape(n, H, hd)
+    v = (h @ B["wv"].T).reshape(n, H, hd)
+    cos, sin = rope_cos_sin(positions, hd, s.rope_base)
+    Q, K, V = c(apply_rope(q, cos, sin)), c(apply_rope(k, cos, sin)), c(v)
+    if cache.kv_int8:
+        if not casts:
+            raise ValueError("INT8 KV quantizes FP16 rows; it needs the FP16 cast points")
+        kq, ks = kv_quantize(K.astype(np.float16))
+        vq, vs = kv_quantize(V.astype(np.float16))
+        cache.write(layer, positions, kv_dequantize(kq, ks), kv_dequantize(vq, vs),
+                    raw=(kq, ks, vq, vs))
+    else:
+        cache.write(layer, positions, K, V)
+    Kall, Vall = cache.read(layer, int(positions[-1]) + 1)
+    O = c(attention(Q, Kall, Vall, positions)).reshape(n, H * hd)
+    x = x + O @ B["wo"].T
+    h2 = c(rmsnorm(x, B["mlp_norm"], s.rms_eps))
+    a = c(silu(h2 @ B["w_gate"].T) * (h2 @ B["w_up"].T))
+    return x + a @ B["w_down"].T
+
+
+def head_logits(model, x_rows, casts=True):
+    """Final RMSNorm, cast, and the head projection: [m][d] -> [m][V] float64."""
+    c = fp16 if casts else _identity
+    z = c(rmsnorm(np.atleast_2d(x_rows), model.final_norm, model.shape.rms_eps))
+    return z @ model.head64.T
+
+
+def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False,
+            max_seq=None, kv_int8=False):
+    """Append `tokens` to a lane at its current length and run all n_pre + L layers.
+
+    Returns a dict with the final residual rows 'hidden' [n][d] (before the
+    final norm), 'logits' (last position [V], all positions [n][V], or None),
+    the 'cache' and, if trace, 'trace': the residual after every effective layer.
+    """
+    s = model.shape
+    tokens = np.asarray(tokens, dtype=np.int64)
+    n = tokens.shape[0]
+    if L < 1:
+        raise ValueError("L must be >= 1")
+    if cache is None:
+        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8)
+    p0 = cache.length
+    if p0 + n > cache.max_seq:
+        raise ValueError("sequence exceeds max_seq")
+    if p0 > 0 and s.n_pre + L > int(cache.depth[:p0].min()):
+        raise ValueError("earlier tokens were not computed to this depth")
+    positions = p0 + np.arange(n)
+    x = model.embed[tokens].astype(np.float64)
+    states = []
+    for b in range(s.n_pre):
+        x = _block_forward(x, model.pre[b], cache, b, positions, s, casts)
+        states.append(x)
+    for i in range(L):  # the same loop-block weights on every iteration
+        x = _block_forward(x, model.loop, cache, s.n_pre + i, positions, s, casts)
+        states.append(x)
+    cache.length = p0 + n
+    cache.depth[positions] = s.n_pre + L
+    out = {"hidden": x, "cache": cache, "logits": None}
+    if logits == "last":
+        out["logits"] = head_logits(model, x[-1:], casts)[0]
+    elif logits == "all":
+        out["logits"] = head_logits(model, x, casts)
+    if trace:
+        out["trace"] = states
+    return out
+
+
+def decode_step(model, cache, token, L, casts=True):
+    """Cached decode: one new token at position cache.length; next-token logits [V]."""
+    r = forward(model, [int(token)], L, cache=cache, casts=casts, logits="last")
+    return r["logits"], r["hidden"][0]
+
+
+def forward_uncached(model, tokens, L, casts=True, kv_int8=False):
+    """Uncached recompute of the whole sequence; logits of the last position."""
+    return forward(model, tokens, L, cache=None, casts=casts, logits="last",
+                   kv_int8=kv_int8)
+
+
+def generate_greedy(model, prompt, L, steps, max_seq, kv_int8=False, casts=True):
+    """Prefill the prompt, then `steps` cached decode steps, greedy (argmax).
+
+    Returns (tokens generated: steps + 1 of them, list of logits per call:
+    the prefill's last position then one per decode step, the cache).
+    """
+    r = forward(model, prompt, L, cache=Cache(model.shape, max_seq, kv_int8), casts=casts)
+    cache = r["cache"]
+    logits = [r["logits"]]
+    toks = [int(np.argmax(r["logits"]))]
+    for _ in range(steps):
+        lg, _ = decode_step(model, cache, toks[-1], L, casts)
+        logits.append(lg)
+        toks.append(int(np.argmax(lg)))
+    return toks, logits, cache

@@ -1,0 +1,209 @@
+/*
+ * tl.h -- C ABI of the looped weight-shared transformer forward pass on
+ * MI355X (gfx950).
+ *
+ * The model family (TinyLoop docs, "TinyLoop Framework" intro page, opening
+ * list): embed tokens, run a few pre-blocks, reuse ONE shared loop block L
+ * times, then final RMSNorm and the output head. L is a per-lane runtime
+ * argument (same page, "What Makes It Different": loop count is a runtime
+ * knob; weight memory is tied to unique blocks, not effective depth). Every
+ * pre-block and every loop iteration is an "effective layer" with its own KV
+ * cache ("Performance and Memory" page, INT8-KV table: 10 layers at 2
+ * pre-blocks and L=8). Cached decode is the default path and an uncached
+ * recompute is its parity reference ("Performance and Memory" page, "Key
+ * Runtime Switches", TINYLOOP_DISABLE_KV_CACHE).
+ *
+ * Conventions for every call:
+ *  - Device pointers ("d_" prefix) are caller-owned device memory; host
+ *    pointers ("h_" prefix, and every struct passed by pointer) are host
+ *    memory read during the call only. The library never allocates or frees
+ *    device memory: workspace sizes come from the *_bytes queries and the
+ *    caller passes the buffers in, aligned to 256 bytes.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it and the call returns without synchronising, except tl_create,
+ *    which also uploads small tables and synchronises the stream once.
+ *  - Every call returns a tl_status. Argument and state errors are detected
+ *    on the host before anything is enqueued and leave all state unchanged;
+ *    a failing HIP call returns TL_E_HIP. tl_last_error() gives a message for
+ *    the last failure on the calling thread. No C++ exception crosses the ABI.
+ *  - Token ids are not range-checked on the device: an id outside
+ *    [0, vocab) is the caller's error.
+ *  - A tl_ctx is not thread-safe. Identical calls give bit-identical results;
+ *    a lane's results do not depend on which other lanes run in the same
+ *    decode step.
+ *  - FP16 values are passed as uint16_t bit patterns (IEEE binary16).
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TL_OK = 0,
+  TL_E_INVAL = 1,        /* bad pointer, alignment, shape or lane index */
+  TL_E_RANGE = 2,        /* L, token count or sequence length out of range */
+  TL_E_STATE = 3,        /* call not valid in the lane's current state */
+  TL_E_HIP = 4,          /* a HIP runtime call failed */
+  TL_E_UNSUPPORTED = 5   /* valid request this build does not implement */
+} tl_status;
+
+typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1 } tl_kv_dtype;
+
+/* Model shape and runtime limits. */
+typedef struct {
+  int32_t vocab, d_model, n_heads, head_dim, ffn_dim;
+  int32_t n_pre;        /* number of pre-blocks (distinct weights each) */
+  int32_t group_size;   /* INT4 scale group along K; must be 128 */
+  float rope_base;      /* rotary base, e.g. 10000 */
+  float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
+  int32_t max_seq;      /* KV rows per lane and effective layer */
+  int32_t max_loops;    /* largest L; KV layers per lane = n_pre + max_loops */
+  int32_t n_lanes;      /* independent sequences (each with its own L and KV) */
+  int32_t kv_dtype;     /* tl_kv_dtype */
+  int32_t max_tokens;   /* largest token count of one tl_prefill call */
+} tl_config;
+
+/* One INT4 linear layer in the canonical layout (device pointers):
+ *   qweight uint32 [N][K/8]: element k of row n is nibble k%8 of word k/8,
+ *           least significant nibble first, two's complement in [-8, 7];
+ *   scales  fp16   [N][ceil(K/group_size)]; W[n][k] = q * scales[n][k/g]. */
+typedef struct {
+  const uint32_t* qweight;
+  const uint16_t* scales;
+} tl_qlinear;
+
+/* One transformer block: pre-norm attention then pre-norm SwiGLU MLP.
+ * wq, wk, wv, wo: N = K = d_model; w_gate, w_up: N = ffn, K = d_model;
+ * w_down: N = d_model, K = ffn. Norm gains are fp16 [d_model]. */
+typedef struct {
+  const uint16_t* attn_norm;
+  tl_qlinear wq, wk, wv, wo;
+  const uint16_t* mlp_norm;
+  tl_qlinear w_gate, w_up, w_down;
+} tl_block;
+
+typedef struct {
+  const uint16_t* embed;       /* fp16 [vocab][d_model], used in place */
+  const tl_block* pre;         /* host array of n_pre blocks */
+  tl_block loop;               /* the shared loop block */
+  const uint16_t* final_norm;  /* fp16 [d_model] */
+  const uint16_t* head;        /* fp16 [vocab][d_model], used in place */
+} tl_weights;
+
+typedef struct tl_ctx tl_ctx;
+
+/* ---- sizes ------------------------------------------------------------- */
+
+/* Repacked block weights, norms and RoPE table. Independent of max_loops:
+ * the loop block is stored once however many times it runs. */
+size_t tl_weights_ws_bytes(const tl_config* cfg);
+/* K and V of one lane for one effective layer:
+ *   FP16: 2 * max_seq * n_heads * head_dim * 2
+ *   INT8: 2 * max_seq * n_heads * (head_dim + 2)   (codes + one fp16 scale
+ *         per token and head, "Performance and Memory" page, INT8-KV). */
+size_t tl_kv_layer_bytes(const tl_config* cfg);
+/* n_lanes * (n_pre + max_loops) * tl_kv_layer_bytes. */
+size_t tl_kv_bytes(const tl_config* cfg);
+/* Activations and scratch for calls of up to max_tokens tokens. */
+size_t tl_act_ws_bytes(const tl_config* cfg);
+
+/* ---- context ----------------------------------------------------------- */
+
+/* Validates cfg and pointers, repacks every INT4 linear of the pre-blocks and
+ * the loop block into d_weights_ws (so the canonical buffers may be freed
+ * afterwards) and clears the per-lane state. embed, head and the norm gains
+ * are read in place and must outlive the context. d_kv holds the caches of
+ * all lanes; d_act_ws the activations. Every lane starts empty with L = 1.
+ * Errors: TL_E_INVAL (null/misaligned pointer, head_dim not 64 or 128,
+ * d_model != n_heads*head_dim, any dimension not a multiple of 16,
+ * group_size != 128), TL_E_RANGE (max_loops outside 1..64, n_lanes outside
+ * 1..8, max_seq or max_tokens < 1), TL_E_HIP. */
+tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_ws, void* d_kv,
+                    void* d_act_ws, void* stream, tl_ctx** out);
+tl_status tl_destroy(tl_ctx* ctx);
+
+/* Loop count of one lane (lane = -1: every lane). 1 <= loops <= max_loops.
+ * A lane holding cached tokens may only run as deep as every cached token
+ * was computed (its KV for deeper layers does not exist): TL_E_STATE if
+ * n_pre + loops exceeds that depth. Host-only; enqueues nothing. */
+tl_status tl_set_loops(tl_ctx* ctx, int32_t lane, int32_t loops);
+tl_status tl_get_loops(const tl_ctx* ctx, int32_t lane, int32_t* loops);
+/* Empties a lane (lane = -1: every lane); its L is kept. Host-only. */
+tl_status tl_reset(tl_ctx* ctx, int32_t lane);
+/* Cached tokens of a lane, or -1 for a bad lane index. */
+int32_t tl_length(const tl_ctx* ctx, int32_t lane);
+
+/* ---- forward ----------------------------------------------------------- */
+
+/* Appends n tokens (d_tokens int32 [n]) to `lane` at its current length p0
+ * and runs all n_pre + L effective layers over them: embed, per layer
+ * RMSNorm -> W4 QKV GEMM -> RoPE -> KV write (FP16 or INT8) -> causal
+ * attention over cache rows 0..p0+n-1 -> W4 O GEMM + residual -> RMSNorm ->
+ * W4 gate/up GEMM + SwiGLU -> W4 down GEMM + residual.
+ * Optional outputs (NULL to skip):
+ *   d_hidden float [n][d_model]: final residual of every position (before
+ *            the final norm);
+ *   d_logits float [vocab]: head logits of the last position;
+ *   d_next   int32 [1]: argmax of those logits (ties -> lowest index).
+ * With d_logits and d_next both NULL the head is not run ("no logits
+ * materialization", "Performance and Memory" page, benchmark shape).
+ * Errors: TL_E_INVAL (bad lane or pointer), TL_E_RANGE (n < 1,
+ * n > max_tokens, p0 + n > max_seq), TL_E_STATE (lane's L deeper than its
+ * cached tokens). */
+tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t n, float* d_hidden,
+                     float* d_logits, int32_t* d_next, void* stream);
+
+/* One cached decode step for every lane with h_active[lane] != 0 (h_active
+ * NULL: all lanes). Consumes d_tokens[lane] (int32 [n_lanes], entries of
+ * inactive lanes ignored) at position tl_length(lane), runs each active lane
+ * through its own n_pre + L layers (loop iteration i runs only the lanes with
+ * L > i, "Current Status" page, L-aware batching with per_lane_loops), then
+ * final norm, head and argmax. Outputs, indexed by lane, NULL to skip:
+ *   d_hidden float [n_lanes][d_model], d_logits float [n_lanes][vocab],
+ *   d_next int32 [n_lanes]. Rows of inactive lanes are left untouched.
+ * Errors: TL_E_INVAL, TL_E_RANGE (a lane at max_seq), TL_E_STATE (an active
+ * lane with no cached token, or deeper than its cache). */
+tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_active,
+                         float* d_hidden, float* d_logits, int32_t* d_next, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* tl_last_error(void);
+
+/* ---- single kernels ----------------------------------------------------
+ * The same kernels the forward pass runs, exposed for per-kernel parity
+ * tests and bandwidth/throughput measurement. */
+
+/* Bytes of one linear in the library's packed layout: 16-row x 128-column
+ * tiles of 1 KiB (MFMA fragment order, offset-binary nibbles, K padded with
+ * zeros to a multiple of 128) followed by fp16 scales [N/16][ceil(K/128)][16]. */
+size_t tl_qlinear_packed_bytes(int32_t N, int32_t K);
+/* Repacks a canonical linear (N % 16 == 0, K % 8 == 0) into d_packed. */
+tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, int32_t N, int32_t K,
+                          void* d_packed, void* stream);
+/* Exact inverse view of the packed layout: d_q int8 [N][K] receives the
+ * signed 4-bit values, d_scales fp16 [N][ceil(K/128)] the scales. Used to
+ * check the repack bit for bit. */
+tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* d_q,
+                            uint16_t* d_scales, void* stream);
+/* C[m][n] = sum_k A[m][k] * W[n][k] over a packed linear, fp32 out [M][N].
+ * A is fp16 [M][K] row-major. M >= 1 (M <= 16 runs the decode GEMV kernel,
+ * larger M the prefill GEMM kernel); fp32 accumulation. */
+tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M,
+                       float* d_C, void* stream);
+/* Per-row symmetric INT8 quantizer of the KV cache (bit-exact definition:
+ * amax = max|x|; s = fp16(amax / 127) with a correctly rounded float32
+ * division; q = clamp(rint_half_even(x / float(s)), -127, 127), 0 if s == 0).
+ * d_x fp16 [rows][hd] -> d_q int8 [rows][hd], d_s fp16 [rows]. hd <= 128,
+ * hd % 2 == 0. */
+tl_status tl_kv_quantize_rows(const uint16_t* d_x, int32_t rows, int32_t hd, int8_t* d_q,
+                              uint16_t* d_s, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TL_H */

@@ -1,0 +1,502 @@
+// Host runtime of the C ABI declared in include/tl.h: argument and state
+// validation, workspace carving, weight repacking at create time, and the
+// layer sequence of prefill and cached decode.
+//
+// The forward pass follows the TinyLoop docs ("TinyLoop Framework" intro
+// page): embed, n_pre distinct pre-blocks, then ONE loop block applied L
+// times, then final norm and head. Effective layer l uses pre-block l for
+// l < n_pre and the loop block otherwise, and writes KV cache layer l.
+// In a decode step the lanes are ordered by descending L so that the lanes
+// still running at loop iteration i are always the first rows of the batch
+// (the "L-aware batching" of the "Current Status" page: each lane keeps its
+// own depth).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tl.h"
+#include "tl_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tl_status fail(tl_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define TL_HIP(expr)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(TL_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct BlockW {
+  tl::Packed qkv, o, gu, down;
+  const uint16_t* attn_norm;
+  const uint16_t* mlp_norm;
+};
+
+bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
+  *st = TL_E_INVAL;
+  if (!c) return *why = "cfg is NULL", false;
+  if (c->head_dim != 64 && c->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
+  if (c->n_heads < 1 || c->d_model != c->n_heads * c->head_dim) return *why = "d_model != n_heads*head_dim", false;
+  if (c->d_model % 32 || c->ffn_dim < 16 || c->ffn_dim % 16) return *why = "d_model % 32 or ffn_dim % 16 != 0", false;
+  if (c->group_size != 128) return *why = "group_size must be 128", false;
+  if (c->vocab < 1 || c->n_pre < 0) return *why = "vocab < 1 or n_pre < 0", false;
+  if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8) return *why = "bad kv_dtype", false;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return *why = "bad rms_eps or rope_base", false;
+  *st = TL_E_RANGE;
+  if (c->max_loops < 1 || c->max_loops > 64) return *why = "max_loops must be in 1..64", false;
+  if (c->n_lanes < 1 || c->n_lanes > 8) return *why = "n_lanes must be in 1..8", false;
+  if (c->max_seq < 1 || c->max_tokens < 1) return *why = "max_seq and max_tokens must be >= 1", false;
+  *st = TL_OK;
+  return true;
+}
+
+size_t block_bytes(const tl_config* c) {
+  const int d = c->d_model, f = c->ffn_dim;
+  return al256(tl::packed_bytes(3 * d, d)) + al256(tl::packed_bytes(d, d)) + al256(tl::packed_bytes(2 * f, d)) +
+         al256(tl::packed_bytes(d, f));
+}
+size_t rope_bytes(const tl_config* c) { return al256((size_t)2 * c->max_seq * (c->head_dim / 2) * 4); }
+
+int tokens_cap(const tl_config* c) { return std::max(c->max_tokens, c->n_lanes); }
+
+struct ActLayout {
+  size_t x, h, qkv, q, o, a, part, logits, total;
+};
+ActLayout act_layout(const tl_config* c) {
+  const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
+  ActLayout L;
+  size_t off = 0;
+  L.x = off; off += al256(T * d * 4);
+  L.h = off; off += al256(T * d * 2);
+  L.qkv = off; off += al256(T * 3 * d * 4);
+  L.q = off; off += al256(T * d * 2);
+  L.o = off; off += al256(T * d * 2);
+  L.a = off; off += al256(T * f * 2);
+  L.part = off; off += al256(tl::attn_decode_scratch_floats(c->n_lanes, c->n_heads, c->head_dim, c->max_seq) * 4);
+  L.logits = off; off += al256((size_t)c->n_lanes * c->vocab * 4);
+  L.total = off;
+  return L;
+}
+
+// The GEMV kernel keeps all M activation rows of K in LDS.
+bool gemv_fits(int M, int K) {
+  const size_t G = (K + 127) / 128;
+  const size_t lds = (((size_t)M * (G * 128 + 8) * 2 + 15) & ~(size_t)15) + 8 * 2 * 256 * 4 + 9 * 16 * 4;
+  return M >= 1 && M <= 16 && lds <= 160 * 1024;
+}
+
+}  // namespace
+
+struct tl_ctx {
+  tl_config cfg;
+  std::vector<BlockW> blocks;  // n_pre pre-blocks, then the loop block
+  const uint16_t* embed;
+  const uint16_t* head;
+  const uint16_t* final_norm;
+  float* rope;
+  tl::KvGeom kv;
+  float* x;
+  uint16_t* h;
+  float* qkv;
+  uint16_t* q;
+  uint16_t* o;
+  uint16_t* a;
+  float* part;
+  float* logits;
+  std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
+};
+
+namespace {
+
+tl_status linear(const tl::Packed& w, const tl::ASrc& src, uint16_t* norm_buf, int M, const tl::Epi& e,
+                 hipStream_t s) {
+  if (gemv_fits(M, w.K) && M <= 8) {
+    TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
+    return TL_OK;
+  }
+  const uint16_t* A = src.a16;
+  if (src.x32) {
+    TL_HIP(tl::launch_rmsnorm(src.x32, src.gamma, src.eps, M, w.K, norm_buf, s));
+    A = norm_buf;
+  }
+  TL_HIP(tl::launch_w4_gemm(w, A, M, e, s));
+  return TL_OK;
+}
+
+// One effective layer over M rows (prefill rows of one lane, or the first M
+// decode rows).
+tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowMap& rm, bool decode,
+                    hipStream_t s) {
+  const int d = c->cfg.d_model, f = c->cfg.ffn_dim;
+  const float eps = c->cfg.rms_eps;
+  tl_status st;
+  // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T
+  st = linear(B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, c->h, M,
+              tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, s);
+  if (st != TL_OK) return st;
+  // RoPE on q, k; fp16 Q; K, V into cache layer `layer`
+  TL_HIP(tl::launch_rope_kv(c->qkv, M, rm, c->rope, c->kv, layer, c->q, s));
+  // causal attention over the lane's cache
+  if (decode)
+    TL_HIP(tl::launch_attn_decode(c->q, M, rm, c->kv, layer, c->part, c->o, s));
+  else
+    TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
+  // x += O W_o^T
+  st = linear(B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, nullptr, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
+  if (st != TL_OK) return st;
+  // a = fp16(silu(h2 W_gate^T) * h2 W_up^T), h2 = fp16(RMSNorm(x))
+  st = linear(B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, c->h, M,
+              tl::Epi{tl::EPI_SWIGLU, nullptr, c->a, f}, s);
+  if (st != TL_OK) return st;
+  // x += a W_down^T
+  return linear(B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, nullptr, M,
+                tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
+}
+
+tl_status check_lane(const tl_ctx* c, int lane) {
+  if (!c) return fail(TL_E_INVAL, "ctx is NULL");
+  if (lane < 0 || lane >= c->cfg.n_lanes) return fail(TL_E_INVAL, "lane index out of range");
+  return TL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tl_last_error(void) { return g_err.c_str(); }
+
+size_t tl_weights_ws_bytes(const tl_config* cfg) {
+  tl_status st;
+  std::string why;
+  if (!check_cfg(cfg, &st, &why)) return 0;
+  return (size_t)(cfg->n_pre + 1) * block_bytes(cfg) + rope_bytes(cfg);
+}
+
+size_t tl_kv_layer_bytes(const tl_config* cfg) {
+  tl_status st;
+  std::string why;
+  if (!check_cfg(cfg, &st, &why)) return 0;
+  const size_t rows = (size_t)cfg->max_seq * cfg->n_heads;
+  if (cfg->kv_dtype == TL_KV_INT8) return 2 * rows * (cfg->head_dim + 2);
+  return 2 * rows * cfg->head_dim * 2;
+}
+
+size_t tl_kv_bytes(const tl_config* cfg) {
+  return (size_t)(cfg ? cfg->n_lanes : 0) * (size_t)(cfg ? cfg->n_pre + cfg->max_loops : 0) *
+         tl_kv_layer_bytes(cfg);
+}
+
+size_t tl_act_ws_bytes(const tl_config* cfg) {
+  tl_status st;
+  std::string why;
+  if (!check_cfg(cfg, &st, &why)) return 0;
+  return act_layout(cfg).total;
+}
+
+tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_ws, void* d_kv, void* d_act_ws,
+                    void* stream, tl_ctx** out) {
+  tl_status st;
+  std::string why;
+  if (!out) return fail(TL_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (!check_cfg(cfg, &st, &why)) return fail(st, why);
+  if (!w || !w->embed || !w->head || !w->final_norm || (cfg->n_pre > 0 && !w->pre))
+    return fail(TL_E_INVAL, "missing weight pointer");
+  if (!d_weights_ws || !d_kv || !d_act_ws) return fail(TL_E_INVAL, "workspace pointer is NULL");
+  if (!aligned(d_weights_ws, 256) || !aligned(d_kv, 256) || !aligned(d_act_ws, 256))
+    return fail(TL_E_INVAL, "workspaces must be 256-byte aligned");
+  if (!aligned(w->embed, 16) || !aligned(w->head, 16)) return fail(TL_E_INVAL, "embed/head must be 16-byte aligned");
+  auto block_ok = [](const tl_block& b) {
+    const tl_qlinear* ls[7] = {&b.wq, &b.wk, &b.wv, &b.wo, &b.w_gate, &b.w_up, &b.w_down};
+    for (auto* l : ls)
+      if (!l->qweight || !l->scales || !aligned(l->qweight, 4) || !aligned(l->scales, 2)) return false;
+    return b.attn_norm && b.mlp_norm;
+  };
+  for (int i = 0; i < cfg->n_pre; ++i)
+    if (!block_ok(w->pre[i])) return fail(TL_E_INVAL, "pre-block weight pointer missing or misaligned");
+  if (!block_ok(w->loop)) return fail(TL_E_INVAL, "loop-block weight pointer missing or misaligned");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  tl_ctx* c = new tl_ctx();
+  c->cfg = *cfg;
+  c->embed = w->embed;
+  c->head = w->head;
+  c->final_norm = w->final_norm;
+  const int d = cfg->d_model, f = cfg->ffn_dim;
+  uint8_t* p = static_cast<uint8_t*>(d_weights_ws);
+  auto carve = [&](int N, int K) {
+    tl::Packed pk;
+    pk.tiles = p;
+    pk.scales = reinterpret_cast<const uint16_t*>(p + tl::packed_tile_bytes(N, K));
+    pk.N = N;
+    pk.K = K;
+    pk.G = (K + 127) / 128;
+    p += al256(tl::packed_bytes(N, K));
+    return pk;
+  };
+  auto pack = [&](const tl_qlinear& l, int N, int K, const tl::Packed& dst, int off, int stride) {
+    return tl::launch_pack(l.qweight, l.scales, N, K, const_cast<uint8_t*>(dst.tiles),
+                           const_cast<uint16_t*>(dst.scales), dst.G, off, stride, s);
+  };
+  for (int b = 0; b <= cfg->n_pre; ++b) {
+    const tl_block& src = b < cfg->n_pre ? w->pre[b] : w->loop;
+    BlockW B;
+    B.qkv = carve(3 * d, d);
+    B.o = carve(d, d);
+    B.gu = carve(2 * f, d);
+    B.down = carve(d, f);
+    B.attn_norm = src.attn_norm;
+    B.mlp_norm = src.mlp_norm;
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = pack(src.wq, d, d, B.qkv, 0, 1);
+    if (e == hipSuccess) e = pack(src.wk, d, d, B.qkv, d / 16, 1);
+    if (e == hipSuccess) e = pack(src.wv, d, d, B.qkv, 2 * d / 16, 1);
+    if (e == hipSuccess) e = pack(src.wo, d, d, B.o, 0, 1);
+    if (e == hipSuccess) e = pack(src.w_gate, f, d, B.gu, 0, 2);  // gate/up n-blocks interleaved
+    if (e == hipSuccess) e = pack(src.w_up, f, d, B.gu, 1, 2);
+    if (e == hipSuccess) e = pack(src.w_down, d, f, B.down, 0, 1);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(TL_E_HIP, std::string("weight repack: ") + hipGetErrorString(e));
+    }
+    c->blocks.push_back(B);
+  }
+  // RoPE table: cos then sin of pos * base^(-2i/hd), computed in double.
+  c->rope = reinterpret_cast<float*>(p);
+  {
+    const int half = cfg->head_dim / 2, S = cfg->max_seq;
+    std::vector<float> tab((size_t)2 * S * half);
+    for (int pos = 0; pos < S; ++pos)
+      for (int i = 0; i < half; ++i) {
+        const double th = std::pow((double)cfg->rope_base, -2.0 * i / cfg->head_dim);
+        tab[(size_t)pos * half + i] = (float)std::cos(pos * th);
+        tab[(size_t)S * half + (size_t)pos * half + i] = (float)std::sin(pos * th);
+      }
+    hipError_t e = hipMemcpyAsync(c->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      delete c;
+      return fail(TL_E_HIP, std::string("rope table upload: ") + hipGetErrorString(e));
+    }
+  }
+  c->kv.base = static_cast<uint8_t*>(d_kv);
+  c->kv.layer_bytes = tl_kv_layer_bytes(cfg);
+  c->kv.n_layers = cfg->n_pre + cfg->max_loops;
+  c->kv.H = cfg->n_heads;
+  c->kv.hd = cfg->head_dim;
+  c->kv.S = cfg->max_seq;
+  c->kv.int8 = cfg->kv_dtype == TL_KV_INT8;
+  const ActLayout L = act_layout(cfg);
+  uint8_t* ab = static_cast<uint8_t*>(d_act_ws);
+  c->x = reinterpret_cast<float*>(ab + L.x);
+  c->h = reinterpret_cast<uint16_t*>(ab + L.h);
+  c->qkv = reinterpret_cast<float*>(ab + L.qkv);
+  c->q = reinterpret_cast<uint16_t*>(ab + L.q);
+  c->o = reinterpret_cast<uint16_t*>(ab + L.o);
+  c->a = reinterpret_cast<uint16_t*>(ab + L.a);
+  c->part = reinterpret_cast<float*>(ab + L.part);
+  c->logits = reinterpret_cast<float*>(ab + L.logits);
+  c->len.assign(cfg->n_lanes, 0);
+  c->loops.assign(cfg->n_lanes, 1);
+  c->depth.assign(cfg->n_lanes, INT_MAX);
+  *out = c;
+  return TL_OK;
+}
+
+tl_status tl_destroy(tl_ctx* ctx) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  delete ctx;
+  return TL_OK;
+}
+
+tl_status tl_set_loops(tl_ctx* ctx, int32_t lane, int32_t loops) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (lane < -1 || lane >= ctx->cfg.n_lanes) return fail(TL_E_INVAL, "lane index out of range");
+  if (loops < 1 || loops > ctx->cfg.max_loops) return fail(TL_E_RANGE, "loops outside 1..max_loops");
+  const int lo = lane < 0 ? 0 : lane, hi = lane < 0 ? ctx->cfg.n_lanes : lane + 1;
+  for (int l = lo; l < hi; ++l)
+    if (ctx->len[l] > 0 && ctx->cfg.n_pre + loops > ctx->depth[l])
+      return fail(TL_E_STATE, "lane holds tokens computed to a smaller depth");
+  for (int l = lo; l < hi; ++l) ctx->loops[l] = loops;
+  return TL_OK;
+}
+
+tl_status tl_get_loops(const tl_ctx* ctx, int32_t lane, int32_t* loops) {
+  tl_status st = check_lane(ctx, lane);
+  if (st != TL_OK) return st;
+  if (!loops) return fail(TL_E_INVAL, "loops is NULL");
+  *loops = ctx->loops[lane];
+  return TL_OK;
+}
+
+tl_status tl_reset(tl_ctx* ctx, int32_t lane) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (lane < -1 || lane >= ctx->cfg.n_lanes) return fail(TL_E_INVAL, "lane index out of range");
+  const int lo = lane < 0 ? 0 : lane, hi = lane < 0 ? ctx->cfg.n_lanes : lane + 1;
+  for (int l = lo; l < hi; ++l) {
+    ctx->len[l] = 0;
+    ctx->depth[l] = INT_MAX;
+  }
+  return TL_OK;
+}
+
+int32_t tl_length(const tl_ctx* ctx, int32_t lane) {
+  if (!ctx || lane < 0 || lane >= ctx->cfg.n_lanes) return -1;
+  return ctx->len[lane];
+}
+
+tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t n, float* d_hidden,
+                     float* d_logits, int32_t* d_next, void* stream) {
+  tl_status st = check_lane(ctx, lane);
+  if (st != TL_OK) return st;
+  if (!d_tokens) return fail(TL_E_INVAL, "d_tokens is NULL");
+  const tl_config& C = ctx->cfg;
+  if (n < 1 || n > C.max_tokens) return fail(TL_E_RANGE, "n outside 1..max_tokens");
+  const int p0 = ctx->len[lane];
+  if (p0 + n > C.max_seq) return fail(TL_E_RANGE, "prefill would exceed max_seq");
+  const int L = ctx->loops[lane];
+  if (p0 > 0 && C.n_pre + L > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  tl::RowMap rm{};
+  rm.per_row = 0;
+  rm.lane = lane;
+  rm.p0 = p0;
+  const int d = C.d_model;
+  TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
+  for (int layer = 0; layer < C.n_pre + L; ++layer) {
+    const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
+    st = run_layer(ctx, B, layer, n, rm, false, s);
+    if (st != TL_OK) return st;
+  }
+  if (d_hidden) TL_HIP(hipMemcpyAsync(d_hidden, ctx->x, (size_t)n * d * 4, hipMemcpyDeviceToDevice, s));
+  if (d_logits || d_next) {
+    float* lg = d_logits ? d_logits : ctx->logits;
+    TL_HIP(tl::launch_rmsnorm(ctx->x + (size_t)(n - 1) * d, ctx->final_norm, C.rms_eps, 1, d, ctx->h, s));
+    tl::RowMap one{};
+    TL_HIP(tl::launch_head_z(ctx->h, 1, ctx->head, C.vocab, d, lg, one, s));
+    if (d_next) TL_HIP(tl::launch_argmax(lg, 1, C.vocab, one, d_next, s));
+  }
+  ctx->len[lane] = p0 + n;
+  ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
+  return TL_OK;
+}
+
+tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_active, float* d_hidden,
+                         float* d_logits, int32_t* d_next, void* stream) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (!d_tokens) return fail(TL_E_INVAL, "d_tokens is NULL");
+  const tl_config& C = ctx->cfg;
+  std::vector<int> rows;
+  for (int l = 0; l < C.n_lanes; ++l)
+    if (!h_active || h_active[l]) rows.push_back(l);
+  for (int l : rows) {
+    if (ctx->len[l] < 1) return fail(TL_E_STATE, "decode on a lane with no cached token");
+    if (ctx->len[l] >= C.max_seq) return fail(TL_E_RANGE, "lane is at max_seq");
+    if (C.n_pre + ctx->loops[l] > ctx->depth[l]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
+  }
+  if (rows.empty()) return TL_OK;
+  std::stable_sort(rows.begin(), rows.end(), [&](int a, int b) { return ctx->loops[a] > ctx->loops[b]; });
+  const int M = (int)rows.size();
+  tl::RowMap rm{};
+  rm.per_row = 1;
+  for (int m = 0; m < M; ++m) {
+    rm.row_lane[m] = rows[m];
+    rm.row_pos[m] = ctx->len[rows[m]];
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int d = C.d_model;
+  TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
+  const int Lmax = ctx->loops[rows[0]];
+  for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
+    int Ml = 0;
+    while (Ml < M && C.n_pre + ctx->loops[rows[Ml]] > layer) ++Ml;
+    const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
+    tl_status st = run_layer(ctx, B, layer, Ml, rm, true, s);
+    if (st != TL_OK) return st;
+  }
+  if (d_logits || d_next) {
+    float* lg = d_logits ? d_logits : ctx->logits;
+    TL_HIP(tl::launch_rmsnorm(ctx->x, ctx->final_norm, C.rms_eps, M, d, ctx->h, s));
+    TL_HIP(tl::launch_head_z(ctx->h, M, ctx->head, C.vocab, d, lg, rm, s));
+    if (d_next) TL_HIP(tl::launch_argmax(lg, M, C.vocab, rm, d_next, s));
+  }
+  if (d_hidden) TL_HIP(tl::launch_scatter_rows(ctx->x, M, d, rm, d_hidden, s));
+  for (int l : rows) {
+    ctx->len[l] += 1;
+    ctx->depth[l] = std::min(ctx->depth[l], C.n_pre + ctx->loops[l]);
+  }
+  return TL_OK;
+}
+
+// ---------------------------------------------------------------- single kernels
+size_t tl_qlinear_packed_bytes(int32_t N, int32_t K) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return 0;
+  return tl::packed_bytes(N, K);
+}
+
+tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, int32_t N, int32_t K, void* d_packed,
+                          void* stream) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
+  if (!d_qweight || !d_scales || !d_packed || !aligned(d_packed, 256)) return fail(TL_E_INVAL, "bad pointer");
+  uint8_t* t = static_cast<uint8_t*>(d_packed);
+  TL_HIP(tl::launch_pack(d_qweight, d_scales, N, K, t, reinterpret_cast<uint16_t*>(t + tl::packed_tile_bytes(N, K)),
+                         (K + 127) / 128, 0, 1, reinterpret_cast<hipStream_t>(stream)));
+  return TL_OK;
+}
+
+static tl::Packed packed_view(const void* d_packed, int N, int K) {
+  tl::Packed p;
+  p.tiles = static_cast<const uint8_t*>(d_packed);
+  p.scales = reinterpret_cast<const uint16_t*>(p.tiles + tl::packed_tile_bytes(N, K));
+  p.N = N;
+  p.K = K;
+  p.G = (K + 127) / 128;
+  return p;
+}
+
+tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* d_q, uint16_t* d_scales,
+                            void* stream) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
+  if (!d_packed || !d_q || !d_scales) return fail(TL_E_INVAL, "bad pointer");
+  TL_HIP(tl::launch_unpack(packed_view(d_packed, N, K), d_q, d_scales, reinterpret_cast<hipStream_t>(stream)));
+  return TL_OK;
+}
+
+tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M, float* d_C,
+                       void* stream) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
+  if (M < 1) return fail(TL_E_RANGE, "M < 1");
+  if (!d_packed || !d_A || !d_C || !aligned(d_A, 16)) return fail(TL_E_INVAL, "bad pointer");
+  const tl::Packed p = packed_view(d_packed, N, K);
+  const tl::Epi e{tl::EPI_STORE, d_C, nullptr, N};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (gemv_fits(M, K))
+    TL_HIP(tl::launch_w4_gemv(p, tl::ASrc{d_A, nullptr, nullptr, 0.f}, M, e, s));
+  else
+    TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, s));
+  return TL_OK;
+}
+
+tl_status tl_kv_quantize_rows(const uint16_t* d_x, int32_t rows, int32_t hd, int8_t* d_q, uint16_t* d_s,
+                              void* stream) {
+  if (rows < 1 || hd < 2 || hd > 128 || hd % 2) return fail(TL_E_INVAL, "need rows >= 1, hd even and <= 128");
+  if (!d_x || !d_q || !d_s) return fail(TL_E_INVAL, "bad pointer");
+  TL_HIP(tl::launch_kv_quantize_rows(d_x, rows, hd, d_q, d_s, reinterpret_cast<hipStream_t>(stream)));
+  return TL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define TL_WAVE 64
+
+namespace tl {
+
+// ---------------------------------------------------------------------------
+// Packed INT4 layout (see pack.hip): a tile covers 16 output rows x 128 input
+// columns, 1 KiB, and lane l of a wave owns the 16-byte slot l of the tile:
+// word s (0..3) of the slot holds the 8 values of row 16*nb + l%16 at columns
+// 128*g + 32*s + 8*(l/16) + 0..7, which is exactly the B operand of one
+// v_mfma_f32_16x16x32_f16 k-step. Nibble p holds column 2p and nibble p+4
+// column 2p+1 (so each 16-bit half of (w >> 4p) & 0x000F000F is one element
+// of a consecutive pair), stored offset-binary u = q + 8.
+// ---------------------------------------------------------------------------
+constexpr int kTileBytes = 1024;
+constexpr int kGroup = 128;
+
+// 8 signed 4-bit values of one packed word -> 8 exact fp16 integers in
+// column order. OR-ing u into the mantissa of 1024.0h gives 1024 + u exactly;
+// subtracting 1032 gives q = u - 8 exactly (integers below 2048 are exact).
+__device__ __forceinline__ half8_t dequant_word(uint32_t w) {
+  const uint32_t magic = 0x64006400u, mask = 0x000F000Fu;
+  uint32_t t0 = (w & mask) | magic;
+  uint32_t t1 = ((w >> 4) & mask) | magic;
+  uint32_t t2 = ((w >> 8) & mask) | magic;
+  uint32_t t3 = ((w >> 12) & mask) | magic;
+  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  half2_t a0 = __builtin_bit_cast(half2_t, t0) + bias;
+  half2_t a1 = __builtin_bit_cast(half2_t, t1) + bias;
+  half2_t a2 = __builtin_bit_cast(half2_t, t2) + bias;
+  half2_t a3 = __builtin_bit_cast(half2_t, t3) + bias;
+  half8_t r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+  return r;
+}
+
+__device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+}
+
+// Butterfly reductions over a whole wave (fixed order: every lane ends with
+// the same value, computed in the same order whatever the data).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, TL_WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, TL_WAVE));
+  return v;
+}
+// Reductions over the 16 lanes of one row of the wave (lanes 16r..16r+15).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, TL_WAVE);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, TL_WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace tl

@@ -1,0 +1,101 @@
+// Host-side launchers of the gfx950 kernels (internal to libtl).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tl {
+
+// A linear in the packed layout: tiles [N/16][G][64 lanes][16 B], then
+// scales fp16 [N/16][G][16]. G = ceil(K / 128).
+struct Packed {
+  const uint8_t* tiles;
+  const uint16_t* scales;
+  int N, K, G;
+};
+
+inline size_t packed_tile_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 1024; }
+inline size_t packed_scale_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 32; }
+inline size_t packed_bytes(int N, int K) { return packed_tile_bytes(N, K) + packed_scale_bytes(N, K); }
+
+// Repack a canonical [N][K/8] / [N][ceil(K/128)] linear into the packed
+// buffer of a (possibly fused) destination: source n-block b goes to
+// destination n-block nb_offset + b * nb_stride.
+hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles,
+                       uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, hipStream_t s);
+hipError_t launch_unpack(const Packed& p, int8_t* q, uint16_t* scales, hipStream_t s);
+
+// Epilogue of the W4 matrix kernels.
+enum EpiMode { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+struct Epi {
+  int mode;
+  float* out_f32;     // STORE: out[m*ldo + n]; RESID: out[m*ldo + n] += v
+  uint16_t* out_f16;  // SWIGLU: fp16 out[m*ldo + c], c = output column
+  int ldo;
+};
+
+// Activation source of the matrix kernels: fp16 rows, or fp32 residual rows
+// normalised on the fly (h = fp16(gamma * x / sqrt(mean(x^2) + eps))).
+struct ASrc {
+  const uint16_t* a16;  // fp16 [M][K] (used when x32 is null)
+  const float* x32;     // fp32 [M][K] residual rows to RMS-normalise
+  const uint16_t* gamma;
+  float eps;
+};
+
+// C = A * W^T for M <= 16 rows (decode GEMV shape); K split across waves.
+hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s);
+// C = A * W^T for any M (prefill GEMM shape); A fp16 [M][K].
+hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, hipStream_t s);
+
+// fp16 h [M][d] = RMSNorm(x) (prefill path).
+hipError_t launch_rmsnorm(const float* x, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
+                          hipStream_t s);
+
+// Per-row placement of the rows of one call: row m belongs to lane
+// row_lane[m] at absolute position row_pos[m]. Prefill rows are all one
+// lane at p0 + m (per_row == 0); decode rows use the arrays (M <= 8).
+struct RowMap {
+  int per_row;
+  int lane, p0;
+  int row_lane[8];
+  int row_pos[8];
+};
+
+struct KvGeom {
+  uint8_t* base;        // start of all caches
+  size_t layer_bytes;   // one lane, one layer
+  int n_layers;         // layers per lane
+  int H, hd, S;         // heads, head_dim, max_seq
+  int int8;
+};
+
+// RoPE on q and k of qkv fp32 [M][3d], fp16 Q out [M][d], K/V into cache layer.
+hipError_t launch_rope_kv(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+                          int layer, uint16_t* q_out, hipStream_t s);
+
+// Causal attention of M new rows of one lane (prefill) over cache rows
+// 0..p0+M-1 of one layer. Q fp16 [M][d] -> O fp16 [M][d].
+hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const KvGeom& kv, int layer,
+                               uint16_t* o, hipStream_t s);
+// Single-query attention for M decode rows (one per lane) over each lane's
+// rows 0..row_pos[m]. part: scratch floats.
+size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
+hipError_t launch_attn_decode(const uint16_t* q, int M, const RowMap& rm, const KvGeom& kv, int layer,
+                              float* part, uint16_t* o, hipStream_t s);
+
+hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d,
+                        float* x, hipStream_t s);
+// logits of normed fp16 rows z [M][d] (M <= 16) against the fp16 head
+// [V][d]; row m is written at logits[out_row(m) * V], out_row = the row's
+// lane in decode (per_row) and m in prefill.
+hipError_t launch_head_z(const uint16_t* z, int M, const uint16_t* head, int V, int d, float* logits,
+                         const RowMap& rm, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int M, int V, const RowMap& rm, int32_t* next, hipStream_t s);
+// dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
+hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
+
+hipError_t launch_kv_quantize_rows(const uint16_t* x, int rows, int hd, int8_t* q, uint16_t* sc,
+                                   hipStream_t s);
+
+}  // namespace tl

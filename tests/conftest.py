@@ -14,3 +14,35 @@ def pytest_configure(config):
 
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def ensure_library():
+    """Build libtl.so from source if it is not there yet, then import the binding."""
+    lib = os.path.join(ROOT, "looped_weight_shared_amd", "libtl.so")
+    if not os.path.exists(lib):
+        from looped_weight_shared_amd.build import build
+        build()
+    import looped_weight_shared_amd
+    return looped_weight_shared_amd
+
+
+def rel_rows(a, b):
+    """max over rows of max|a - b| / max|b| (b is the reference)."""
+    import numpy as np
+    a = np.atleast_2d(np.asarray(a, dtype=np.float64))
+    b = np.atleast_2d(np.asarray(b, dtype=np.float64))
+    return float((np.abs(a - b).max(axis=-1) / np.abs(b).max(axis=-1)).max())
+
+
+def pytest_collection_modifyitems(config, items):
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="needs a GPU")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

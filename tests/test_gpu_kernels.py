@@ -1,0 +1,153 @@
+"""GPU parity of single kernels through the C ABI: the INT4 repack and the
+INT8 KV quantizer bit for bit against the oracle, and the W4 linear (decode
+GEMV and prefill GEMM kernels) against the oracle's exact dequantize-then-matmul."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import GOLDEN, ensure_library, rel_rows
+
+pytestmark = pytest.mark.gpu
+tl = ensure_library()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dev(a):
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.float16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t, dtype=None):
+    a = t.cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def _linear(rng, N, K):
+    qw = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32)
+    sc = (0.02 / 7 * rng.uniform(0.5, 1.5, size=(N, -(-K // 128)))).astype(np.float16)
+    return qw, sc
+
+
+def _packed(qw, sc, N, K):
+    from looped_weight_shared_amd.model import device_bytes
+    p = device_bytes(tl.tl_qlinear_packed_bytes(N, K))
+    tl.tl_qlinear_pack(dev(qw), dev(sc), N, K, p)
+    return p
+
+
+@pytest.mark.parametrize("N,K", [(16, 8), (32, 704), (256, 256), (2048, 5632), (6144, 2048)])
+def test_repack_is_bit_exact(N, K):
+    torch = _torch()
+    rng = np.random.default_rng(N + K)
+    qw, sc = _linear(rng, N, K)
+    p = _packed(qw, sc, N, K)
+    q = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((N, -(-K // 128)), dtype=torch.int16, device="cuda")
+    tl.tl_qlinear_unpack(p, N, K, q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), oracle.unpack_int4(qw))
+    assert np.array_equal(host(s, np.float16).view(np.uint16), sc.view(np.uint16))
+
+
+LIN_CASES = [(6144, 2048, m) for m in (1, 3, 8, 16, 17, 128, 130)] + \
+            [(2048, 5632, m) for m in (1, 2, 64, 1024)] + \
+            [(256, 704, m) for m in (1, 5, 32, 33)] + [(11264, 2048, 1), (11264, 2048, 256)]
+
+
+@pytest.mark.parametrize("N,K,M", LIN_CASES)
+def test_w4_linear_matches_oracle(N, K, M):
+    torch = _torch()
+    rng = np.random.default_rng(7 * N + K + M)
+    qw, sc = _linear(rng, N, K)
+    p = _packed(qw, sc, N, K)
+    A = rng.standard_normal((M, K)).astype(np.float16)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    tl.tl_w4_linear(p, N, K, dev(A), M, C)
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ oracle.dequantize(qw, sc).T
+    err = rel_rows(host(C), ref)
+    print(f"N={N} K={K} M={M} rel_row_err={err:.2e}")
+    assert err < 1e-4
+    # run twice: bit-identical
+    C2 = torch.empty_like(C)
+    tl.tl_w4_linear(p, N, K, dev(A), M, C2)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+
+
+def test_gemv_rows_do_not_depend_on_batch():
+    torch = _torch()
+    N, K = 2048, 2048
+    rng = np.random.default_rng(11)
+    qw, sc = _linear(rng, N, K)
+    p = _packed(qw, sc, N, K)
+    A = rng.standard_normal((8, K)).astype(np.float16)
+    full = torch.empty((8, N), dtype=torch.float32, device="cuda")
+    tl.tl_w4_linear(p, N, K, dev(A), 8, full)
+    for m in range(8):
+        one = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        tl.tl_w4_linear(p, N, K, dev(A[m:m + 1]), 1, one)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], full[m])
+
+
+def _quant_gpu(x):
+    torch = _torch()
+    rows, hd = x.shape
+    q = torch.empty((rows, hd), dtype=torch.int8, device="cuda")
+    s = torch.empty((rows,), dtype=torch.int16, device="cuda")
+    tl.tl_kv_quantize_rows(dev(x), rows, hd, q, s)
+    torch.cuda.synchronize()
+    return host(q), host(s, np.float16)
+
+
+def _adversarial_rows():
+    rows = []
+    # exact ties: scale 1/16 (amax 127/16), values (k + 1/2)/16
+    k = np.arange(-127, 127)
+    for start in range(0, len(k), 127):
+        r = np.zeros(128)
+        vals = (k[start:start + 127] + 0.5) / 16.0
+        r[:len(vals)] = vals
+        r[127] = 127 / 16.0
+        rows.append(r)
+    rows.append(np.zeros(128))                                    # zero row, scale 0
+    r = np.zeros(128); r[0] = 2.0 ** -10; r[1] = -(2.0 ** -10); r[2] = 2.0 ** -24
+    rows.append(r)                                                # subnormal scale, clamp
+    r = np.full(128, 65504.0); r[::2] = -65504.0
+    rows.append(r)                                                # largest finite fp16
+    return np.array(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("hd", [128, 64])
+def test_kv_quantizer_bit_exact(hd):
+    rng = np.random.default_rng(hd)
+    parts = [(rng.standard_normal((4000, hd)) * sp).astype(np.float16) for sp in (0.01, 1.0, 40.0)]
+    if hd == 128:
+        parts.append(_adversarial_rows())
+    x = np.concatenate(parts)
+    q, s = _quant_gpu(x)
+    qo, so = oracle.kv_quantize(x)
+    assert np.array_equal(s.view(np.uint16), so.view(np.uint16))
+    assert np.array_equal(q, qo)
+
+
+def test_kv_quantizer_worked_rows():
+    cases = json.load(open(os.path.join(GOLDEN, "kv_int8_worked.json")))["cases"]
+    x = np.array([c["x"] for c in cases], dtype=np.float16)
+    q, s = _quant_gpu(x)
+    for i, c in enumerate(cases):
+        assert float(s[i]) == c["scale"]
+        assert q[i].tolist() == c["q"]

@@ -1,0 +1,237 @@
+"""Benchmark of the looped weight-shared transformer forward pass on one MI355X.
+
+Timed step: one tl_prefill of 128 uniform token ids through the 407M-shaped
+model (d 2048, 16 x 128 heads, ffn 5632, 2 pre-blocks + the shared loop block
+at L = 8, INT4 group-128 weights, FP16 KV) with no logits materialised -- the
+benchmark shape of the "Performance and Memory" page ("Benchmark Shape
+Matters": seq_len 128, loops 8, no logits). `value` is prefill tokens/s.
+
+Also reported (same JSON line):
+  decode   -- cached greedy decode at L = 8 after a 256-token prompt, 128 steps,
+              each step's argmax fed to the next on the device; ms/token.
+  roofline -- the dominant prefill kernel (W4A16 MFMA GEMM) against the fp16
+              MFMA peak; roofline_decode -- the W4 decode GEMV against HBM.
+              Per-launch durations come from HIP event pairs the library
+              records around every launch on its stream (tl_profile_begin/end)
+              during a separate pass over the same steps.
+  cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
+              the same prefill step (reported, not a target).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import importlib.util
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + decode ms/token, 407M-shape W4 loop L=8; % HBM/MFMA peak"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "looped_weight_shared_amd", "libtl.so")
+    if not os.path.exists(lib):
+        spec = importlib.util.spec_from_file_location(
+            "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "looped_weight_shared_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_files, launches_bytes_expected=None):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != _src_hash(*src_files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--prompt", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the forward pass would shard across GPUs by lanes (data parallel).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    _ensure_built()
+    import numpy as np
+    import torch
+
+    import synth
+    import looped_weight_shared_amd as tl
+    from looped_weight_shared_amd.model import Model
+
+    torch.cuda.set_device(0)
+    s = synth.SHAPES["m407"]
+    L, SEQ = 8, 128
+    t0 = time.time()
+    w = synth.make_weights(s, seed=0)
+    print(f"[bench] synthetic 407M-shape weights in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    m = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=tl.TL_KV_FP16,
+              max_tokens=max(SEQ, args.prompt))
+    m.set_loops(0, L)
+    toks = torch.from_numpy(synth.make_tokens(s.vocab, SEQ, seed=0)).cuda()
+    stream = torch.cuda.current_stream()
+
+    def prefill_step():
+        m.reset(0)               # host-only: the lane is empty again
+        m.prefill(toks)          # no hidden, no logits
+
+    # ---------------------------------------------------------------- prefill leg
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        prefill_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tok_s = SEQ / (ms_step / 1e3)
+    print(f"[bench] prefill seq {SEQ} L={L}: {ms_step:.3f} ms/step, {tok_s:,.0f} tok/s",
+          file=sys.stderr, flush=True)
+
+    # per-kernel durations over the same steps (HIP events around every launch)
+    tl.tl_profile_begin(m.ctx, 200000)
+    for _ in range(args.steps):
+        prefill_step()
+    prof = tl.tl_profile_end(m.ctx)
+    kern_prefill = {k: (n, ms / n * 1e3) for k, (n, ms) in prof.items() if n}
+    d, f = s.d_model, s.ffn_dim
+    flops = {"qkv": 2 * SEQ * 3 * d * d, "o": 2 * SEQ * d * d, "gate_up": 2 * SEQ * 2 * f * d,
+             "down": 2 * SEQ * d * f}
+    gemm_kinds = [k for k in flops if k in kern_prefill]
+    dom = max(gemm_kinds, key=lambda k: kern_prefill[k][0] * kern_prefill[k][1])
+    avg_us = kern_prefill[dom][1]
+    achieved = flops[dom] / (avg_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                "traffic": _traffic("gemm_" + dom, ["w4mm.hip", "tl_device.h"]),
+                "kernel": f"w4_gemm_kernel ({dom}: M={SEQ} N={2 * f if dom == 'gate_up' else (3 * d if dom == 'qkv' else d)} "
+                          f"K={f if dom == 'down' else d})",
+                "flop_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3)}
+
+    out = {"metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": "407M-shape looped transformer prefill, seq 128, L=8 (2 pre + 1 loop "
+                                  "block, 10 effective layers), W4 g128 weights, FP16 KV, no logits",
+                      "global_batch": 1, "seq_len": SEQ, "loops": L, "parallelism": "none (1 GPU)"},
+           "roofline": roofline,
+           "kernels_prefill_us": {k: round(v[1], 3) for k, v in kern_prefill.items()}}
+
+    # ---------------------------------------------------------------- decode leg
+    if not args.no_decode:
+        P, D = args.prompt, args.decode_steps
+        ptoks = torch.from_numpy(synth.make_tokens(s.vocab, P, seed=0)).cuda()
+        nx = torch.zeros(1, dtype=torch.int32, device="cuda")
+        bufs = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+
+        def decode_run(steps, timed):
+            m.reset(0)
+            m.prefill(ptoks, next_tok=bufs[0])
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for t in range(steps):
+                m.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1])
+
+        decode_run(8, False)                       # warm-up
+        ms = decode_run(D, True)
+        ms_tok = ms / D
+        print(f"[bench] decode L={L} prompt {P} + {D} steps: {ms_tok:.4f} ms/token",
+              file=sys.stderr, flush=True)
+        # profiled pass
+        m.reset(0)
+        m.prefill(ptoks, next_tok=bufs[0])
+        tl.tl_profile_begin(m.ctx, 200000)
+        for t in range(D):
+            m.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+        dprof = tl.tl_profile_end(m.ctx)
+        kern_dec = {k: (n, ms_ / n * 1e3) for k, (n, ms_) in dprof.items() if n}
+        wbytes = {"qkv": tl.tl_qlinear_packed_bytes(3 * d, d), "o": tl.tl_qlinear_packed_bytes(d, d),
+                  "gate_up": tl.tl_qlinear_packed_bytes(2 * f, d), "down": tl.tl_qlinear_packed_bytes(d, f)}
+        gb = {k: wbytes[k] / (kern_dec[k][1] * 1e-6) / 1e9 for k in wbytes if k in kern_dec}
+        dk = "gate_up"
+        rd = {"bound": "hbm", "achieved": round(gb[dk], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(gb[dk] / PEAK_HBM_GBS, 4),
+              "traffic": _traffic("gemv_" + dk, ["w4mm.hip", "tl_device.h"]),
+              "kernel": "w4_gemv_kernel (gate_up: M=1 N=11264 K=2048)",
+              "bytes_per_launch": wbytes[dk], "avg_launch_us": round(kern_dec[dk][1], 3),
+              "note": "weights of the loop block are re-read every iteration; iterations after the "
+                      "first can be served from the 256 MB Infinity Cache, so this is an in-situ rate"}
+        algo = (sum(wbytes.values()) * (s.n_pre + L) + s.vocab * d * 2
+                + 2 * 2 * s.n_heads * s.head_dim * (s.n_pre + L) * (P + D / 2))
+        out["decode"] = {"ms_per_token": round(ms_tok, 4), "prompt": P, "steps": D, "loops": L,
+                         "kv": "fp16", "graph_replayed": False,
+                         "algorithmic_bytes_per_token": int(algo),
+                         "hbm_roofline_ms_per_token": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+                         "frac_of_hbm_roofline": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3 / ms_tok, 4),
+                         "kernels_us": {k: round(v[1], 3) for k, v in kern_dec.items()},
+                         "gemv_GBps": {k: round(v, 1) for k, v in gb.items()}}
+        out["roofline_decode"] = rd
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        except Exception:
+            cores = os.cpu_count()
+        om = oracle.OracleModel(w)
+        ptok = synth.make_tokens(s.vocab, SEQ, seed=0)
+        n, t_start = 0, time.perf_counter()
+        while True:
+            oracle.forward(om, ptok, L, logits=None)
+            n += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or n >= 50:
+                break
+        out["cpu_baseline"] = {"value": round(SEQ * n / el, 2), "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"{n} x float64 oracle prefill of the same 128-token L=8 step "
+                                         f"({el:.1f} s; weight dequantization not timed)"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

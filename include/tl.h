@@ -174,6 +174,24 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
 /* Message of the last failed call on this thread ("" if none). */
 const char* tl_last_error(void);
 
+/* ---- kernel timing ------------------------------------------------------
+ * For measurement ("Performance and Memory" page, "How To Publish Numbers
+ * Responsibly" and the phase timings of TINYLOOP_CUDA_PROFILE): while a
+ * window is open, every kernel the context launches is bracketed by a pair
+ * of HIP events recorded on the call's stream, up to max_launches launches.
+ * tl_profile_end waits for the recorded events and returns, per kernel kind,
+ * the number of launches and their summed event-to-event time. */
+typedef enum {
+  TL_K_EMBED = 0, TL_K_NORM, TL_K_QKV, TL_K_ROPE_KV, TL_K_ATTN, TL_K_O, TL_K_GATE_UP, TL_K_DOWN,
+  TL_K_HEAD, TL_K_ARGMAX, TL_K_COPY, TL_K_COUNT
+} tl_kernel_kind;
+/* Errors: TL_E_STATE if a window is already open, TL_E_RANGE for
+ * max_launches outside 1..1000000, TL_E_HIP if events cannot be created. */
+tl_status tl_profile_begin(tl_ctx* ctx, int32_t max_launches);
+/* total_ms double[TL_K_COUNT], count int32[TL_K_COUNT] (host arrays).
+ * Errors: TL_E_STATE if no window is open, TL_E_HIP. */
+tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count);
+
 /* ---- single kernels ----------------------------------------------------
  * The same kernels the forward pass runs, exposed for per-kernel parity
  * tests and bandwidth/throughput measurement. */

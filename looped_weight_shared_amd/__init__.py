@@ -24,12 +24,13 @@ __all__ = [
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
-    "tl_qlinear_unpack", "tl_w4_linear", "tl_kv_quantize_rows", "EXPORTED",
+    "tl_qlinear_unpack", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
+    "KERNEL_KINDS", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtl.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with looped_weight_shared_amd.build.build()")
+    raise ImportError(f"{LIB_PATH} is missing: build it with python looped_weight_shared_amd/build.py")
 lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -93,10 +94,15 @@ _SIGS = {
     "tl_qlinear_unpack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_w4_linear": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
     "tl_kv_quantize_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "tl_profile_begin": (ctypes.c_int, [_vp, _i32]),
+    "tl_profile_end": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]),
 }
 EXPORTED = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(lib, _name)
+    try:
+        _fn = getattr(lib, _name)
+    except AttributeError as _e:
+        raise ImportError(f"{LIB_PATH} lacks {_name}: it is older than the sources, rebuild it") from _e
     _fn.restype = _res
     _fn.argtypes = _args
 
@@ -210,3 +216,19 @@ def tl_w4_linear(packed, N: int, K: int, A, M: int, C, stream=None) -> None:
 
 def tl_kv_quantize_rows(x, rows: int, hd: int, q, s, stream=None) -> None:
     _check(lib.tl_kv_quantize_rows(_ptr(x), rows, hd, _ptr(q), _ptr(s), _stream(stream)))
+
+
+KERNEL_KINDS = ("embed", "norm", "qkv", "rope_kv", "attn", "o", "gate_up", "down", "head", "argmax", "copy")
+
+
+def tl_profile_begin(ctx, max_launches: int) -> None:
+    _check(lib.tl_profile_begin(ctx, max_launches))
+
+
+def tl_profile_end(ctx) -> dict:
+    """{kind: (launches, total_ms)} for the window that just closed."""
+    n = len(KERNEL_KINDS)
+    tot = (ctypes.c_double * n)()
+    cnt = (_i32 * n)()
+    _check(lib.tl_profile_end(ctx, tot, cnt))
+    return {k: (int(cnt[i]), float(tot[i])) for i, k in enumerate(KERNEL_KINDS)}

@@ -1,7 +1,7 @@
 """Build libtl.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
 Every call compiles from source; the library is written next to this file.
-Run directly: python -m looped_weight_shared_amd.build
+Run directly (this file does not import the package): python looped_weight_shared_amd/build.py
 """
 import concurrent.futures
 import glob
@@ -28,6 +28,7 @@ def _run(cmd):
     # hipcc's host pass does not know the GPU target feature above; drop that note
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     return r.returncode, out
+
 
 
 def build(verbose: bool = False) -> str:

@@ -118,21 +118,47 @@ struct tl_ctx {
   float* part;
   float* logits;
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
+  // kernel timing window
+  bool prof_on = false;
+  int prof_cap = 0, prof_used = 0, prof_cur = -1;
+  std::vector<hipEvent_t> prof_ev;  // 2 per launch
+  std::vector<int> prof_kind;
 };
 
 namespace {
 
-tl_status linear(const tl::Packed& w, const tl::ASrc& src, uint16_t* norm_buf, int M, const tl::Epi& e,
-                 hipStream_t s) {
+// Brackets one kernel launch with an event pair while a timing window is open.
+struct KScope {
+  tl_ctx* c;
+  hipStream_t s;
+  KScope(tl_ctx* ctx, int kind, hipStream_t st) : c(ctx), s(st) {
+    c->prof_cur = -1;
+    if (!c->prof_on || c->prof_used >= c->prof_cap) return;
+    const int i = c->prof_used++;
+    c->prof_kind[i] = kind;
+    (void)hipEventRecord(c->prof_ev[2 * i], s);
+    c->prof_cur = i;
+  }
+  ~KScope() {
+    if (c->prof_cur >= 0) (void)hipEventRecord(c->prof_ev[2 * c->prof_cur + 1], s);
+    c->prof_cur = -1;
+  }
+};
+
+tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, uint16_t* norm_buf, int M,
+                 const tl::Epi& e, hipStream_t s) {
   if (gemv_fits(M, w.K) && M <= 8) {
+    KScope k(c, kind, s);
     TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
     return TL_OK;
   }
   const uint16_t* A = src.a16;
   if (src.x32) {
+    KScope k(c, TL_K_NORM, s);
     TL_HIP(tl::launch_rmsnorm(src.x32, src.gamma, src.eps, M, w.K, norm_buf, s));
     A = norm_buf;
   }
+  KScope k(c, kind, s);
   TL_HIP(tl::launch_w4_gemm(w, A, M, e, s));
   return TL_OK;
 }
@@ -145,25 +171,32 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   const float eps = c->cfg.rms_eps;
   tl_status st;
   // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T
-  st = linear(B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, c->h, M,
+  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, c->h, M,
               tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, s);
   if (st != TL_OK) return st;
   // RoPE on q, k; fp16 Q; K, V into cache layer `layer`
-  TL_HIP(tl::launch_rope_kv(c->qkv, M, rm, c->rope, c->kv, layer, c->q, s));
+  {
+    KScope k(c, TL_K_ROPE_KV, s);
+    TL_HIP(tl::launch_rope_kv(c->qkv, M, rm, c->rope, c->kv, layer, c->q, s));
+  }
   // causal attention over the lane's cache
-  if (decode)
-    TL_HIP(tl::launch_attn_decode(c->q, M, rm, c->kv, layer, c->part, c->o, s));
-  else
-    TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
+  {
+    KScope k(c, TL_K_ATTN, s);
+    if (decode)
+      TL_HIP(tl::launch_attn_decode(c->q, M, rm, c->kv, layer, c->part, c->o, s));
+    else
+      TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
+  }
   // x += O W_o^T
-  st = linear(B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, nullptr, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
+  st = linear(c, TL_K_O, B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, nullptr, M,
+              tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
   if (st != TL_OK) return st;
   // a = fp16(silu(h2 W_gate^T) * h2 W_up^T), h2 = fp16(RMSNorm(x))
-  st = linear(B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, c->h, M,
+  st = linear(c, TL_K_GATE_UP, B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, c->h, M,
               tl::Epi{tl::EPI_SWIGLU, nullptr, c->a, f}, s);
   if (st != TL_OK) return st;
   // x += a W_down^T
-  return linear(B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, nullptr, M,
+  return linear(c, TL_K_DOWN, B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, nullptr, M,
                 tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
 }
 
@@ -319,6 +352,7 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
 
 tl_status tl_destroy(tl_ctx* ctx) {
   if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
   delete ctx;
   return TL_OK;
 }
@@ -376,19 +410,34 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   rm.lane = lane;
   rm.p0 = p0;
   const int d = C.d_model;
-  TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
+  {
+    KScope k(ctx, TL_K_EMBED, s);
+    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
+  }
   for (int layer = 0; layer < C.n_pre + L; ++layer) {
     const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
     st = run_layer(ctx, B, layer, n, rm, false, s);
     if (st != TL_OK) return st;
   }
-  if (d_hidden) TL_HIP(hipMemcpyAsync(d_hidden, ctx->x, (size_t)n * d * 4, hipMemcpyDeviceToDevice, s));
+  if (d_hidden) {
+    KScope k(ctx, TL_K_COPY, s);
+    TL_HIP(hipMemcpyAsync(d_hidden, ctx->x, (size_t)n * d * 4, hipMemcpyDeviceToDevice, s));
+  }
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
-    TL_HIP(tl::launch_rmsnorm(ctx->x + (size_t)(n - 1) * d, ctx->final_norm, C.rms_eps, 1, d, ctx->h, s));
     tl::RowMap one{};
-    TL_HIP(tl::launch_head_z(ctx->h, 1, ctx->head, C.vocab, d, lg, one, s));
-    if (d_next) TL_HIP(tl::launch_argmax(lg, 1, C.vocab, one, d_next, s));
+    {
+      KScope k(ctx, TL_K_NORM, s);
+      TL_HIP(tl::launch_rmsnorm(ctx->x + (size_t)(n - 1) * d, ctx->final_norm, C.rms_eps, 1, d, ctx->h, s));
+    }
+    {
+      KScope k(ctx, TL_K_HEAD, s);
+      TL_HIP(tl::launch_head_z(ctx->h, 1, ctx->head, C.vocab, d, lg, one, s));
+    }
+    if (d_next) {
+      KScope k(ctx, TL_K_ARGMAX, s);
+      TL_HIP(tl::launch_argmax(lg, 1, C.vocab, one, d_next, s));
+    }
   }
   ctx->len[lane] = p0 + n;
   ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
@@ -419,7 +468,10 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int d = C.d_model;
-  TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
+  {
+    KScope k(ctx, TL_K_EMBED, s);
+    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
+  }
   const int Lmax = ctx->loops[rows[0]];
   for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
     int Ml = 0;
@@ -430,15 +482,71 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   }
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
-    TL_HIP(tl::launch_rmsnorm(ctx->x, ctx->final_norm, C.rms_eps, M, d, ctx->h, s));
-    TL_HIP(tl::launch_head_z(ctx->h, M, ctx->head, C.vocab, d, lg, rm, s));
-    if (d_next) TL_HIP(tl::launch_argmax(lg, M, C.vocab, rm, d_next, s));
+    {
+      KScope k(ctx, TL_K_NORM, s);
+      TL_HIP(tl::launch_rmsnorm(ctx->x, ctx->final_norm, C.rms_eps, M, d, ctx->h, s));
+    }
+    {
+      KScope k(ctx, TL_K_HEAD, s);
+      TL_HIP(tl::launch_head_z(ctx->h, M, ctx->head, C.vocab, d, lg, rm, s));
+    }
+    if (d_next) {
+      KScope k(ctx, TL_K_ARGMAX, s);
+      TL_HIP(tl::launch_argmax(lg, M, C.vocab, rm, d_next, s));
+    }
   }
-  if (d_hidden) TL_HIP(tl::launch_scatter_rows(ctx->x, M, d, rm, d_hidden, s));
+  if (d_hidden) {
+    KScope k(ctx, TL_K_COPY, s);
+    TL_HIP(tl::launch_scatter_rows(ctx->x, M, d, rm, d_hidden, s));
+  }
   for (int l : rows) {
     ctx->len[l] += 1;
     ctx->depth[l] = std::min(ctx->depth[l], C.n_pre + ctx->loops[l]);
   }
+  return TL_OK;
+}
+
+tl_status tl_profile_begin(tl_ctx* ctx, int32_t max_launches) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (ctx->prof_on) return fail(TL_E_STATE, "a timing window is already open");
+  if (max_launches < 1 || max_launches > 1000000) return fail(TL_E_RANGE, "max_launches outside 1..1000000");
+  ctx->prof_ev.assign((size_t)2 * max_launches, nullptr);
+  for (auto& e : ctx->prof_ev) {
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      for (auto& x : ctx->prof_ev)
+        if (x) (void)hipEventDestroy(x);
+      ctx->prof_ev.clear();
+      return fail(TL_E_HIP, std::string("hipEventCreate: ") + hipGetErrorString(err));
+    }
+  }
+  ctx->prof_kind.assign(max_launches, 0);
+  ctx->prof_cap = max_launches;
+  ctx->prof_used = 0;
+  ctx->prof_on = true;
+  return TL_OK;
+}
+
+tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (!ctx->prof_on) return fail(TL_E_STATE, "no timing window is open");
+  if (!total_ms || !count) return fail(TL_E_INVAL, "output arrays are NULL");
+  for (int k = 0; k < TL_K_COUNT; ++k) {
+    total_ms[k] = 0.0;
+    count[k] = 0;
+  }
+  hipError_t err = hipSuccess;
+  for (int i = 0; i < ctx->prof_used && err == hipSuccess; ++i) {
+    err = hipEventSynchronize(ctx->prof_ev[2 * i + 1]);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, ctx->prof_ev[2 * i], ctx->prof_ev[2 * i + 1]);
+    total_ms[ctx->prof_kind[i]] += ms;
+    count[ctx->prof_kind[i]] += 1;
+  }
+  for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
+  ctx->prof_ev.clear();
+  ctx->prof_on = false;
+  if (err != hipSuccess) return fail(TL_E_HIP, std::string("event timing: ") + hipGetErrorString(err));
   return TL_OK;
 }
 

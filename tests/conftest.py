@@ -20,8 +20,12 @@ def ensure_library():
     """Build libtl.so from source if it is not there yet, then import the binding."""
     lib = os.path.join(ROOT, "looped_weight_shared_amd", "libtl.so")
     if not os.path.exists(lib):
-        from looped_weight_shared_amd.build import build
-        build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import looped_weight_shared_amd
     return looped_weight_shared_amd
 

@@ -209,10 +209,15 @@ tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, i
 tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* d_q,
                             uint16_t* d_scales, void* stream);
 /* C[m][n] = sum_k A[m][k] * W[n][k] over a packed linear, fp32 out [M][N].
- * A is fp16 [M][K] row-major. M >= 1 (M <= 16 runs the decode GEMV kernel,
- * larger M the prefill GEMM kernel); fp32 accumulation. */
+ * A is fp16 [M][K] row-major. M >= 1: M <= 8 runs the decode GEMV kernel,
+ * larger M the prefill GEMM kernel with the launch plan the forward pass
+ * uses for that shape (including its K split); fp32 accumulation.
+ * d_ws: scratch of tl_w4_linear_ws_bytes(N, K, M) bytes (may be NULL when
+ * that is 0), 256-byte aligned, owned by the caller; calls sharing one d_ws
+ * must not overlap. */
+size_t tl_w4_linear_ws_bytes(int32_t N, int32_t K, int32_t M);
 tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M,
-                       float* d_C, void* stream);
+                       float* d_C, void* d_ws, void* stream);
 /* Per-row symmetric INT8 quantizer of the KV cache (bit-exact definition:
  * amax = max|x|; s = fp16(amax / 127) with a correctly rounded float32
  * division; q = clamp(rint_half_even(x / float(s)), -127, 127), 0 if s == 0).

@@ -24,7 +24,7 @@ __all__ = [
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
-    "tl_qlinear_unpack", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
+    "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
     "KERNEL_KINDS", "EXPORTED",
 ]
 
@@ -92,7 +92,8 @@ _SIGS = {
     "tl_qlinear_packed_bytes": (_sz, [_i32, _i32]),
     "tl_qlinear_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "tl_qlinear_unpack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
-    "tl_w4_linear": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "tl_w4_linear_ws_bytes": (_sz, [_i32, _i32, _i32]),
+    "tl_w4_linear": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "tl_kv_quantize_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_profile_begin": (ctypes.c_int, [_vp, _i32]),
     "tl_profile_end": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]),
@@ -210,8 +211,12 @@ def tl_qlinear_unpack(packed, N: int, K: int, q, scales, stream=None) -> None:
     _check(lib.tl_qlinear_unpack(_ptr(packed), N, K, _ptr(q), _ptr(scales), _stream(stream)))
 
 
-def tl_w4_linear(packed, N: int, K: int, A, M: int, C, stream=None) -> None:
-    _check(lib.tl_w4_linear(_ptr(packed), N, K, _ptr(A), M, _ptr(C), _stream(stream)))
+def tl_w4_linear_ws_bytes(N: int, K: int, M: int) -> int:
+    return lib.tl_w4_linear_ws_bytes(N, K, M)
+
+
+def tl_w4_linear(packed, N: int, K: int, A, M: int, C, ws, stream=None) -> None:
+    _check(lib.tl_w4_linear(_ptr(packed), N, K, _ptr(A), M, _ptr(C), _ptr(ws), _stream(stream)))
 
 
 def tl_kv_quantize_rows(x, rows: int, hd: int, q, s, stream=None) -> None:

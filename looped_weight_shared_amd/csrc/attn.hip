@@ -13,10 +13,9 @@
 // MFMAs run on the codes and the per-key scales multiply the score columns
 // and the probabilities (P is rounded to fp16 for the PV MFMA).
 //
-// Decode: one query per lane; the context is cut in 128-key chunks, each
-// block (2 waves) scores its chunk with 16 lanes per key (8 dims each), keeps
-// the chunk max/sum and the unnormalised P V in fp32, and a combine pass
-// merges the chunks of a head in chunk order.
+// Decode: one query per lane; see attn_decode_kernel below.
+#include <type_traits>
+
 #include "tl_device.h"
 #include "tl_kernels.h"
 
@@ -214,137 +213,299 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 }
 
 // ------------------------------------------------------------------ decode
-constexpr int kChunk = 128;  // keys per decode block (2 waves x 64)
+// A block (8 waves) covers up to 512 keys of the context 0..pos of one row's
+// lane for one head; wave w takes the 64-key chunk 8*blockIdx.x + w. The wave
+// first issues every K and V load of its chunk (32 KiB in flight for FP16 KV),
+// then builds Q = fp16(RoPE(q)) for its 8 dims from the raw QKV projection.
+// The wave whose chunk holds the new position also rotates/rounds (and, in
+// INT8 mode, quantizes) the new K and V, stores them in the cache and scores
+// that key from registers. Lanes are 16 per key (8 dims each) x 4 keys per
+// pass. Waves merge in LDS in wave order; a row whose context spans several
+// blocks gets its blocks merged in block order by attn_merge_kernel.
+constexpr int kDecChunk = 64;
+constexpr int kDecWaves = 8;
+constexpr int kDecPart = kDecChunk * kDecWaves;  // keys per block
 
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S) {
-  const int nch = (S + kChunk - 1) / kChunk;
-  return (size_t)max_rows * H * nch * (hd + 2);
+  const int np = (S + kDecPart - 1) / kDecPart;
+  return (size_t)max_rows * H * np * (hd + 2);
 }
 
-template <int HD>
-__global__ __launch_bounds__(128) void attn_decode_kernel(const uint16_t* __restrict__ q, RowMap rm, KvGeom kv,
-                                                          int layer, float* __restrict__ part) {
+template <int HD, bool I8>
+__global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float* __restrict__ qkv, RowMap rm,
+                                                                     const float* __restrict__ rope_cs, KvGeom kv,
+                                                                     int layer, float* __restrict__ part, int np_max,
+                                                                     uint16_t* __restrict__ o) {
   constexpr int LPK = HD / 8;    // lanes per key
-  constexpr int KPP = 64 / LPK;  // keys per wave pass
-  constexpr int NP = 64 / KPP;   // passes per wave (64 keys per wave)
-  __shared__ float red_m[2], red_l[2];
-  __shared__ float red_o[2][HD];
-
-  const int chunk = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
-  const int nch = gridDim.x;
-  const int lane_id = rm.row_lane[m];
-  const int ctx = rm.row_pos[m] + 1;
-  const int c0 = chunk * kChunk;
-  if (c0 >= ctx) return;  // whole block exits: nothing to do for this chunk
+  constexpr int KPP = 64 / LPK;  // keys per pass
+  constexpr int NP = kDecChunk / KPP;
+  constexpr int HALF = HD / 2;
+  __shared__ float red_o[kDecWaves][HD];
+  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
+  const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
+  const int pos = rm.row_pos[m], ctx = pos + 1;
+  const int nparts = (ctx + kDecPart - 1) / kDecPart;
+  if (bp >= nparts) return;  // the whole block exits
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
-  const int sub = ln % LPK, kg = ln / LPK;
-  const int d0 = sub * 8;
+  const int sub = ln % LPK, kg = ln / LPK, d0 = sub * 8;
   const int d = kv.H * HD;
+  const int lane_id = rm.row_lane[m];
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
-  const float scale = 1.0f / sqrtf((float)HD);
+  const int rowb = I8 ? HD : 2 * HD;
+  const int k0 = (bp * kDecWaves + wave) * kDecChunk;
+  const bool active = k0 <= pos;
 
+  // ---- all loads of the chunk's cached keys (positions < pos): 8 dims per
+  // lane, fp16 (16 B) or int8 codes (8 B) plus the row scales
+  using Row = typename std::conditional<I8, uint2, u32x4_t>::type;
+  Row kr[NP], vr[NP];
+  float ks[I8 ? NP : 1], vs[I8 ? NP : 1];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int key = k0 + p * KPP + kg;
+    kr[p] = vr[p] = Row{};
+    if constexpr (I8) ks[p] = vs[p] = 1.f;
+    if (key < pos) {
+      kr[p] = *reinterpret_cast<const Row*>(cp.k + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
+      vr[p] = *reinterpret_cast<const Row*>(cp.v + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
+      if constexpr (I8) {
+        ks[p] = h2f(cp.ks[key]);
+        vs[p] = h2f(cp.vs[key]);
+      }
+    }
+  }
+
+  // ---- Q = fp16(RoPE(q)) for dims d0..d0+7 (pair partner is dim +-HALF)
+  const float* row = qkv + (size_t)m * 3 * d;
+  const float* cosr = rope_cs + (size_t)pos * HALF;
+  const float* sinr = rope_cs + (size_t)kv.S * HALF + (size_t)pos * HALF;
+  const bool lo = d0 < HALF;
+  const int i0 = lo ? d0 : d0 - HALF;  // pair index of the first dim
   float qv[8];
   {
-    const half8_t qh =
-        __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(q + (size_t)m * d + h * HD + d0));
+    const float* qh = row + h * HD;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qv[j] = (float)qh[j];
+    for (int j = 0; j < 8; ++j) {
+      _Float16 r1, r2;
+      rope_pair(qh[i0 + j], qh[i0 + j + HALF], cosr[i0 + j], sinr[i0 + j], &r1, &r2);
+      qv[j] = (float)(lo ? r1 : r2);
+    }
   }
-  const int rowb = kv.int8 ? HD : HD * 2;
+  // ---- the new key/value (only the chunk that holds pos)
+  const bool own = (pos >= k0) && (pos < k0 + kDecChunk);
+  float kn[8], vn[8], ksn = 1.f, vsn = 1.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kn[j] = vn[j] = 0.f;
+  if (own) {
+    const float* kh = row + d + h * HD;
+    const float* vh = row + 2 * d + h * HD;
+    _Float16 kf[8], vf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 r1, r2;
+      rope_pair(kh[i0 + j], kh[i0 + j + HALF], cosr[i0 + j], sinr[i0 + j], &r1, &r2);
+      kf[j] = lo ? r1 : r2;
+      vf[j] = (_Float16)vh[d0 + j];
+    }
+    const bool writer = (kg == 0);
+    if constexpr (I8) {
+      float ka = 0.f, va = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ka = fmaxf(ka, fabsf((float)kf[j]));
+        va = fmaxf(va, fabsf((float)vf[j]));
+      }
+#pragma unroll
+      for (int off = LPK / 2; off >= 1; off >>= 1) {
+        ka = fmaxf(ka, __shfl_xor(ka, off, 64));
+        va = fmaxf(va, __shfl_xor(va, off, 64));
+      }
+      const _Float16 s16k = kv_scale(ka), s16v = kv_scale(va);
+      ksn = (float)s16k;
+      vsn = (float)s16v;
+      uint32_t kw[2] = {0, 0}, vw[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qk = kv_code((float)kf[j], ksn), qvv = kv_code((float)vf[j], vsn);
+        kn[j] = (float)qk;
+        vn[j] = (float)qvv;
+        kw[j >> 2] |= ((uint32_t)(qk & 0xFF)) << (8 * (j & 3));
+        vw[j >> 2] |= ((uint32_t)(qvv & 0xFF)) << (8 * (j & 3));
+      }
+      if (writer) {
+        uint8_t* K = const_cast<uint8_t*>(cp.k) + (size_t)pos * rowb + d0;
+        uint8_t* V = const_cast<uint8_t*>(cp.v) + (size_t)pos * rowb + d0;
+        *reinterpret_cast<uint2*>(K) = make_uint2(kw[0], kw[1]);
+        *reinterpret_cast<uint2*>(V) = make_uint2(vw[0], vw[1]);
+        if (sub == 0) {
+          const_cast<uint16_t*>(cp.ks)[pos] = __builtin_bit_cast(uint16_t, s16k);
+          const_cast<uint16_t*>(cp.vs)[pos] = __builtin_bit_cast(uint16_t, s16v);
+        }
+      }
+    } else {
+      half8_t kh8, vh8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kh8[j] = kf[j];
+        vh8[j] = vf[j];
+        kn[j] = (float)kf[j];
+        vn[j] = (float)vf[j];
+      }
+      if (writer) {
+        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.k) + (size_t)pos * rowb + d0 * 2) = kh8;
+        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.v) + (size_t)pos * rowb + d0 * 2) = vh8;
+      }
+    }
+  }
+
+  // ---- scores, chunk max
+  const float scale = 1.0f / sqrtf((float)HD);
   float sc[NP];
   float mx = -INFINITY;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int key = c0 + wave * 64 + p * KPP + kg;
-    float s = -INFINITY;
-    if (key < ctx) {
-      const half8_t kh = __builtin_bit_cast(half8_t, load8_as_f16(cp.k + (size_t)key * rowb, d0, kv.int8));
-      float t = 0.f;
+    const int key = k0 + p * KPP + kg;
+    float t = 0.f;
+    if (key < pos) {
+      if constexpr (I8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t = fmaf(qv[j], (float)kh[j], t);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = j < 4 ? kr[p].x : kr[p].y;
+          t = fmaf(qv[j], (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF), t);
+        }
+      } else {
+        const half8_t kh8 = __builtin_bit_cast(half8_t, kr[p]);
 #pragma unroll
-      for (int off = LPK / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-      s = t * scale * (kv.int8 ? h2f(cp.ks[key]) : 1.0f);
+        for (int j = 0; j < 8; ++j) t = fmaf(qv[j], (float)kh8[j], t);
+      }
+    } else if (key == pos) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t = fmaf(qv[j], kn[j], t);
     }
-    sc[p] = s;
-    mx = fmaxf(mx, s);
+#pragma unroll
+    for (int off = LPK / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+    float kscale = ksn;
+    if constexpr (I8) kscale = key < pos ? ks[p] : ksn;
+    sc[p] = key <= pos ? t * scale * kscale : -INFINITY;
+    mx = fmaxf(mx, sc[p]);
   }
-  mx = wave_max(mx);
-  if (ln == 0) red_m[wave] = mx;
-  __syncthreads();
-  const float cm = fmaxf(red_m[0], red_m[1]);  // chunk max (finite: key c0 < ctx)
-  float lsum = 0.f;
-  float ov[8];
+  mx = wave_max(mx);  // -inf only for a wave whose chunk starts after pos
+  float lsum = 0.f, ov[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) ov[j] = 0.f;
+  if (active) {
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int key = c0 + wave * 64 + p * KPP + kg;
-    if (key < ctx) {
-      const float pr = expf(sc[p] - cm);
+    for (int p = 0; p < NP; ++p) {
+      const int key = k0 + p * KPP + kg;
+      const float pr = key <= pos ? expf(sc[p] - mx) : 0.f;
       if (sub == 0) lsum += pr;
-      const float pv = pr * (kv.int8 ? h2f(cp.vs[key]) : 1.0f);
-      const half8_t vh = __builtin_bit_cast(half8_t, load8_as_f16(cp.v + (size_t)key * rowb, d0, kv.int8));
+      if (key < pos) {
+        if constexpr (I8) {
+          const float pv = pr * vs[p];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ov[j] = fmaf(pv, (float)vh[j], ov[j]);
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t w = j < 4 ? vr[p].x : vr[p].y;
+            ov[j] = fmaf(pv, (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF), ov[j]);
+          }
+        } else {
+          const float pv = pr;
+          const half8_t vh8 = __builtin_bit_cast(half8_t, vr[p]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ov[j] = fmaf(pv, (float)vh8[j], ov[j]);
+        }
+      } else if (key == pos) {
+        const float pv = pr * vsn;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ov[j] = fmaf(pv, vn[j], ov[j]);
+      }
     }
   }
   lsum = wave_sum(lsum);
-  // reduce ov over the KPP key groups of the wave (lanes with equal `sub`)
 #pragma unroll
   for (int off = LPK; off < 64; off <<= 1)
 #pragma unroll
     for (int j = 0; j < 8; ++j) ov[j] += __shfl_xor(ov[j], off, 64);
-  if (ln == 0) red_l[wave] = lsum;
   if (kg == 0)
 #pragma unroll
     for (int j = 0; j < 8; ++j) red_o[wave][d0 + j] = ov[j];
+  if (ln == 0) {
+    red_m[wave] = mx;
+    red_l[wave] = lsum;
+  }
   __syncthreads();
-  float* dst = part + ((size_t)(m * kv.H + h) * nch + chunk) * (HD + 2);
-  for (int i = tid; i < HD; i += 128) dst[i] = red_o[0][i] + red_o[1][i];
-  if (tid == 0) {
-    dst[HD] = cm;
-    dst[HD + 1] = red_l[0] + red_l[1];
-  }
-}
-
-__global__ void attn_combine_kernel(const float* __restrict__ part, RowMap rm, int H, int hd, int nch,
-                                    uint16_t* __restrict__ o) {
-  const int h = blockIdx.x, m = blockIdx.y;
-  const int ctx = rm.row_pos[m] + 1;
-  const int used = (ctx + kChunk - 1) / kChunk;
-  const float* base = part + (size_t)(m * H + h) * nch * (hd + 2);
-  float gm = -INFINITY;
-  for (int c = 0; c < used; ++c) gm = fmaxf(gm, base[c * (hd + 2) + hd]);
-  for (int i = threadIdx.x; i < hd; i += blockDim.x) {
+  // ---- merge the waves in wave order
+  float bm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) bm = fmaxf(bm, red_m[w]);
+  if (tid < HD) {
     float num = 0.f, den = 0.f;
-    for (int c = 0; c < used; ++c) {
-      const float w = expf(base[c * (hd + 2) + hd] - gm);
-      num = fmaf(w, base[c * (hd + 2) + i], num);
-      den = fmaf(w, base[c * (hd + 2) + hd + 1], den);
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      if (red_m[w] == -INFINITY) continue;  // chunk beyond the context
+      const float sw = expf(red_m[w] - bm);
+      num = fmaf(sw, red_o[w][tid], num);
+      den = fmaf(sw, red_l[w], den);
     }
-    o[(size_t)m * H * hd + h * hd + i] = f2h(num / den);
+    if (nparts == 1) {
+      o[(size_t)m * d + h * HD + tid] = f2h(num / den);
+    } else {
+      float* dst = part + ((size_t)(m * kv.H + h) * np_max + bp) * (HD + 2);
+      dst[tid] = num;
+      if (tid == 0) {
+        dst[HD] = bm;
+        dst[HD + 1] = den;
+      }
+    }
   }
 }
 
-hipError_t launch_attn_decode(const uint16_t* q, int M, const RowMap& rm, const KvGeom& kv, int layer,
-                              float* part, uint16_t* o, hipStream_t s) {
+// Rows whose context spans several blocks: merge the block results in block order.
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict__ part, RowMap rm, int H, int np_max,
+                                                        uint16_t* __restrict__ o) {
+  const int h = blockIdx.x, m = blockIdx.y;
+  const int nparts = (rm.row_pos[m] + 1 + kDecPart - 1) / kDecPart;
+  if (nparts < 2) return;
+  const float* base = part + (size_t)(m * H + h) * np_max * (HD + 2);
+  float gm = -INFINITY;
+  for (int q = 0; q < nparts; ++q) gm = fmaxf(gm, base[(size_t)q * (HD + 2) + HD]);
+  const int i = threadIdx.x;
+  float num = 0.f, den = 0.f;
+  for (int q = 0; q < nparts; ++q) {
+    const float* pq = base + (size_t)q * (HD + 2);
+    const float w = expf(pq[HD] - gm);
+    num = fmaf(w, pq[i], num);
+    den = fmaf(w, pq[HD + 1], den);
+  }
+  o[(size_t)m * H * HD + h * HD + i] = f2h(num / den);
+}
+
+template <int HD, bool I8>
+static void decode_launch(dim3 grid, int used, const float* qkv, const RowMap& rm, const float* rope_cs,
+                          const KvGeom& kv, int layer, float* part, int np_max, uint16_t* o, hipStream_t s) {
+  hipLaunchKernelGGL((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part,
+                     np_max, o);
+  if (used > 1)
+    hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, rm, kv.H, np_max, o);
+}
+
+hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+                              int layer, float* part, uint16_t* o, hipStream_t s) {
   int maxctx = 0;
   for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1);
-  const int nch = (kv.S + kChunk - 1) / kChunk;
-  const int used = (maxctx + kChunk - 1) / kChunk;
-  // Blocks beyond a row's context exit at once; the grid spans the longest row.
+  const int np_max = (kv.S + kDecPart - 1) / kDecPart;
+  const int used = (maxctx + kDecPart - 1) / kDecPart;
   dim3 grid(used, kv.H, M);
-  (void)nch;
-  if (kv.hd == 128)
-    hipLaunchKernelGGL(attn_decode_kernel<128>, grid, dim3(128), 0, s, q, rm, kv, layer, part);
+  if (kv.hd == 128 && kv.int8)
+    decode_launch<128, true>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+  else if (kv.hd == 128)
+    decode_launch<128, false>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+  else if (kv.hd == 64 && kv.int8)
+    decode_launch<64, true>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 64)
-    hipLaunchKernelGGL(attn_decode_kernel<64>, grid, dim3(128), 0, s, q, rm, kv, layer, part);
+    decode_launch<64, false>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(kv.H, M), dim3(128), 0, s, part, rm, kv.H, kv.hd, used, o);
   return hipGetLastError();
 }
 

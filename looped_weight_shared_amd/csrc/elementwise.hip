@@ -28,25 +28,90 @@ hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, con
 }
 
 // ------------------------------------------------------------------ RMSNorm
-// h[m] = fp16(gamma * x[m] / sqrt(mean(x[m]^2) + eps)); one block per row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const uint16_t* __restrict__ g,
-                                                      float eps, int d, uint16_t* __restrict__ h) {
+// One block (256 threads) per row: x += the pending split-K partials of the
+// residual GEMM that produced x (split order), then h = fp16(gamma * x /
+// sqrt(mean(x^2) + eps)). Thread t owns the float4 chunks t, t + 256, ...
+// (CH of them); every load is issued before the first store.
+constexpr int kMaxSplits = kMaxSplitK;
+
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pending pend, int M,
+                                                      const uint16_t* __restrict__ g, float eps, int d,
+                                                      uint16_t* __restrict__ h) {
   __shared__ float part[4];
   const int m = blockIdx.x, tid = threadIdx.x;
-  const float* xr = x + (size_t)m * d;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
+  const int nc = d / 4;
+  float4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = tid + 256 * c;
+    v[c] = ci < nc ? xr[ci] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (pend.part) {
+    const float4* pp = reinterpret_cast<const float4*>(pend.part) + (size_t)m * nc;
+    const size_t split = (size_t)M * nc;
+    float4 p[CH][kMaxSplits];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) {
+        const int ci = tid + 256 * c;
+        p[c][s] = (ci < nc && s < pend.S) ? pp[s * split + ci] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      float4 a = p[c][0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s)
+        if (s < pend.S) {
+          a.x += p[c][s].x;
+          a.y += p[c][s].y;
+          a.z += p[c][s].z;
+          a.w += p[c][s].w;
+        }
+      v[c].x += a.x;
+      v[c].y += a.y;
+      v[c].z += a.z;
+      v[c].w += a.w;
+      const int ci = tid + 256 * c;
+      if (ci < nc) xr[ci] = v[c];
+    }
+  }
   float acc = 0.f;
-  for (int k = tid; k < d; k += 256) acc += xr[k] * xr[k];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   acc = wave_sum(acc);
   if ((tid & 63) == 0) part[tid >> 6] = acc;
   __syncthreads();
   const float ss = part[0] + part[1] + part[2] + part[3];
   const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int k = tid; k < d; k += 256) h[(size_t)m * d + k] = f2h((xr[k] * rinv) * h2f(g[k]));
+  if (!h) return;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = tid + 256 * c;
+    if (ci >= nc) continue;
+    const int k = ci * 4;
+    const uint2 gr = *reinterpret_cast<const uint2*>(g + k);
+    const float g0 = h2f(gr.x & 0xFFFF), g1 = h2f(gr.x >> 16), g2 = h2f(gr.y & 0xFFFF), g3 = h2f(gr.y >> 16);
+    const uint32_t lo = (uint32_t)f2h((v[c].x * rinv) * g0) | ((uint32_t)f2h((v[c].y * rinv) * g1) << 16);
+    const uint32_t hi = (uint32_t)f2h((v[c].z * rinv) * g2) | ((uint32_t)f2h((v[c].w * rinv) * g3) << 16);
+    *reinterpret_cast<uint2*>(h + (size_t)m * d + k) = make_uint2(lo, hi);
+  }
 }
 
-hipError_t launch_rmsnorm(const float* x, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
+hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
                           hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, x, gamma, eps, d, h);
+  if (d % 4 || d > 8192 || pend.S > kMaxSplits) return hipErrorInvalidValue;
+  const int ch = (d / 4 + 255) / 256;
+  if (ch <= 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else if (ch <= 2)
+    hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else if (ch <= 4)
+    hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
   return hipGetLastError();
 }
 
@@ -58,16 +123,11 @@ hipError_t launch_rmsnorm(const float* x, const uint16_t* gamma, float eps, int 
 __device__ __forceinline__ void quant_pair(float a, float b, bool valid, int8_t* qa, int8_t* qb, uint16_t* sc) {
   float am = valid ? fmaxf(fabsf(a), fabsf(b)) : 0.f;
   am = wave_max(am);
-  const _Float16 s16 = (_Float16)__fdiv_rn(am, 127.0f);
+  const _Float16 s16 = kv_scale(am);
   const float sf = (float)s16;
   if (valid) {
-    float x0 = 0.f, x1 = 0.f;
-    if (sf > 0.f) {
-      x0 = fminf(fmaxf(rintf(__fdiv_rn(a, sf)), -127.f), 127.f);
-      x1 = fminf(fmaxf(rintf(__fdiv_rn(b, sf)), -127.f), 127.f);
-    }
-    *qa = (int8_t)(int)x0;
-    *qb = (int8_t)(int)x1;
+    *qa = (int8_t)kv_code(a, sf);
+    *qb = (int8_t)kv_code(b, sf);
   }
   *sc = __builtin_bit_cast(uint16_t, s16);
 }
@@ -103,7 +163,7 @@ hipError_t launch_kv_quantize_rows(const uint16_t* x, int rows, int hd, int8_t* 
 // and k by angle pos * base^(-2i/hd) (cos/sin table computed on the host in
 // double precision), rounds Q, K, V to fp16, writes Q and stores K, V in the
 // cache of the row's lane at its position (FP16, or INT8 + scale).
-__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int M, RowMap rm,
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int S, int M, RowMap rm,
                                                       const float* __restrict__ rope_cs, KvGeom kv, int layer,
                                                       uint16_t* __restrict__ qout) {
   const int m = blockIdx.y;
@@ -114,20 +174,27 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   const bool valid = ln < half;
   const int lane = row_lane(rm, m), pos = row_pos(rm, m);
   const float* row = qkv + (size_t)m * 3 * d;
+  const size_t split = (size_t)M * 3 * d;  // stride between split-K partials
+  auto val = [&](int col) {
+    float v = row[col];
+    for (int s = 1; s < S; ++s) v += row[s * split + col];
+    return v;
+  };
   float c = 0.f, sn = 0.f;
   float q1 = 0.f, q2 = 0.f, k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
   if (valid) {
     c = rope_cs[(size_t)pos * half + ln];
     sn = rope_cs[(size_t)kv.S * half + (size_t)pos * half + ln];
-    q1 = row[h * hd + ln];
-    q2 = row[h * hd + ln + half];
-    k1 = row[d + h * hd + ln];
-    k2 = row[d + h * hd + ln + half];
-    v1 = row[2 * d + h * hd + ln];
-    v2 = row[2 * d + h * hd + ln + half];
+    q1 = val(h * hd + ln);
+    q2 = val(h * hd + ln + half);
+    k1 = val(d + h * hd + ln);
+    k2 = val(d + h * hd + ln + half);
+    v1 = val(2 * d + h * hd + ln);
+    v2 = val(2 * d + h * hd + ln + half);
   }
-  const _Float16 Q1 = (_Float16)(q1 * c - q2 * sn), Q2 = (_Float16)(q2 * c + q1 * sn);
-  const _Float16 K1 = (_Float16)(k1 * c - k2 * sn), K2 = (_Float16)(k2 * c + k1 * sn);
+  _Float16 Q1, Q2, K1, K2;
+  rope_pair(q1, q2, c, sn, &Q1, &Q2);
+  rope_pair(k1, k2, c, sn, &K1, &K2);
   const _Float16 V1 = (_Float16)v1, V2 = (_Float16)v2;
   if (valid) {
     qout[(size_t)m * d + h * hd + ln] = __builtin_bit_cast(uint16_t, Q1);
@@ -167,114 +234,208 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_rope_kv(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+hipError_t launch_rope_kv(const float* qkv, int S, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                           int layer, uint16_t* q_out, hipStream_t s) {
-  if (kv.hd > 128 || kv.hd % 2) return hipErrorInvalidValue;
+  if (kv.hd > 128 || kv.hd % 2 || S < 1) return hipErrorInvalidValue;
   dim3 grid((kv.H + 3) / 4, M);
-  hipLaunchKernelGGL(rope_kv_kernel, grid, dim3(256), 0, s, qkv, M, rm, rope_cs, kv, layer, q_out);
+  hipLaunchKernelGGL(rope_kv_kernel, grid, dim3(256), 0, s, qkv, S, M, rm, rope_cs, kv, layer, q_out);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ head
-// logits[row][v] = sum_k z[m][k] * Head[v][k] for M <= 16 normed rows z (fp16
-// [M][d], produced by rmsnorm_kernel). A wave owns one 16-row block of the
-// head and walks K in 32-deep MFMA steps, 8 steps of loads in flight.
-__global__ __launch_bounds__(256) void head_kernel(const uint16_t* __restrict__ z, int M,
-                                                   const uint16_t* __restrict__ head, int V, int d,
-                                                   float* __restrict__ logits, RowMap rm) {
+// Final RMSNorm and head projection in one launch, plus per-block argmax
+// candidates. Block b owns vocab rows 64b..64b+63 (4 waves x 16 rows). Its
+// head rows are requested first (they do not depend on the activations), then
+// the block normalises the M <= 8 residual rows into LDS (z = fp16(gamma x /
+// rms)), and each wave walks K in 32-deep MFMA steps. Every block writes its
+// logits and, per row, its (max, lowest index) candidate.
+constexpr int kHeadSteps = 16;  // 32-deep k-steps of head rows in flight per wave
+constexpr int kHeadKpt = 8;     // residual elements per thread (d <= 2048) held in registers
+
+__global__ __launch_bounds__(256) void head_kernel(const float* __restrict__ x, int M, const uint16_t* __restrict__ gamma,
+                                                   float eps, const uint16_t* __restrict__ head, int V, int d,
+                                                   float* __restrict__ logits, RowMap rm, float* __restrict__ cval,
+                                                   int* __restrict__ cidx) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int lda = d + 8;
   _Float16* Z = reinterpret_cast<_Float16*>(smem);
+  __shared__ float red[4][8];
+  __shared__ float bval[4][8];
+  __shared__ int bidx[4][8];
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int l16 = ln & 15, lq = ln >> 4;
-  for (int i = tid; i < M * (d / 8); i += 256) {
-    const int m = i / (d / 8), c = (i % (d / 8)) * 8;
-    *reinterpret_cast<u32x4_t*>(Z + m * lda + c) = *reinterpret_cast<const u32x4_t*>(z + (size_t)m * d + c);
-  }
-  __syncthreads();
   const int nb = blockIdx.x * 4 + wave;
   const int v = nb * 16 + l16;
   const bool vrow = v < V;
+  const int nsteps = d / 32;
+  u32x4_t w[kHeadSteps];
+  auto load_w = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < kHeadSteps; ++j) {
+      w[j] = (u32x4_t){0, 0, 0, 0};
+      if (vrow && s0 + j < nsteps)
+        w[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(head + (size_t)v * d + (s0 + j) * 32 + 8 * lq));
+    }
+  };
+  load_w(0);
+  // ---- z = fp16(RMSNorm(x)) for the M rows; x and gamma in one round trip
+  if (d <= kHeadKpt * 256) {
+    float xv[8][kHeadKpt], gv[kHeadKpt];
+#pragma unroll
+    for (int i = 0; i < kHeadKpt; ++i) {
+      const int k = tid + 256 * i;
+      gv[i] = k < d ? h2f(gamma[k]) : 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) xv[m][i] = (m < M && k < d) ? x[(size_t)m * d + k] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < M) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < kHeadKpt; ++i) a += xv[m][i] * xv[m][i];
+        a = wave_sum(a);
+        if (ln == 0) red[wave][m] = a;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < M) {
+        const float rinv = 1.0f / sqrtf((red[0][m] + red[1][m] + red[2][m] + red[3][m]) / (float)d + eps);
+#pragma unroll
+        for (int i = 0; i < kHeadKpt; ++i) {
+          const int k = tid + 256 * i;
+          if (k < d) Z[m * lda + k] = (_Float16)((xv[m][i] * rinv) * gv[i]);
+        }
+      }
+    }
+  } else {
+    for (int m = 0; m < M; ++m) {
+      const float* xr = x + (size_t)m * d;
+      float a = 0.f;
+      for (int k = tid; k < d; k += 256) a += xr[k] * xr[k];
+      a = wave_sum(a);
+      if (ln == 0) red[wave][m] = a;
+    }
+    __syncthreads();
+    for (int m = 0; m < M; ++m) {
+      const float rinv = 1.0f / sqrtf((red[0][m] + red[1][m] + red[2][m] + red[3][m]) / (float)d + eps);
+      const float* xr = x + (size_t)m * d;
+      for (int k = tid; k < d; k += 256) Z[m * lda + k] = (_Float16)((xr[k] * rinv) * h2f(gamma[k]));
+    }
+  }
+  __syncthreads();
   const bool arow = l16 < M;
   const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int nsteps = d / 32;
-  for (int s0 = 0; s0 < nsteps; s0 += 8) {
-    u32x4_t w[8];
+  for (int s0 = 0; s0 < nsteps; s0 += kHeadSteps) {
+    if (s0) load_w(s0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w[j] = (u32x4_t){0, 0, 0, 0};
-      if (vrow && s0 + j < nsteps)
-        w[j] = *reinterpret_cast<const u32x4_t*>(head + (size_t)v * d + (s0 + j) * 32 + 8 * lq);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kHeadSteps; ++j) {
       if (s0 + j < nsteps) {
-        const half8_t af =
-            arow ? *reinterpret_cast<const half8_t*>(Z + l16 * lda + (s0 + j) * 32 + 8 * lq) : hz;
+        const half8_t af = arow ? *reinterpret_cast<const half8_t*>(Z + l16 * lda + (s0 + j) * 32 + 8 * lq) : hz;
         acc = mfma16(af, __builtin_bit_cast(half8_t, w[j]), acc);
       }
     }
   }
+  // ---- logits and per-row candidates; lane holds row m = 4lq + r, vocab v
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * lq + r;
-    if (m < M && vrow) logits[(size_t)out_row(rm, m) * V + v] = acc[r];
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (m < M && vrow) {
+      logits[(size_t)out_row(rm, m) * V + v] = acc[r];
+      bv = acc[r];
+      bi = v;
+    }
+    // max over the 16 lanes of this row group, ties to the lowest index
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (l16 == 0 && m < 8) {
+      bval[wave][m] = bv;
+      bidx[wave][m] = bi;
+    }
+  }
+  __syncthreads();
+  const int nblk = gridDim.x;
+  if (tid < M) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int wv = 0; wv < 4; ++wv)
+      if (bval[wv][tid] > bv || (bval[wv][tid] == bv && bidx[wv][tid] < bi)) {
+        bv = bval[wv][tid];
+        bi = bidx[wv][tid];
+      }
+    cval[(size_t)tid * nblk + blockIdx.x] = bv;
+    cidx[(size_t)tid * nblk + blockIdx.x] = bi;
   }
 }
 
-hipError_t launch_head_z(const uint16_t* z, int M, const uint16_t* head, int V, int d, float* logits,
-                         const RowMap& rm, hipStream_t s) {
-  if (M < 1 || M > 16 || d % 32) return hipErrorInvalidValue;
-  const size_t lds = (size_t)M * (d + 8) * 2;
-  const int nblk = (V + 15) / 16;
-  hipLaunchKernelGGL(head_kernel, dim3((nblk + 3) / 4), dim3(256), lds, s, z, M, head, V, d, logits, rm);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ argmax
-// Greedy next token per row: the largest logit, ties to the lowest index.
-__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int V, RowMap rm,
-                                                      int32_t* __restrict__ next) {
-  __shared__ float bv[16];
-  __shared__ int bi[16];
+// Greedy next token of each row from the head blocks' candidates, scanned in
+// block order with ties to the lowest index.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ cval, const int* __restrict__ cidx,
+                                                     int nblk, RowMap rm, int32_t* __restrict__ next) {
+  __shared__ float bv_s[4];
+  __shared__ int bi_s[4];
   const int m = blockIdx.x, tid = threadIdx.x;
-  const float* lg = logits + (size_t)out_row(rm, m) * V;
-  float best = -INFINITY;
-  int idx = 0x7fffffff;
-  for (int v = tid; v < V; v += 1024) {
-    const float x = lg[v];
-    if (x > best) {
-      best = x;
-      idx = v;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int b = tid; b < nblk; b += 256) {
+    const float cv = cval[(size_t)m * nblk + b];
+    const int ci = cidx[(size_t)m * nblk + b];
+    if (cv > bv || (cv == bv && ci < bi)) {
+      bv = cv;
+      bi = ci;
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const float ob = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(idx, o, 64);
-    if (ob > best || (ob == best && oi < idx)) {
-      best = ob;
-      idx = oi;
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
     }
   }
   if ((tid & 63) == 0) {
-    bv[tid >> 6] = best;
-    bi[tid >> 6] = idx;
+    bv_s[tid >> 6] = bv;
+    bi_s[tid >> 6] = bi;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < 16; ++w)
-      if (bv[w] > best || (bv[w] == best && bi[w] < idx)) {
-        best = bv[w];
-        idx = bi[w];
+    for (int w = 1; w < 4; ++w)
+      if (bv_s[w] > bv_s[0] || (bv_s[w] == bv_s[0] && bi_s[w] < bi_s[0])) {
+        bv_s[0] = bv_s[w];
+        bi_s[0] = bi_s[w];
       }
-    next[out_row(rm, m)] = idx == 0x7fffffff ? 0 : idx;
+    next[out_row(rm, m)] = bi_s[0] == 0x7fffffff ? 0 : bi_s[0];
   }
 }
 
-hipError_t launch_argmax(const float* logits, int M, int V, const RowMap& rm, int32_t* next, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(1024), 0, s, logits, V, rm, next);
+size_t head_scratch_bytes(int max_rows, int V) { return (size_t)max_rows * ((V + 63) / 64) * 8; }
+
+hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
+                       float* logits, const RowMap& rm, void* scratch, int32_t* next, hipStream_t s) {
+  if (M < 1 || M > 8 || d % 32) return hipErrorInvalidValue;
+  const size_t lds = (size_t)M * (d + 8) * 2;
+  const int nblk = (V + 63) / 64;
+  float* cval = static_cast<float*>(scratch);
+  int* cidx = reinterpret_cast<int*>(cval + (size_t)M * nblk);
+  hipLaunchKernelGGL(head_kernel, dim3(nblk), dim3(256), lds, s, x, M, gamma, eps, head, V, d, logits, rm, cval,
+                     cidx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !next) return e;
+  hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next);
   return hipGetLastError();
 }
 

@@ -73,8 +73,21 @@ size_t rope_bytes(const tl_config* c) { return al256((size_t)2 * c->max_seq * (c
 
 int tokens_cap(const tl_config* c) { return std::max(c->max_tokens, c->n_lanes); }
 
+// Largest split-K partial buffer any prefill GEMM of this model can need.
+size_t gemm_scratch_bytes(const tl_config* c) {
+  const int d = c->d_model, f = c->ffn_dim, T = tokens_cap(c);
+  size_t mx = 0;
+  for (int M = 1; M <= T; ++M) {
+    mx = std::max(mx, tl::w4_gemm_scratch_bytes(3 * d, d, M, false));
+    mx = std::max(mx, tl::w4_gemm_scratch_bytes(d, d, M, false));
+    mx = std::max(mx, tl::w4_gemm_scratch_bytes(2 * f, d, M, true));
+    mx = std::max(mx, tl::w4_gemm_scratch_bytes(d, f, M, false));
+  }
+  return mx;
+}
+
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -88,6 +101,8 @@ ActLayout act_layout(const tl_config* c) {
   L.a = off; off += al256(T * f * 2);
   L.part = off; off += al256(tl::attn_decode_scratch_floats(c->n_lanes, c->n_heads, c->head_dim, c->max_seq) * 4);
   L.logits = off; off += al256((size_t)c->n_lanes * c->vocab * 4);
+  L.gpart = off; off += al256(gemm_scratch_bytes(c));
+  L.hscr = off; off += al256(tl::head_scratch_bytes(c->n_lanes, c->vocab));
   L.total = off;
   return L;
 }
@@ -117,6 +132,9 @@ struct tl_ctx {
   uint16_t* a;
   float* part;
   float* logits;
+  float* gpart;      // split-K partial tiles of the prefill GEMM
+  tl::Pending pend;  // residual partials not yet added to x
+  void* hscr;        // head/argmax per-block candidates
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
   // kernel timing window
   bool prof_on = false;
@@ -145,21 +163,28 @@ struct KScope {
   }
 };
 
-tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, uint16_t* norm_buf, int M,
-                 const tl::Epi& e, hipStream_t s) {
-  if (gemv_fits(M, w.K) && M <= 8) {
+// Decode-shaped calls (M <= 8) use the split-K-in-block GEMV with the RMSNorm
+// fused; larger M uses the MFMA GEMM, whose K-split partials (if the plan
+// splits) are left for the consumer: *S_out receives the split count.
+tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, int M, const tl::Epi& e,
+                 int* S_out, hipStream_t s) {
+  *S_out = 1;
+  if (M <= 8 && gemv_fits(M, w.K)) {
     KScope k(c, kind, s);
     TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
     return TL_OK;
   }
   const uint16_t* A = src.a16;
   if (src.x32) {
+    // x += pending residual partials, then h = fp16(RMSNorm(x))
     KScope k(c, TL_K_NORM, s);
-    TL_HIP(tl::launch_rmsnorm(src.x32, src.gamma, src.eps, M, w.K, norm_buf, s));
-    A = norm_buf;
+    TL_HIP(tl::launch_rmsnorm(c->x, c->pend, src.gamma, src.eps, M, w.K, c->h, s));
+    c->pend = tl::Pending{nullptr, 1};
+    A = c->h;
   }
   KScope k(c, kind, s);
-  TL_HIP(tl::launch_w4_gemm(w, A, M, e, s));
+  TL_HIP(tl::launch_w4_gemm(w, A, M, e, c->gpart, s));
+  *S_out = tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
   return TL_OK;
 }
 
@@ -170,34 +195,49 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   const int d = c->cfg.d_model, f = c->cfg.ffn_dim;
   const float eps = c->cfg.rms_eps;
   tl_status st;
+  int S = 1;
   // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T
-  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, c->h, M,
-              tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, s);
+  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, M,
+              tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, &S, s);
   if (st != TL_OK) return st;
-  // RoPE on q, k; fp16 Q; K, V into cache layer `layer`
-  {
-    KScope k(c, TL_K_ROPE_KV, s);
-    TL_HIP(tl::launch_rope_kv(c->qkv, M, rm, c->rope, c->kv, layer, c->q, s));
-  }
-  // causal attention over the lane's cache
-  {
+  const float* qkv = S > 1 ? c->gpart : c->qkv;
+  if (decode) {
+    // RoPE, new K/V into cache layer `layer`, single-query attention
     KScope k(c, TL_K_ATTN, s);
-    if (decode)
-      TL_HIP(tl::launch_attn_decode(c->q, M, rm, c->kv, layer, c->part, c->o, s));
-    else
-      TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
+    TL_HIP(tl::launch_attn_decode(qkv, M, rm, c->rope, c->kv, layer, c->part, c->o, s));
+  } else {
+    // RoPE on q, k (summing the split-K partials); fp16 Q; K, V into cache layer `layer`
+    {
+      KScope k(c, TL_K_ROPE_KV, s);
+      TL_HIP(tl::launch_rope_kv(qkv, S, M, rm, c->rope, c->kv, layer, c->q, s));
+    }
+    KScope k(c, TL_K_ATTN, s);
+    TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
   }
-  // x += O W_o^T
-  st = linear(c, TL_K_O, B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, nullptr, M,
-              tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
+  // x += O W_o^T (deferred to the next RMSNorm when K is split)
+  st = linear(c, TL_K_O, B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d},
+              &S, s);
   if (st != TL_OK) return st;
+  if (S > 1) c->pend = tl::Pending{c->gpart, S};
   // a = fp16(silu(h2 W_gate^T) * h2 W_up^T), h2 = fp16(RMSNorm(x))
-  st = linear(c, TL_K_GATE_UP, B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, c->h, M,
-              tl::Epi{tl::EPI_SWIGLU, nullptr, c->a, f}, s);
+  st = linear(c, TL_K_GATE_UP, B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, M,
+              tl::Epi{tl::EPI_SWIGLU, nullptr, c->a, f}, &S, s);
   if (st != TL_OK) return st;
-  // x += a W_down^T
-  return linear(c, TL_K_DOWN, B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, nullptr, M,
-                tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, s);
+  // x += a W_down^T (deferred likewise)
+  st = linear(c, TL_K_DOWN, B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, M,
+              tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, &S, s);
+  if (st != TL_OK) return st;
+  if (S > 1) c->pend = tl::Pending{c->gpart, S};
+  return TL_OK;
+}
+
+// Apply any pending residual partials to x (after the last layer).
+tl_status resolve(tl_ctx* c, int M, hipStream_t s) {
+  if (!c->pend.part) return TL_OK;
+  KScope k(c, TL_K_NORM, s);
+  TL_HIP(tl::launch_rmsnorm(c->x, c->pend, c->final_norm, c->cfg.rms_eps, M, c->cfg.d_model, nullptr, s));
+  c->pend = tl::Pending{nullptr, 1};
+  return TL_OK;
 }
 
 tl_status check_lane(const tl_ctx* c, int lane) {
@@ -343,6 +383,9 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->a = reinterpret_cast<uint16_t*>(ab + L.a);
   c->part = reinterpret_cast<float*>(ab + L.part);
   c->logits = reinterpret_cast<float*>(ab + L.logits);
+  c->gpart = reinterpret_cast<float*>(ab + L.gpart);
+  c->hscr = ab + L.hscr;
+  c->pend = tl::Pending{nullptr, 1};
   c->len.assign(cfg->n_lanes, 0);
   c->loops.assign(cfg->n_lanes, 1);
   c->depth.assign(cfg->n_lanes, INT_MAX);
@@ -419,6 +462,8 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
     st = run_layer(ctx, B, layer, n, rm, false, s);
     if (st != TL_OK) return st;
   }
+  st = resolve(ctx, n, s);
+  if (st != TL_OK) return st;
   if (d_hidden) {
     KScope k(ctx, TL_K_COPY, s);
     TL_HIP(hipMemcpyAsync(d_hidden, ctx->x, (size_t)n * d * 4, hipMemcpyDeviceToDevice, s));
@@ -426,18 +471,9 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
     tl::RowMap one{};
-    {
-      KScope k(ctx, TL_K_NORM, s);
-      TL_HIP(tl::launch_rmsnorm(ctx->x + (size_t)(n - 1) * d, ctx->final_norm, C.rms_eps, 1, d, ctx->h, s));
-    }
-    {
-      KScope k(ctx, TL_K_HEAD, s);
-      TL_HIP(tl::launch_head_z(ctx->h, 1, ctx->head, C.vocab, d, lg, one, s));
-    }
-    if (d_next) {
-      KScope k(ctx, TL_K_ARGMAX, s);
-      TL_HIP(tl::launch_argmax(lg, 1, C.vocab, one, d_next, s));
-    }
+    KScope k(ctx, TL_K_HEAD, s);
+    TL_HIP(tl::launch_head(ctx->x + (size_t)(n - 1) * d, 1, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg,
+                           one, ctx->hscr, d_next, s));
   }
   ctx->len[lane] = p0 + n;
   ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
@@ -482,18 +518,9 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   }
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
-    {
-      KScope k(ctx, TL_K_NORM, s);
-      TL_HIP(tl::launch_rmsnorm(ctx->x, ctx->final_norm, C.rms_eps, M, d, ctx->h, s));
-    }
-    {
-      KScope k(ctx, TL_K_HEAD, s);
-      TL_HIP(tl::launch_head_z(ctx->h, M, ctx->head, C.vocab, d, lg, rm, s));
-    }
-    if (d_next) {
-      KScope k(ctx, TL_K_ARGMAX, s);
-      TL_HIP(tl::launch_argmax(lg, M, C.vocab, rm, d_next, s));
-    }
+    KScope k(ctx, TL_K_HEAD, s);
+    TL_HIP(tl::launch_head(ctx->x, M, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg, rm, ctx->hscr, d_next,
+                           s));
   }
   if (d_hidden) {
     KScope k(ctx, TL_K_COPY, s);
@@ -584,18 +611,28 @@ tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* 
   return TL_OK;
 }
 
+size_t tl_w4_linear_ws_bytes(int32_t N, int32_t K, int32_t M) {
+  if (N < 16 || N % 16 || K < 8 || K % 8 || M < 1) return 0;
+  return al256(tl::w4_gemm_scratch_bytes(N, K, M, false));
+}
+
 tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M, float* d_C,
-                       void* stream) {
+                       void* d_ws, void* stream) {
   if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
   if (M < 1) return fail(TL_E_RANGE, "M < 1");
   if (!d_packed || !d_A || !d_C || !aligned(d_A, 16)) return fail(TL_E_INVAL, "bad pointer");
   const tl::Packed p = packed_view(d_packed, N, K);
   const tl::Epi e{tl::EPI_STORE, d_C, nullptr, N};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (gemv_fits(M, K))
+  if (M <= 8 && gemv_fits(M, K)) {
     TL_HIP(tl::launch_w4_gemv(p, tl::ASrc{d_A, nullptr, nullptr, 0.f}, M, e, s));
-  else
-    TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, s));
+    return TL_OK;
+  }
+  const int S = tl::plan_w4_gemm(N, K, M, false).S;
+  if (S > 1 && (!d_ws || !aligned(d_ws, 256))) return fail(TL_E_INVAL, "this shape needs d_ws");
+  float* part = static_cast<float*>(d_ws);
+  TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, part, s));
+  if (S > 1) TL_HIP(tl::launch_reduce_partials(part, S, M, N, d_C, 0, s));
   return TL_OK;
 }
 

@@ -77,4 +77,22 @@ __device__ __forceinline__ float row16_max(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Rotary embedding of one pair (x1 = dim i, x2 = dim i + hd/2) by the angle
+// whose cos/sin are c, s; both results are rounded to fp16 (Q and K cast
+// points). Every kernel that rotates uses this one expression.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, _Float16* r1, _Float16* r2) {
+  *r1 = (_Float16)(x1 * c - x2 * s);
+  *r2 = (_Float16)(x2 * c + x1 * s);
+}
+
+// INT8 KV quantizer of one (token, head) row: scale = fp16(amax / 127) with a
+// correctly rounded fp32 division, code = clamp(rint(x / f32(scale)), -127,
+// 127) with a correctly rounded division and round-half-even, 0 when the
+// scale is 0.
+__device__ __forceinline__ _Float16 kv_scale(float amax) { return (_Float16)__fdiv_rn(amax, 127.0f); }
+__device__ __forceinline__ int kv_code(float x, float sf) {
+  if (!(sf > 0.f)) return 0;
+  return (int)fminf(fmaxf(rintf(__fdiv_rn(x, sf)), -127.f), 127.f);
+}
+
 }  // namespace tl

@@ -45,11 +45,30 @@ struct ASrc {
 
 // C = A * W^T for M <= 16 rows (decode GEMV shape); K split across waves.
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s);
-// C = A * W^T for any M (prefill GEMM shape); A fp16 [M][K].
-hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, hipStream_t s);
+// Launch plan of the prefill GEMM: row tile 16*mb, nbw n-blocks per wave,
+// gx column blocks x gy row tiles x S K-splits of gps groups each.
+struct GemmPlan {
+  int mb, nbw, gx, gy, S, gps, blocks;
+  float* part;  // S > 1: fp32 partial tiles [S][M][N], summed by the consumer
+};
+constexpr int kMaxSplitK = 16;  // consumers sum at most this many partials
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu);
+size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu);
+// C = A * W^T for any M (prefill GEMM shape); A fp16 [M][K]. When the plan
+// splits K (S > 1, never for SwiGLU) the kernel writes the S partials to
+// `part` instead of running the epilogue; the caller passes them on.
+hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s);
+// out (= or +=) sum of S partials [S][M][N], in split order.
+hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float* out, int accumulate, hipStream_t s);
 
-// fp16 h [M][d] = RMSNorm(x) (prefill path).
-hipError_t launch_rmsnorm(const float* x, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
+// Pending split-K partials of a residual GEMM: x += sum_s part[s] (split
+// order) before x is used.
+struct Pending {
+  const float* part;  // [S][M][d] or null
+  int S;
+};
+// x += pending (if any), then fp16 h [M][d] = RMSNorm(x) (prefill path).
+hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
                           hipStream_t s);
 
 // Per-row placement of the rows of one call: row m belongs to lane
@@ -70,8 +89,9 @@ struct KvGeom {
   int int8;
 };
 
-// RoPE on q and k of qkv fp32 [M][3d], fp16 Q out [M][d], K/V into cache layer.
-hipError_t launch_rope_kv(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+// RoPE on q and k of qkv fp32 [M][3d] (the sum of S split-K partials, each
+// [M][3d], in split order), fp16 Q out [M][d], K/V into cache layer.
+hipError_t launch_rope_kv(const float* qkv, int S, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                           int layer, uint16_t* q_out, hipStream_t s);
 
 // Causal attention of M new rows of one lane (prefill) over cache rows
@@ -79,19 +99,22 @@ hipError_t launch_rope_kv(const float* qkv, int M, const RowMap& rm, const float
 hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const KvGeom& kv, int layer,
                                uint16_t* o, hipStream_t s);
 // Single-query attention for M decode rows (one per lane) over each lane's
-// rows 0..row_pos[m]. part: scratch floats.
+// rows 0..row_pos[m], from the raw QKV projection qkv fp32 [M][3d]: applies
+// RoPE, writes the new K/V row into cache layer `layer`, attends, O fp16
+// [M][d]. part: scratch floats (used when a context exceeds 512 keys).
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
-hipError_t launch_attn_decode(const uint16_t* q, int M, const RowMap& rm, const KvGeom& kv, int layer,
-                              float* part, uint16_t* o, hipStream_t s);
+hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+                              int layer, float* part, uint16_t* o, hipStream_t s);
 
 hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d,
                         float* x, hipStream_t s);
-// logits of normed fp16 rows z [M][d] (M <= 16) against the fp16 head
-// [V][d]; row m is written at logits[out_row(m) * V], out_row = the row's
-// lane in decode (per_row) and m in prefill.
-hipError_t launch_head_z(const uint16_t* z, int M, const uint16_t* head, int V, int d, float* logits,
-                         const RowMap& rm, hipStream_t s);
-hipError_t launch_argmax(const float* logits, int M, int V, const RowMap& rm, int32_t* next, hipStream_t s);
+// Final RMSNorm of the residual rows x [M][d] (M <= 8), logits against the
+// fp16 head [V][d] written at logits[out_row(m) * V] (out_row = the row's lane
+// in decode, m in prefill) and, if next != null, the greedy argmax of each row
+// into next[out_row(m)] (second small launch). scratch: head_scratch_bytes.
+size_t head_scratch_bytes(int max_rows, int V);
+hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
+                       float* logits, const RowMap& rm, void* scratch, int32_t* next, hipStream_t s);
 // dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
 

@@ -22,6 +22,8 @@
 // double-buffered through LDS (global loads of group g+1 overlap the MFMAs of
 // group g) and shared by the 4 waves, while each wave streams its own weight
 // tiles one group ahead.
+#include <type_traits>
+
 #include "tl_device.h"
 #include "tl_kernels.h"
 
@@ -40,6 +42,7 @@ __device__ __forceinline__ void epi_swiglu(const Epi& e, int m, int c, float g, 
 
 // ---------------------------------------------------------------- GEMV
 constexpr int kGemvMaxIt = 8;  // weight tiles kept in flight per wave and n-block
+constexpr int kNormKpt = 4;    // residual elements per thread held in registers by the fused RMSNorm
 
 template <int WK, int NBB>
 __global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
@@ -56,8 +59,67 @@ __global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restr
   const int nb0 = blockIdx.x * NBB;
   const int Kp = G * 128;
 
+  // ---- the weight tiles do not depend on the activations: start their loads
+  // before staging the activations so both latencies overlap.
+  u32x4_t wv[kGemvMaxIt][NBB];
+  uint16_t sc[kGemvMaxIt][NBB];  // raw fp16 bits: converting at load time would force a wait
+  auto load_batch = [&](int gb) {
+#pragma unroll
+    for (int it = 0; it < kGemvMaxIt; ++it) {
+      const int g = gb + it * WK;
+#pragma unroll
+      for (int j = 0; j < NBB; ++j) {
+        if (g < G) {
+          const size_t tile = (size_t)(nb0 + j) * G + g;
+          wv[it][j] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes) + lane);
+          sc[it][j] = scales[tile * 16 + l16];
+        }
+      }
+    }
+  };
+  load_batch(wave);
+
   // ---- stage the M activation rows (fp16) into LDS
-  if (a.x32) {
+  if (a.x32 && K <= kNormKpt * WK * 64 && M <= 8) {
+    // every x and gamma element this thread needs, in one round trip
+    float xv[8][kNormKpt];
+    float gv[kNormKpt];
+#pragma unroll
+    for (int i = 0; i < kNormKpt; ++i) {
+      const int k = tid + WK * 64 * i;
+      gv[i] = k < K ? h2f(a.gamma[k]) : 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) xv[m][i] = (m < M && k < K) ? a.x32[(size_t)m * K + k] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < M) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < kNormKpt; ++i) acc += xv[m][i] * xv[m][i];
+        acc = wave_sum(acc);
+        if (lane == 0) nrm[wave * 16 + m] = acc;
+      }
+    }
+    __syncthreads();
+    if (tid < M) {
+      float t = 0.f;
+      for (int w = 0; w < WK; ++w) t += nrm[w * 16 + tid];
+      nrm[WK * 16 + tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < M) {
+        const float rinv = nrm[WK * 16 + m];
+#pragma unroll
+        for (int i = 0; i < kNormKpt; ++i) {
+          const int k = tid + WK * 64 * i;
+          if (k < Kp) As[m * lda + k] = (_Float16)(k < K ? (xv[m][i] * rinv) * gv[i] : 0.f);
+        }
+      }
+    }
+  } else if (a.x32) {
     for (int m = 0; m < M; ++m) {
       const float* xr = a.x32 + (size_t)m * K;
       float acc = 0.f;
@@ -99,20 +161,7 @@ __global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restr
   const bool arow = l16 < M;
   const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int gb = wave; gb < G; gb += WK * kGemvMaxIt) {
-    u32x4_t wv[kGemvMaxIt][NBB];
-    float sc[kGemvMaxIt][NBB];
-#pragma unroll
-    for (int it = 0; it < kGemvMaxIt; ++it) {
-      const int g = gb + it * WK;
-#pragma unroll
-      for (int j = 0; j < NBB; ++j) {
-        if (g < G) {
-          const size_t tile = (size_t)(nb0 + j) * G + g;
-          wv[it][j] = *reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes + lane * 16);
-          sc[it][j] = h2f(scales[tile * 16 + l16]);
-        }
-      }
-    }
+    if (gb != wave) load_batch(gb);
 #pragma unroll
     for (int it = 0; it < kGemvMaxIt; ++it) {
       const int g = gb + it * WK;
@@ -126,8 +175,9 @@ __global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restr
           float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) t = mfma16(af[s], dequant_word(wv[it][j][s]), t);
+          const float scf = h2f(sc[it][j]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], sc[it][j], acc[j][r]);
+          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], scf, acc[j][r]);
         }
       }
     }
@@ -184,53 +234,153 @@ hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, h
 }
 
 // ---------------------------------------------------------------- GEMM
-constexpr int kLdsA = 136;  // halves per LDS row of the A tile (128 + 8 pad)
+// Every operand reaches LDS by global_load_lds (no staging registers), into a
+// ring of NST one-group stages. Stage layout (group g of the block's K range):
+//   A  : MB*4 blocks of 1 KiB; block (mb, s) holds at byte 16*l row
+//        m0 + 16mb + l%16, columns 128g + 32s + 8(l/16)..+7 -- exactly lane
+//        l's MFMA A operand, so each is one conflict-free ds_read_b128;
+//   B  : per wave, NBW weight tiles of 1 KiB in the packed layout (lane l's
+//        16 bytes are its four k-steps' B operands);
+//   Sc : per wave, NBW x 16 fp16 group scales.
+// The loop over groups is compact (not unrolled): issue group g+NST-1 into
+// the slot freed by group g-1, wait (compile-time vmcnt per look-ahead) until
+// group g's copies have landed, barrier, compute group g, barrier. Rows >= M
+// and columns >= K read in-bounds elements: those rows are never stored and
+// those columns meet zero weights.
+template <int MB, int NBW>
+struct GemmCfg {
+  static constexpr int kA = MB * 4 * 1024;
+  static constexpr int kB = 4 * NBW * 1024;
+  static constexpr int kSc = 4 * NBW * 32;
+  static constexpr int kSlot = kA + kB + kSc;
+  static constexpr int NST = (144 * 1024) / kSlot > 6 ? 6 : (144 * 1024) / kSlot;  // ring depth
+  static constexpr int OPS = MB + 2 * NBW;  // copies one wave issues per group
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// wait until at most ahead*OPS copies of this wave are in flight, then barrier
+template <int OPS, int NST>
+__device__ __forceinline__ void stage_wait(int ahead) {
+  static_assert(NST <= 6, "ring depth");
+  switch (ahead) {
+    case 0: wait_vm_barrier<0>(); break;
+    case 1: wait_vm_barrier<1 * OPS>(); break;
+    case 2: wait_vm_barrier<(NST > 2 ? 2 : 0) * OPS>(); break;
+    case 3: wait_vm_barrier<(NST > 3 ? 3 : 0) * OPS>(); break;
+    case 4: wait_vm_barrier<(NST > 4 ? 4 : 0) * OPS>(); break;
+    default: wait_vm_barrier<(NST > 5 ? 5 : 0) * OPS>(); break;
+  }
+}
+
+// LDS reads of one wave written as asm that also waits for them: plain C++
+// loads (or a memory clobber) would make the compiler wait for every LDS copy
+// in flight, including the later stages'. Volatile asm keeps its order against
+// the stage barriers, which are volatile too.
+template <int MB>
+__device__ __forceinline__ void lds_frags(uint32_t addr, half8_t* f);
+template <>
+__device__ __forceinline__ void lds_frags<1>(uint32_t a, half8_t* f) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f[0]) : "v"(a));
+}
+template <>
+__device__ __forceinline__ void lds_frags<2>(uint32_t a, half8_t* f) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(f[0]), "=v"(f[1]) : "v"(a));
+}
+template <>
+__device__ __forceinline__ void lds_frags<4>(uint32_t a, half8_t* f) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\t"
+      "ds_read_b128 %2, %4 offset:8192\n\tds_read_b128 %3, %4 offset:12288\n\ts_waitcnt lgkmcnt(0)"
+      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]) : "v"(a));
+}
+template <>
+__device__ __forceinline__ void lds_frags<8>(uint32_t a, half8_t* f) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:4096\n\t"
+      "ds_read_b128 %2, %8 offset:8192\n\tds_read_b128 %3, %8 offset:12288\n\t"
+      "ds_read_b128 %4, %8 offset:16384\n\tds_read_b128 %5, %8 offset:20480\n\t"
+      "ds_read_b128 %6, %8 offset:24576\n\tds_read_b128 %7, %8 offset:28672\n\ts_waitcnt lgkmcnt(0)"
+      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]), "=v"(f[4]), "=v"(f[5]), "=v"(f[6]), "=v"(f[7])
+      : "v"(a));
+}
+// NBW (1 or 2) weight tiles (16 B per lane, 1 KiB apart) and their scales
+// (2 bytes per lane at l16, 32 bytes apart).
+template <int NBW>
+__device__ __forceinline__ void lds_tiles(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s);
+template <>
+__device__ __forceinline__ void lds_tiles<1>(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(w[0]), "=v"(s[0]) : "v"(wa), "v"(sa));
+}
+template <>
+__device__ __forceinline__ void lds_tiles<2>(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_u16 %2, %5\n\tds_read_u16 %3, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+      : "=v"(w[0]), "=v"(w[1]), "=v"(s[0]), "=v"(s[1]) : "v"(wa), "v"(sa));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
+}
+__device__ __forceinline__ void lds_copy16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
 
 template <int MB, int NBW>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int N, int K, int G,
-                                                      const uint16_t* __restrict__ A, int M, Epi e) {
-  constexpr int BM = 16 * MB;
-  __shared__ __align__(16) _Float16 As[2][BM * kLdsA];
+                                                      const uint16_t* __restrict__ A, int M, Epi e, GemmPlan pl) {
+  using C = GemmCfg<MB, NBW>;
+  constexpr int NST = C::NST;
+  __shared__ __align__(16) uint8_t ring[NST * C::kSlot];
+  const int L = blockIdx.x;
+  const int U = pl.gy * pl.S;
+  const int xcd = L & 7, r = L >> 3;
+  const int cl = r / U, u = r - cl * U;
+  const int cb = cl * 8 + xcd;
+  if (cb >= pl.gx) return;  // padding block of the XCD mapping
+  const int my = u / pl.S, sp = u - my * pl.S;
+  const int kg0 = sp * pl.gps, kg1 = min(G, kg0 + pl.gps);
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int NB = N / 16;
-  const int nbw0 = (blockIdx.x * 4 + wave) * NBW;
-  const int m0 = blockIdx.y * BM;
+  const int nbw0 = (cb * 4 + wave) * NBW;
+  const int m0 = my * 16 * MB;
 
-  // A loader: BM rows x 16 chunks of 8 halves = MB chunks per thread.
-  u32x4_t an[MB];
-  auto load_a = [&](int g) {
+  // per-lane sources: A rows of the m-blocks this wave copies (wave w copies
+  // k-step s = w of every m-block), its weight tiles and scales
+  const uint16_t* arow[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = g * 128 + (c & 15) * 8;
-      const int m = m0 + row;
-      u32x4_t v = {0, 0, 0, 0};
-      if (m < M && col < K) v = *reinterpret_cast<const u32x4_t*>(A + (size_t)m * K + col);
-      an[i] = v;
-    }
-  };
-  auto store_a = [&](int buf) {
+  for (int i = 0; i < MB; ++i) arow[i] = A + (size_t)min(m0 + i * 16 + l16, M - 1) * K;
+  const int acol = 32 * wave + 8 * lq;
+  int nbc[NBW];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int c = tid + 256 * i, row = c >> 4;
-      *reinterpret_cast<u32x4_t*>(&As[buf][row * kLdsA + (c & 15) * 8]) = an[i];
-    }
-  };
-  u32x4_t bw[NBW], bn[NBW];
-  float bs[NBW], bsn[NBW];
-  auto load_b = [&](int g, u32x4_t* w, float* sc) {
+  for (int j = 0; j < NBW; ++j) nbc[j] = min(nbw0 + j, NB - 1);
+
+  auto issue = [&](int g) {
+    uint8_t* slot = ring + (g % NST) * C::kSlot;
+    const int col = min(g * 128 + acol, K - 8);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) lds_copy16(arow[i] + col, slot + (i * 4 + wave) * 1024);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int nb = nbw0 + j;
-      if (nb < NB) {
-        const size_t tile = (size_t)nb * G + g;
-        w[j] = *reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes + lane * 16);
-        sc[j] = h2f(scales[tile * 16 + l16]);
-      } else {
-        w[j] = (u32x4_t){0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        sc[j] = 0.f;
-      }
+      const size_t tile = (size_t)nbc[j] * G + g;
+      lds_copy16(tiles + tile * kTileBytes + lane * 16, slot + C::kA + (wave * NBW + j) * 1024);
+      if (lane < 2) lds_copy16(scales + tile * 16 + lane * 8, slot + C::kA + C::kB + (wave * NBW + j) * 32);
     }
   };
 
@@ -240,17 +390,17 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
-  store_a(0);
-  load_b(0, bw, bs);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) {
-      load_a(g + 1);
-      load_b(g + 1, bn, bsn);
-    }
+  for (int i = 0; i < NST - 1; ++i)
+    if (kg0 + i < kg1) issue(kg0 + i);
+#pragma unroll 1
+  for (int g = kg0; g < kg1; ++g) {
+    if (g + NST - 1 < kg1) issue(g + NST - 1);
+    stage_wait<C::OPS, NST>(min(NST - 1, kg1 - 1 - g));
+    const uint8_t* slot = ring + (g % NST) * C::kSlot;
+    u32x4_t bw[NBW];
+    uint32_t bsr[NBW];
+    lds_tiles<NBW>(lds_addr(slot + C::kA + wave * NBW * 1024 + lane * 16),
+                   lds_addr(slot + C::kA + C::kB + wave * NBW * 32 + l16 * 2), bw, bsr);
     float4_t t[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -258,87 +408,155 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
       for (int j = 0; j < NBW; ++j) t[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      half8_t af[MB];
+      lds_frags<MB>(lds_addr(slot + s * 1024 + lane * 16), af);
       half8_t bf[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) bf[j] = dequant_word(bw[j][s]);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const half8_t af =
-            *reinterpret_cast<const half8_t*>(&As[buf][(i * 16 + l16) * kLdsA + 32 * s + 8 * lq]);
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) t[i][j] = mfma16(af, bf[j], t[i][j]);
-      }
+        for (int j = 0; j < NBW; ++j) t[mb][j] = mfma16(af[mb], bf[j], t[mb][j]);
     }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const float sc = h2f((uint16_t)bsr[j]);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[i][j][rr] = fmaf(t[i][j][rr], sc, acc[i][j][rr]);
+    }
+    plain_barrier();  // every wave is done with this slot before it is refilled
+  }
+
+  // ---- split-K: publish this split's partial tile; the kernel that consumes
+  // the result sums the S partials in split order (kernel boundaries make
+  // them visible; no in-kernel cross-block traffic).
+  if (pl.S > 1) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NBW; ++j)
+      for (int rr = 0; rr < 4; ++rr) {
+        const int m = m0 + i * 16 + 4 * lq + rr;
+        if (m >= M) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(t[i][j][r], bs[j], acc[i][j][r]);
-    if (g + 1 < G) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        bw[j] = bn[j];
-        bs[j] = bsn[j];
+        for (int j = 0; j < NBW; ++j)
+          if (nbw0 + j < NB) pl.part[((size_t)sp * M + m) * N + (nbw0 + j) * 16 + l16] = acc[i][j][rr];
       }
-    }
-    __syncthreads();
+    return;
   }
 
   // ---- epilogue: lane holds C[m0 + 16i + 4lq + r][16*(nbw0 + j) + l16]
+  if (e.mode == EPI_RESID) {
+    // read every residual element first (one round trip), then write
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int m = min(m0 + i * 16 + 4 * lq + rr, M - 1);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const int n = min(nbw0 + j, NB - 1) * 16 + l16;
+          acc[i][j][rr] += e.out_f32[(size_t)m * e.ldo + n];
+        }
+      }
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + i * 16 + 4 * lq + r;
+    for (int rr = 0; rr < 4; ++rr) {
+      const int m = m0 + i * 16 + 4 * lq + rr;
       if (m >= M) continue;
       if (e.mode == EPI_SWIGLU) {
         if constexpr (NBW % 2 == 0) {
 #pragma unroll
           for (int j = 0; j < NBW; j += 2)
-            if (nbw0 + j < NB) epi_swiglu(e, m, ((nbw0 + j) >> 1) * 16 + l16, acc[i][j][r], acc[i][j + 1][r]);
+            if (nbw0 + j < NB) epi_swiglu(e, m, ((nbw0 + j) >> 1) * 16 + l16, acc[i][j][rr], acc[i][j + 1][rr]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
-          if (nbw0 + j < NB) epi_store(e, m, (nbw0 + j) * 16 + l16, acc[i][j][r]);
+          if (nbw0 + j < NB) e.out_f32[(size_t)m * e.ldo + (nbw0 + j) * 16 + l16] = acc[i][j][rr];
       }
     }
   }
 }
 
-template <int MB, int NBW>
-static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const Epi& e, hipStream_t s) {
-  const int NB = w.N / 16;
-  dim3 grid((NB + 4 * NBW - 1) / (4 * NBW), (M + 16 * MB - 1) / (16 * MB));
-  hipLaunchKernelGGL((w4_gemm_kernel<MB, NBW>), grid, dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G, A, M, e);
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu) {
+  GemmPlan p{};
+  const int NB = N / 16, G = (K + 127) / 128;
+  p.nbw = 2;
+  p.mb = M > 64 ? 8 : (M > 32 ? 4 : (M > 16 ? 2 : 1));
+  p.gx = (NB + 4 * p.nbw - 1) / (4 * p.nbw);
+  auto gy = [&](int mb) { return (M + 16 * mb - 1) / (16 * mb); };
+  int S = 1;
+  if (swiglu) {
+    while (p.mb > 1 && p.gx * gy(p.mb) < 160) p.mb >>= 1;
+  } else {
+    const int tiles = p.gx * gy(p.mb);
+    while (S < kMaxSplitK && tiles * (S + 1) <= 256 && (G + S) / (S + 1) >= 1) {
+      const int gps_next = (G + S) / (S + 1);
+      if (gps_next < 1) break;
+      ++S;
+    }
+  }
+  p.gy = gy(p.mb);
+  p.gps = (G + S - 1) / S;
+  p.S = (G + p.gps - 1) / p.gps;
+  p.blocks = ((p.gx + 7) / 8) * 8 * p.gy * p.S;
+  return p;
+}
+
+size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu) {
+  const GemmPlan p = plan_w4_gemm(N, K, M, swiglu);
+  if (p.S == 1) return 0;
+  return (size_t)p.S * M * N * 4;
+}
+
+// out[m][n] (= or +=) sum_s part[s][m][n], summed in split order.
+__global__ void reduce_partials_kernel(const float* __restrict__ part, int S, int M, int N, float* __restrict__ out,
+                                       int accumulate) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t MN = (size_t)M * N;
+  if (i >= MN) return;
+  float v = part[i];
+  for (int s = 1; s < S; ++s) v += part[s * MN + i];
+  out[i] = accumulate ? out[i] + v : v;
+}
+
+hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float* out, int accumulate, hipStream_t s) {
+  const size_t MN = (size_t)M * N;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part, S, M, N, out,
+                     accumulate);
   return hipGetLastError();
 }
 
-hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, hipStream_t s) {
+template <int MB, int NBW>
+static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const Epi& e, const GemmPlan& pl,
+                              hipStream_t s) {
+  hipLaunchKernelGGL((w4_gemm_kernel<MB, NBW>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K,
+                     w.G, A, M, e, pl);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s) {
   if (M < 1) return hipErrorInvalidValue;
-  const int NB = w.N / 16;
-  const bool swiglu = e.mode == EPI_SWIGLU;
-  // Two n-blocks per wave when the shape allows (SwiGLU needs the gate/up pair).
-  const int nbw = (swiglu || NB % 8 == 0) ? 2 : 1;
-  // Largest row tile that still gives about one block per CU.
-  int mb = M > 64 ? 8 : (M > 32 ? 4 : (M > 16 ? 2 : 1));
-  auto blocks = [&](int mbv) { return ((NB + 4 * nbw - 1) / (4 * nbw)) * ((M + 16 * mbv - 1) / (16 * mbv)); };
-  while (mb > 1 && blocks(mb) < 240) mb >>= 1;
-  if (nbw == 2) {
-    switch (mb) {
-      case 8: return gemm_launch<8, 2>(w, A, M, e, s);
-      case 4: return gemm_launch<4, 2>(w, A, M, e, s);
-      case 2: return gemm_launch<2, 2>(w, A, M, e, s);
-      default: return gemm_launch<1, 2>(w, A, M, e, s);
+  GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU);
+  if (pl.S > 1 && !part) return hipErrorInvalidValue;
+  pl.part = part;
+  if (pl.nbw == 2) {
+    switch (pl.mb) {
+      case 8: return gemm_launch<8, 2>(w, A, M, e, pl, s);
+      case 4: return gemm_launch<4, 2>(w, A, M, e, pl, s);
+      case 2: return gemm_launch<2, 2>(w, A, M, e, pl, s);
+      default: return gemm_launch<1, 2>(w, A, M, e, pl, s);
     }
   }
-  switch (mb) {
-    case 8: return gemm_launch<8, 1>(w, A, M, e, s);
-    case 4: return gemm_launch<4, 1>(w, A, M, e, s);
-    case 2: return gemm_launch<2, 1>(w, A, M, e, s);
-    default: return gemm_launch<1, 1>(w, A, M, e, s);
+  switch (pl.mb) {
+    case 8: return gemm_launch<8, 1>(w, A, M, e, pl, s);
+    case 4: return gemm_launch<4, 1>(w, A, M, e, pl, s);
+    case 2: return gemm_launch<2, 1>(w, A, M, e, pl, s);
+    default: return gemm_launch<1, 1>(w, A, M, e, pl, s);
   }
 }
 

@@ -40,6 +40,11 @@ def _linear(rng, N, K):
     return qw, sc
 
 
+def _ws(N, K, M):
+    from looped_weight_shared_amd.model import device_bytes
+    return device_bytes(max(256, tl.tl_w4_linear_ws_bytes(N, K, M)))
+
+
 def _packed(qw, sc, N, K):
     from looped_weight_shared_amd.model import device_bytes
     p = device_bytes(tl.tl_qlinear_packed_bytes(N, K))
@@ -74,7 +79,8 @@ def test_w4_linear_matches_oracle(N, K, M):
     p = _packed(qw, sc, N, K)
     A = rng.standard_normal((M, K)).astype(np.float16)
     C = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    tl.tl_w4_linear(p, N, K, dev(A), M, C)
+    ws = _ws(N, K, M)
+    tl.tl_w4_linear(p, N, K, dev(A), M, C, ws)
     torch.cuda.synchronize()
     ref = A.astype(np.float64) @ oracle.dequantize(qw, sc).T
     err = rel_rows(host(C), ref)
@@ -82,7 +88,7 @@ def test_w4_linear_matches_oracle(N, K, M):
     assert err < 1e-4
     # run twice: bit-identical
     C2 = torch.empty_like(C)
-    tl.tl_w4_linear(p, N, K, dev(A), M, C2)
+    tl.tl_w4_linear(p, N, K, dev(A), M, C2, ws)
     torch.cuda.synchronize()
     assert torch.equal(C, C2)
 
@@ -95,10 +101,11 @@ def test_gemv_rows_do_not_depend_on_batch():
     p = _packed(qw, sc, N, K)
     A = rng.standard_normal((8, K)).astype(np.float16)
     full = torch.empty((8, N), dtype=torch.float32, device="cuda")
-    tl.tl_w4_linear(p, N, K, dev(A), 8, full)
+    ws = _ws(N, K, 8)
+    tl.tl_w4_linear(p, N, K, dev(A), 8, full, ws)
     for m in range(8):
         one = torch.empty((1, N), dtype=torch.float32, device="cuda")
-        tl.tl_w4_linear(p, N, K, dev(A[m:m + 1]), 1, one)
+        tl.tl_w4_linear(p, N, K, dev(A[m:m + 1]), 1, one, ws)
         torch.cuda.synchronize()
         assert torch.equal(one[0], full[m])
 

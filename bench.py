@@ -12,7 +12,7 @@ Also reported (same JSON line):
   roofline -- the dominant prefill kernel (W4A16 MFMA GEMM) against the fp16
               MFMA peak; roofline_decode -- the W4 decode GEMV against HBM.
               Per-launch durations come from HIP event pairs the library
-              records around every launch on its stream (tl_profile_begin/end)
+              attaches to every launch's own dispatch (tl_profile_begin/end)
               during a separate pass over the same steps.
   cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
               the same prefill step (reported, not a target).

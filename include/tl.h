@@ -177,10 +177,13 @@ const char* tl_last_error(void);
 /* ---- kernel timing ------------------------------------------------------
  * For measurement ("Performance and Memory" page, "How To Publish Numbers
  * Responsibly" and the phase timings of TINYLOOP_CUDA_PROFILE): while a
- * window is open, every kernel the context launches is bracketed by a pair
- * of HIP events recorded on the call's stream, up to max_launches launches.
+ * window is open, every kernel the context launches (up to max_launches)
+ * carries a pair of HIP events attached to its own dispatch
+ * (hipExtLaunchKernel), so each pair spans that kernel's execution alone.
+ * Windows are per context; launches are attributed on the calling thread.
  * tl_profile_end waits for the recorded events and returns, per kernel kind,
- * the number of launches and their summed event-to-event time. */
+ * the number of launches and their summed durations (TL_K_COPY counts the
+ * row scatter of decode hidden states; plain memory copies are not timed). */
 typedef enum {
   TL_K_EMBED = 0, TL_K_NORM, TL_K_QKV, TL_K_ROPE_KV, TL_K_ATTN, TL_K_O, TL_K_GATE_UP, TL_K_DOWN,
   TL_K_HEAD, TL_K_ARGMAX, TL_K_COPY, TL_K_COUNT

@@ -204,9 +204,9 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
                                uint16_t* o, hipStream_t s) {
   dim3 grid((M + 63) / 64, kv.H);
   if (kv.hd == 128)
-    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    launch(attn_prefill_kernel<128>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
   else if (kv.hd == 64)
-    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    launch(attn_prefill_kernel<64>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -483,10 +483,10 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict_
 template <int HD, bool I8>
 static void decode_launch(dim3 grid, int used, const float* qkv, const RowMap& rm, const float* rope_cs,
                           const KvGeom& kv, int layer, float* part, int np_max, uint16_t* o, hipStream_t s) {
-  hipLaunchKernelGGL((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part,
+  launch((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part,
                      np_max, o);
   if (used > 1)
-    hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, rm, kv.H, np_max, o);
+    launch(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, rm, kv.H, np_max, o);
 }
 
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,

@@ -23,7 +23,7 @@ __global__ void embed_kernel(const uint16_t* __restrict__ E, const int32_t* __re
 
 hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d, float* x,
                         hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, s, embed, tokens, rm, d, x);
+  launch(embed_kernel, dim3(M), dim3(256), 0, s, embed, tokens, rm, d, x);
   return hipGetLastError();
 }
 
@@ -105,13 +105,13 @@ hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float e
   if (d % 4 || d > 8192 || pend.S > kMaxSplits) return hipErrorInvalidValue;
   const int ch = (d / 4 + 255) / 256;
   if (ch <= 1)
-    hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
   else if (ch <= 2)
-    hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
   else if (ch <= 4)
-    hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
   return hipGetLastError();
 }
 
@@ -154,7 +154,7 @@ __global__ void kv_quant_rows_kernel(const uint16_t* __restrict__ x, int rows, i
 }
 
 hipError_t launch_kv_quantize_rows(const uint16_t* x, int rows, int hd, int8_t* q, uint16_t* sc, hipStream_t s) {
-  hipLaunchKernelGGL(kv_quant_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, hd, q, sc);
+  launch(kv_quant_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, hd, q, sc);
   return hipGetLastError();
 }
 
@@ -238,7 +238,7 @@ hipError_t launch_rope_kv(const float* qkv, int S, int M, const RowMap& rm, cons
                           int layer, uint16_t* q_out, hipStream_t s) {
   if (kv.hd > 128 || kv.hd % 2 || S < 1) return hipErrorInvalidValue;
   dim3 grid((kv.H + 3) / 4, M);
-  hipLaunchKernelGGL(rope_kv_kernel, grid, dim3(256), 0, s, qkv, S, M, rm, rope_cs, kv, layer, q_out);
+  launch(rope_kv_kernel, grid, dim3(256), 0, s, qkv, S, M, rm, rope_cs, kv, layer, q_out);
   return hipGetLastError();
 }
 
@@ -425,17 +425,22 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ c
 size_t head_scratch_bytes(int max_rows, int V) { return (size_t)max_rows * ((V + 63) / 64) * 8; }
 
 hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
-                       float* logits, const RowMap& rm, void* scratch, int32_t* next, hipStream_t s) {
+                       float* logits, const RowMap& rm, void* scratch, hipStream_t s) {
   if (M < 1 || M > 8 || d % 32) return hipErrorInvalidValue;
   const size_t lds = (size_t)M * (d + 8) * 2;
   const int nblk = (V + 63) / 64;
   float* cval = static_cast<float*>(scratch);
   int* cidx = reinterpret_cast<int*>(cval + (size_t)M * nblk);
-  hipLaunchKernelGGL(head_kernel, dim3(nblk), dim3(256), lds, s, x, M, gamma, eps, head, V, d, logits, rm, cval,
-                     cidx);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !next) return e;
-  hipLaunchKernelGGL(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next);
+  launch(head_kernel, dim3(nblk), dim3(256), lds, s, x, M, gamma, eps, head, V, d, logits, rm, cval, cidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s) {
+  if (M < 1 || M > 8) return hipErrorInvalidValue;
+  const int nblk = (V + 63) / 64;
+  const float* cval = static_cast<const float*>(scratch);
+  const int* cidx = reinterpret_cast<const int*>(cval + (size_t)M * nblk);
+  launch(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next);
   return hipGetLastError();
 }
 
@@ -447,7 +452,7 @@ __global__ void scatter_rows_kernel(const float* __restrict__ src, int d, RowMap
 }
 
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3(M), dim3(256), 0, s, src, d, rm, dst);
+  launch(scatter_rows_kernel, dim3(M), dim3(256), 0, s, src, d, rm, dst);
   return hipGetLastError();
 }
 

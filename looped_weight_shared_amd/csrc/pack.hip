@@ -55,7 +55,7 @@ hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, i
   const long long total = (long long)(N / 16) * ((K + 127) / 128) * 256;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, qweight, scales, N, K,
+  launch(pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, qweight, scales, N, K,
                      reinterpret_cast<uint32_t*>(dst_tiles), dst_scales, dst_G, nb_offset, nb_stride);
   return hipGetLastError();
 }
@@ -88,7 +88,7 @@ hipError_t launch_unpack(const Packed& p, int8_t* q, uint16_t* scales, hipStream
   const long long total = (long long)(p.N / 16) * p.G * 256;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(threads), 0, s,
+  launch(unpack_kernel, dim3((unsigned)blocks), dim3(threads), 0, s,
                      reinterpret_cast<const uint32_t*>(p.tiles), p.scales, p.N, p.K, p.G, q, scales);
   return hipGetLastError();
 }

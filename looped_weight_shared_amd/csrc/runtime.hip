@@ -138,29 +138,25 @@ struct tl_ctx {
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
   // kernel timing window
   bool prof_on = false;
-  int prof_cap = 0, prof_used = 0, prof_cur = -1;
   std::vector<hipEvent_t> prof_ev;  // 2 per launch
   std::vector<int> prof_kind;
+  tl::LaunchTimer timer;
 };
+
+namespace tl {
+thread_local LaunchTimer* t_launch_timer = nullptr;
+}
 
 namespace {
 
-// Brackets one kernel launch with an event pair while a timing window is open.
+// Sets the kind under which the launches inside the scope are timed while a
+// timing window is open (each launch records its own event pair).
 struct KScope {
-  tl_ctx* c;
-  hipStream_t s;
-  KScope(tl_ctx* ctx, int kind, hipStream_t st) : c(ctx), s(st) {
-    c->prof_cur = -1;
-    if (!c->prof_on || c->prof_used >= c->prof_cap) return;
-    const int i = c->prof_used++;
-    c->prof_kind[i] = kind;
-    (void)hipEventRecord(c->prof_ev[2 * i], s);
-    c->prof_cur = i;
+  KScope(tl_ctx* ctx, int kind, hipStream_t) {
+    tl::t_launch_timer = ctx->prof_on ? &ctx->timer : nullptr;
+    ctx->timer.cur_kind = kind;
   }
-  ~KScope() {
-    if (c->prof_cur >= 0) (void)hipEventRecord(c->prof_ev[2 * c->prof_cur + 1], s);
-    c->prof_cur = -1;
-  }
+  ~KScope() { tl::t_launch_timer = nullptr; }
 };
 
 // Decode-shaped calls (M <= 8) use the split-K-in-block GEMV with the RMSNorm
@@ -471,9 +467,15 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
     tl::RowMap one{};
-    KScope k(ctx, TL_K_HEAD, s);
-    TL_HIP(tl::launch_head(ctx->x + (size_t)(n - 1) * d, 1, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg,
-                           one, ctx->hscr, d_next, s));
+    {
+      KScope k(ctx, TL_K_HEAD, s);
+      TL_HIP(tl::launch_head(ctx->x + (size_t)(n - 1) * d, 1, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg,
+                             one, ctx->hscr, s));
+    }
+    if (d_next) {
+      KScope k(ctx, TL_K_ARGMAX, s);
+      TL_HIP(tl::launch_argmax(1, C.vocab, one, ctx->hscr, d_next, s));
+    }
   }
   ctx->len[lane] = p0 + n;
   ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
@@ -518,9 +520,14 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   }
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
-    KScope k(ctx, TL_K_HEAD, s);
-    TL_HIP(tl::launch_head(ctx->x, M, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg, rm, ctx->hscr, d_next,
-                           s));
+    {
+      KScope k(ctx, TL_K_HEAD, s);
+      TL_HIP(tl::launch_head(ctx->x, M, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg, rm, ctx->hscr, s));
+    }
+    if (d_next) {
+      KScope k(ctx, TL_K_ARGMAX, s);
+      TL_HIP(tl::launch_argmax(M, C.vocab, rm, ctx->hscr, d_next, s));
+    }
   }
   if (d_hidden) {
     KScope k(ctx, TL_K_COPY, s);
@@ -548,8 +555,7 @@ tl_status tl_profile_begin(tl_ctx* ctx, int32_t max_launches) {
     }
   }
   ctx->prof_kind.assign(max_launches, 0);
-  ctx->prof_cap = max_launches;
-  ctx->prof_used = 0;
+  ctx->timer = tl::LaunchTimer{ctx->prof_ev.data(), ctx->prof_kind.data(), max_launches, 0, 0};
   ctx->prof_on = true;
   return TL_OK;
 }
@@ -563,7 +569,7 @@ tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count) {
     count[k] = 0;
   }
   hipError_t err = hipSuccess;
-  for (int i = 0; i < ctx->prof_used && err == hipSuccess; ++i) {
+  for (int i = 0; i < ctx->timer.used && err == hipSuccess; ++i) {
     err = hipEventSynchronize(ctx->prof_ev[2 * i + 1]);
     float ms = 0.f;
     if (err == hipSuccess) err = hipEventElapsedTime(&ms, ctx->prof_ev[2 * i], ctx->prof_ev[2 * i + 1]);
@@ -572,6 +578,7 @@ tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count) {
   }
   for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
   ctx->prof_ev.clear();
+  ctx->timer = tl::LaunchTimer{};
   ctx->prof_on = false;
   if (err != hipSuccess) return fail(TL_E_HIP, std::string("event timing: ") + hipGetErrorString(err));
   return TL_OK;

@@ -1,10 +1,34 @@
 // Host-side launchers of the gfx950 kernels (internal to libtl).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace tl {
+
+// Kernel timing. While a timing window is open on the calling thread, every
+// launch takes the next event pair and attaches it to its own dispatch
+// (hipExtLaunchKernel), so the pair measures that kernel alone, under the
+// kind the caller set.
+struct LaunchTimer {
+  hipEvent_t* ev = nullptr;  // 2 per launch
+  int* kind = nullptr;
+  int cap = 0, used = 0, cur_kind = 0;
+};
+extern thread_local LaunchTimer* t_launch_timer;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
+  LaunchTimer* t = t_launch_timer;
+  if (t && t->used < t->cap) {
+    const int i = t->used++;
+    t->kind[i] = t->cur_kind;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t->ev[2 * i], t->ev[2 * i + 1], 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+}
 
 // A linear in the packed layout: tiles [N/16][G][64 lanes][16 B], then
 // scales fp16 [N/16][G][16]. G = ceil(K / 128).
@@ -114,7 +138,10 @@ hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, con
 // into next[out_row(m)] (second small launch). scratch: head_scratch_bytes.
 size_t head_scratch_bytes(int max_rows, int V);
 hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
-                       float* logits, const RowMap& rm, void* scratch, int32_t* next, hipStream_t s);
+                       float* logits, const RowMap& rm, void* scratch, hipStream_t s);
+// next[out_row(m)] = argmax of row m's logits, from the head's per-block
+// candidates in `scratch` (ties: lowest index).
+hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s);
 // dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
 

@@ -222,7 +222,7 @@ static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& 
     attr_set = true;
   }
   const int blocks = w.N / 16 / NBB;
-  hipLaunchKernelGGL((w4_gemv_kernel<WK, NBB>), dim3(blocks), dim3(WK * 64), lds, s, w.tiles, w.scales, w.N,
+  launch((w4_gemv_kernel<WK, NBB>), dim3(blocks), dim3(WK * 64), lds, s, w.tiles, w.scales, w.N,
                      w.K, w.G, a, M, e);
   return hipGetLastError();
 }
@@ -526,7 +526,7 @@ __global__ void reduce_partials_kernel(const float* __restrict__ part, int S, in
 
 hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float* out, int accumulate, hipStream_t s) {
   const size_t MN = (size_t)M * N;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part, S, M, N, out,
+  launch(reduce_partials_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, part, S, M, N, out,
                      accumulate);
   return hipGetLastError();
 }
@@ -534,7 +534,7 @@ hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float*
 template <int MB, int NBW>
 static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const Epi& e, const GemmPlan& pl,
                               hipStream_t s) {
-  hipLaunchKernelGGL((w4_gemm_kernel<MB, NBW>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K,
+  launch((w4_gemm_kernel<MB, NBW>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K,
                      w.G, A, M, e, pl);
   return hipGetLastError();
 }

@@ -69,6 +69,77 @@ def _traffic(kernel_key, src_files, launches_bytes_expected=None):
     return ent.get("bytes_per_launch")
 
 
+def _pmc_dispatches(d, counter):
+    """(kernel name, grid size, value) per dispatch from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    out = []
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def ingest_pmc(fetch_dir, write_dir, copy_mib):
+    """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
+    `bench.py --steps 3 --warmup 1 --no-cpu --decode-steps 4 --copy-mib <copy_mib>`, one with
+    FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
+    for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
+    fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
+    write = _pmc_dispatches(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2**20
+
+    def pick(rows, pred):
+        v = [x[2] * 1024 for x in rows if pred(x[0], x[1])]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    def is_copy(name, grid):
+        return "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name
+    cf, _ = pick([x for x in fetch if is_copy(x[0], x[1])][-1:], lambda n, g: True)
+    cw, _ = pick([x for x in write if is_copy(x[0], x[1])][-1:], lambda n, g: True)
+    if not cf or not cw:
+        raise SystemExit("no copy-kernel dispatch found in the counter runs")
+    kf, kw = copy_bytes / cf, copy_bytes / cw
+    d, f = 2048, 5632
+    kernels = {
+        # dominant prefill kernel: gate/up GEMM at M=128 (the only <4, 2> instance of the bench)
+        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<4, 2>" in n,
+                         tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
+        # decode gate/up GEMV (the only <8, 2> GEMV instance)
+        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<8, 2>" in n,
+                         tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    run = "bench.py --steps 3 --warmup 1 --no-cpu --decode-steps 4 --copy-mib %d" % copy_mib
+    data = {"commands": [
+        "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
+        "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,
+        "python bench.py --ingest-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write --copy-mib %d" % copy_mib],
+        "note": "per-dispatch KiB counters x 1024 x (copy bytes / the counter's reading for the plain device copy); "
+                "bytes_per_launch = scaled FETCH_SIZE + scaled WRITE_SIZE, averaged over the kernel's dispatches"}
+    for key, (pred, algo) in kernels.items():
+        fb, nf = pick(fetch, pred)
+        wb, nw = pick(write, pred)
+        if fb is None or wb is None:
+            continue
+        data[key] = {"source_hash": _src_hash("w4mm.hip", "tl_device.h"),
+                     "bytes_per_launch": round(fb * kf + wb * kw),
+                     "fetch_bytes_per_launch": round(fb * kf), "write_bytes_per_launch": round(wb * kw),
+                     "algorithmic_bytes_per_launch": algo, "dispatches": [nf, nw],
+                     "copy_calibration": {"bytes": copy_bytes, "fetch_factor": round(kf, 4),
+                                          "write_factor": round(kw, 4)}}
+    with open(path, "w") as fo:
+        json.dump(data, fo, indent=1)
+    print(json.dumps(data, indent=1))
+
+
+def tl_packed_bytes(N, K):
+    """Packed bytes of an N x K W4 linear: 1 KiB per 16x128 tile plus 32 B of scales."""
+    return (N // 16) * ((K + 127) // 128) * 1056
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,7 +150,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mib or 256)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; the forward pass would shard across GPUs by lanes (data parallel).",
@@ -230,6 +308,13 @@ def main():
                                "kind": "oracle",
                                "sample": f"{n} x float64 oracle prefill of the same 128-token L=8 step "
                                          f"({el:.1f} s; weight dequantization not timed)"}
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib * 2**18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(out), flush=True)
 
 

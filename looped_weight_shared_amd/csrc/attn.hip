@@ -11,7 +11,8 @@
 // LDS, S = Q K^T and O += P V on v_mfma_f32_16x16x32_f16, online softmax in
 // fp32 (running max and sum per row). INT8 codes are exact in fp16, so the
 // MFMAs run on the codes and the per-key scales multiply the score columns
-// and the probabilities (P is rounded to fp16 for the PV MFMA).
+// and the probabilities. P enters the PV MFMA as two fp16 parts (high part and
+// the rounded remainder), so the weights keep about 22 significant bits.
 //
 // Decode: one query per lane; see attn_decode_kernel below.
 #include <type_traits>
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   constexpr int LV = 64 + 8;      // LDS row stride of the transposed V tile
   __shared__ __align__(16) _Float16 Ks[64 * LK];
   __shared__ __align__(16) _Float16 Vt[HD * LV];
-  __shared__ __align__(16) _Float16 Ps[4][16 * LV];
+  __shared__ __align__(16) _Float16 Ps[4][2][16 * LV];  // P as fp16 high and low parts
   __shared__ float ksc[64], vsc[64];
 
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
@@ -167,17 +168,28 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
       for (int b = 0; b < DB; ++b) oacc[b][r] *= alpha;
     }
-    // ---- P (fp16, value scale folded in) through LDS into A-operand order
+    // ---- P (value scale folded in) through LDS into A-operand order, split
+    // into an fp16 high part and the fp16 rounding of the remainder: the two
+    // MFMAs below then apply P with about 22 significant bits instead of 11,
+    // so the softmax weights are not rounded to fp16 before the weighted sum.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const float vs = vsc[kb * 16 + l16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ps[wave][(4 * lq + r) * LV + kb * 16 + l16] = (_Float16)(sv[kb][r] * vs);
+      for (int r = 0; r < 4; ++r) {
+        const float x = sv[kb][r] * vs;
+        const _Float16 hi = (_Float16)x;
+        Ps[wave][0][(4 * lq + r) * LV + kb * 16 + l16] = hi;
+        Ps[wave][1][(4 * lq + r) * LV + kb * 16 + l16] = (_Float16)(x - (float)hi);
+      }
     }
     __syncthreads();
-    half8_t pa[2];
+    half8_t pa[2], pl[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) pa[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][l16 * LV + 32 * s + 8 * lq]);
+    for (int s = 0; s < 2; ++s) {
+      pa[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][0][l16 * LV + 32 * s + 8 * lq]);
+      pl[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][1][l16 * LV + 32 * s + 8 * lq]);
+    }
     // ---- O += P V
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -185,6 +197,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
       for (int s = 0; s < 2; ++s) {
         const half8_t bf = *reinterpret_cast<const half8_t*>(&Vt[(b * 16 + l16) * LV + 32 * s + 8 * lq]);
         oacc[b] = mfma16(pa[s], bf, oacc[b]);
+        oacc[b] = mfma16(pl[s], bf, oacc[b]);
       }
     }
     __syncthreads();

@@ -108,11 +108,6 @@ ActLayout act_layout(const tl_config* c) {
 }
 
 // The GEMV kernel keeps all M activation rows of K in LDS.
-bool gemv_fits(int M, int K) {
-  const size_t G = (K + 127) / 128;
-  const size_t lds = (((size_t)M * (G * 128 + 8) * 2 + 15) & ~(size_t)15) + 8 * 2 * 256 * 4 + 9 * 16 * 4;
-  return M >= 1 && M <= 16 && lds <= 160 * 1024;
-}
 
 }  // namespace
 
@@ -165,7 +160,7 @@ struct KScope {
 tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, int M, const tl::Epi& e,
                  int* S_out, hipStream_t s) {
   *S_out = 1;
-  if (M <= 8 && gemv_fits(M, w.K)) {
+  if (tl::gemv_supported(M, w.K, src.x32 != nullptr)) {
     KScope k(c, kind, s);
     TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
     return TL_OK;
@@ -631,7 +626,7 @@ tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_
   const tl::Packed p = packed_view(d_packed, N, K);
   const tl::Epi e{tl::EPI_STORE, d_C, nullptr, N};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (M <= 8 && gemv_fits(M, K)) {
+  if (tl::gemv_supported(M, K, false)) {
     TL_HIP(tl::launch_w4_gemv(p, tl::ASrc{d_A, nullptr, nullptr, 0.f}, M, e, s));
     return TL_OK;
   }

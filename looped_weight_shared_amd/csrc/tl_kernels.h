@@ -67,7 +67,10 @@ struct ASrc {
   float eps;
 };
 
-// C = A * W^T for M <= 16 rows (decode GEMV shape); K split across waves.
+// C = A * W^T for M <= 8 rows (decode GEMV shape); K split across waves.
+// With a.x32 set the A operand is fp16(RMSNorm(x32) * gamma), which needs
+// ceil(K/128) <= 16; gemv_supported tells whether a shape can run here.
+bool gemv_supported(int M, int K, bool norm);
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s);
 // Launch plan of the prefill GEMM: row tile 16*mb, nbw n-blocks per wave,
 // gx column blocks x gy row tiles x S K-splits of gps groups each.

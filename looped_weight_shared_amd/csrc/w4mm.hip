@@ -41,144 +41,162 @@ __device__ __forceinline__ void epi_swiglu(const Epi& e, int m, int c, float g, 
 }
 
 // ---------------------------------------------------------------- GEMV
-constexpr int kGemvMaxIt = 8;  // weight tiles kept in flight per wave and n-block
-constexpr int kNormKpt = 4;    // residual elements per thread held in registers by the fused RMSNorm
+// Decode-shaped products (M <= 8 rows). A block owns NBB n-blocks of 16
+// output rows; its 8 waves split the K groups (wave w takes groups w, w+8,
+// ...). The block stages the M activation rows in LDS as fp16 (the MFMA A
+// operand; rows >= M read as zero) and every wave reads its fragments from
+// there. Order of work, chosen so no wait ever covers the weight requests:
+//   1. each thread requests its activation elements (coalesced), then
+//   2. each wave requests all its weight tiles and scales;
+//   3. activation math (NORM: per-row sums of squares, one LDS exchange,
+//      h = fp16(x * rinv * gamma)) and the LDS stores, barrier (LDS only);
+//   4. dequant + MFMA as the tiles arrive; fixed-order cross-wave sum.
+// The vmcnt counter is in order, so the activation requests go first; the
+// empty asm statements keep the compiler from hoisting the activation math
+// (and its waits) above the weight requests.
+constexpr int kGemvWaves = 8;
+constexpr int kGemvThreads = kGemvWaves * 64;
+constexpr int kGemvIt = 8;        // groups per wave at most: K <= 8 * 8 * 128
+constexpr int kGemvAChunks = 16;  // fp16 16-byte chunks per thread at most: M * K <= 8 * 8192
 
-template <int WK, int NBB>
-__global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
-                                                          const uint16_t* __restrict__ scales, int N, int K,
-                                                          int G, ASrc a, int M, Epi e) {
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// GI: groups requested per wave (ceil(G / 8) rounded up to 2 or 8; a wave
+// with fewer groups re-requests its last one and skips it in the math). APT:
+// fp16 activation chunks per thread (fp16 input). All requests are
+// unconditional with clamped addresses, so the code between them is
+// straight-line and the compiler's waits stay exact.
+template <int NBB, bool NORM, int MR, int GI, int APT>
+__global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
+                                                               const uint16_t* __restrict__ scales, int N, int K,
+                                                               int G, ASrc a, int M, Epi e) {
+  constexpr int WK = kGemvWaves;
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float red[WK * NBB * 256];
+  __shared__ float nrm[WK][MR];
   const int lda = G * 128 + 8;  // LDS row stride in halves (16-byte pad)
   _Float16* As = reinterpret_cast<_Float16*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (((size_t)M * lda * 2 + 15) & ~(size_t)15));
-  float* nrm = red + WK * NBB * 256;  // [WK][16] sum-of-squares partials, then [16] rinv
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int nb0 = blockIdx.x * NBB;
   const int Kp = G * 128;
 
-  // ---- the weight tiles do not depend on the activations: start their loads
-  // before staging the activations so both latencies overlap.
-  u32x4_t wv[kGemvMaxIt][NBB];
-  uint16_t sc[kGemvMaxIt][NBB];  // raw fp16 bits: converting at load time would force a wait
-  auto load_batch = [&](int gb) {
+  // ---- 1. activation requests
+  float4_t xv[NORM ? MR : 1];
+  uint2 gr = {0, 0};
+  u32x4_t av[NORM ? 1 : APT];
+  const int k4 = 4 * tid;  // NORM: this thread's 4 columns (K <= 2048)
+  const int chunks = K / 8, nch = M * chunks;
+  if constexpr (NORM) {
+    const int kc = min(k4, K - 4);
 #pragma unroll
-    for (int it = 0; it < kGemvMaxIt; ++it) {
-      const int g = gb + it * WK;
+    for (int m = 0; m < MR; ++m) xv[m] = *reinterpret_cast<const float4_t*>(a.x32 + (size_t)min(m, M - 1) * K + kc);
+    gr = *reinterpret_cast<const uint2*>(a.gamma + kc);
+  } else {
 #pragma unroll
-      for (int j = 0; j < NBB; ++j) {
-        if (g < G) {
-          const size_t tile = (size_t)(nb0 + j) * G + g;
-          wv[it][j] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes) + lane);
-          sc[it][j] = scales[tile * 16 + l16];
-        }
-      }
+    for (int i = 0; i < APT; ++i) {
+      const int c = min(tid + kGemvThreads * i, nch - 1);
+      const int m = c / chunks, kk = (c - m * chunks) * 8;
+      av[i] = *reinterpret_cast<const u32x4_t*>(a.a16 + (size_t)m * K + kk);
     }
-  };
-  load_batch(wave);
+  }
+  // ---- 2. weight requests
+  u32x4_t wv[GI][NBB];
+  uint32_t sc[GI][NBB];  // raw fp16 bits: converting at load time would force a wait
+#pragma unroll
+  for (int it = 0; it < GI; ++it) {
+    const int g = min(wave + it * WK, G - 1);
+#pragma unroll
+    for (int j = 0; j < NBB; ++j) {
+      const size_t tile = (size_t)(nb0 + j) * G + g;
+      wv[it][j] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes) + lane);
+      sc[it][j] = scales[tile * 16 + l16];
+    }
+  }
+  asm volatile("" ::: "memory");
+  if constexpr (NORM) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) asm volatile("" : "+v"(xv[m]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) asm volatile("" : "+v"(av[i]));
+  }
 
-  // ---- stage the M activation rows (fp16) into LDS
-  if (a.x32 && K <= kNormKpt * WK * 64 && M <= 8) {
-    // every x and gamma element this thread needs, in one round trip
-    float xv[8][kNormKpt];
-    float gv[kNormKpt];
+  // ---- 3. activations into LDS
+  if constexpr (NORM) {
+    const bool kin = k4 < K;
 #pragma unroll
-    for (int i = 0; i < kNormKpt; ++i) {
-      const int k = tid + WK * 64 * i;
-      gv[i] = k < K ? h2f(a.gamma[k]) : 0.f;
+    for (int m = 0; m < MR; ++m) {
+      float ss = 0.f;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) xv[m][i] = (m < M && k < K) ? a.x32[(size_t)m * K + k] : 0.f;
+      for (int c = 0; c < 4; ++c) ss = fmaf(xv[m][c], xv[m][c], ss);
+      ss = wave_sum(kin ? ss : 0.f);
+      if (lane == 0) nrm[wave][m] = ss;
     }
+    lds_barrier();
+    const half2_t* gh = reinterpret_cast<const half2_t*>(&gr);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < M) {
-        float acc = 0.f;
+    for (int m = 0; m < MR; ++m) {
+      if (m < M && k4 < Kp) {
+        float t = 0.f;
 #pragma unroll
-        for (int i = 0; i < kNormKpt; ++i) acc += xv[m][i] * xv[m][i];
-        acc = wave_sum(acc);
-        if (lane == 0) nrm[wave * 16 + m] = acc;
-      }
-    }
-    __syncthreads();
-    if (tid < M) {
-      float t = 0.f;
-      for (int w = 0; w < WK; ++w) t += nrm[w * 16 + tid];
-      nrm[WK * 16 + tid] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < M) {
-        const float rinv = nrm[WK * 16 + m];
-#pragma unroll
-        for (int i = 0; i < kNormKpt; ++i) {
-          const int k = tid + WK * 64 * i;
-          if (k < Kp) As[m * lda + k] = (_Float16)(k < K ? (xv[m][i] * rinv) * gv[i] : 0.f);
-        }
-      }
-    }
-  } else if (a.x32) {
-    for (int m = 0; m < M; ++m) {
-      const float* xr = a.x32 + (size_t)m * K;
-      float acc = 0.f;
-      for (int k = tid; k < K; k += WK * 64) acc += xr[k] * xr[k];
-      acc = wave_sum(acc);
-      if (lane == 0) nrm[wave * 16 + m] = acc;
-    }
-    __syncthreads();
-    if (tid < M) {
-      float t = 0.f;
-      for (int w = 0; w < WK; ++w) t += nrm[w * 16 + tid];
-      nrm[WK * 16 + tid] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-    for (int m = 0; m < M; ++m) {
-      const float rinv = nrm[WK * 16 + m];
-      const float* xr = a.x32 + (size_t)m * K;
-      for (int k = tid; k < Kp; k += WK * 64) {
-        float v = 0.f;
-        if (k < K) v = (xr[k] * rinv) * h2f(a.gamma[k]);
-        As[m * lda + k] = (_Float16)v;
+        for (int w = 0; w < WK; ++w) t += nrm[w][m];
+        const float rinv = 1.0f / sqrtf(t / (float)K + a.eps);
+        half2_t h01, h23;
+        h01.x = (_Float16)((xv[m][0] * rinv) * (float)gh[0].x);
+        h01.y = (_Float16)((xv[m][1] * rinv) * (float)gh[0].y);
+        h23.x = (_Float16)((xv[m][2] * rinv) * (float)gh[1].x);
+        h23.y = (_Float16)((xv[m][3] * rinv) * (float)gh[1].y);
+        const half2_t z2 = {0, 0};
+        *reinterpret_cast<half2_t*>(As + m * lda + k4) = kin ? h01 : z2;
+        *reinterpret_cast<half2_t*>(As + m * lda + k4 + 2) = kin ? h23 : z2;
       }
     }
   } else {
-    const int chunks = Kp / 8;
-    for (int i = tid; i < M * chunks; i += WK * 64) {
-      const int m = i / chunks, c = (i - m * chunks) * 8;
-      u32x4_t v = {0, 0, 0, 0};
-      if (c < K) v = *reinterpret_cast<const u32x4_t*>(a.a16 + (size_t)m * K + c);
-      *reinterpret_cast<u32x4_t*>(As + m * lda + c) = v;
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int c = tid + kGemvThreads * i;
+      if (c < nch) {
+        const int m = c / chunks, kk = (c - m * chunks) * 8;
+        *reinterpret_cast<u32x4_t*>(As + m * lda + kk) = av[i];
+      }
+    }
+    // zero columns K..Kp-1 of the M rows (K not a multiple of 128)
+    const int padc = (Kp - K) / 8;
+    for (int c = tid; c < M * padc; c += kGemvThreads) {
+      const int m = c / padc;
+      *reinterpret_cast<u32x4_t*>(As + m * lda + K + (c - m * padc) * 8) = (u32x4_t){0, 0, 0, 0};
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- K groups g = wave, wave + WK, ... ; up to kGemvMaxIt tiles in flight
+  // ---- 4. dequant + MFMA per group, scaled once per group
   float4_t acc[NBB];
 #pragma unroll
   for (int j = 0; j < NBB; ++j) acc[j] = (float4_t){0.f, 0.f, 0.f, 0.f};
   const bool arow = l16 < M;
   const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int gb = wave; gb < G; gb += WK * kGemvMaxIt) {
-    if (gb != wave) load_batch(gb);
 #pragma unroll
-    for (int it = 0; it < kGemvMaxIt; ++it) {
-      const int g = gb + it * WK;
-      if (g < G) {
-        half8_t af[4];
+  for (int it = 0; it < GI; ++it) {
+    const int g = wave + it * WK;
+    if (g < G) {
+      half8_t af[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          af[s] = arow ? *reinterpret_cast<const half8_t*>(As + l16 * lda + g * 128 + 32 * s + 8 * lq) : hz;
+      for (int s = 0; s < 4; ++s)
+        af[s] = arow ? *reinterpret_cast<const half8_t*>(As + l16 * lda + g * 128 + 32 * s + 8 * lq) : hz;
 #pragma unroll
-        for (int j = 0; j < NBB; ++j) {
-          float4_t t = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NBB; ++j) {
+        float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) t = mfma16(af[s], dequant_word(wv[it][j][s]), t);
-          const float scf = h2f(sc[it][j]);
+        for (int s = 0; s < 4; ++s) t = mfma16(af[s], dequant_word(wv[it][j][s]), t);
+        const float scf = h2f((uint16_t)sc[it][j]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], scf, acc[j][r]);
-        }
+        for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], scf, acc[j][r]);
       }
     }
   }
@@ -210,27 +228,52 @@ __global__ __launch_bounds__(WK * 64) void w4_gemv_kernel(const uint8_t* __restr
   }
 }
 
-template <int WK, int NBB>
+bool gemv_supported(int M, int K, bool norm) {
+  const int G = (K + 127) / 128;
+  if (M < 1 || M > 8 || K < 8 || K % 8) return false;
+  if (norm) return K <= 4 * kGemvThreads;                       // one float4 per thread and row
+  return G <= kGemvWaves * kGemvIt && M * (K / 8) <= kGemvThreads * kGemvAChunks;
+}
+
+template <int NBB, bool NORM, int MR, int GI, int APT>
 static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
-  const size_t lds = (((size_t)M * (w.G * 128 + 8) * 2 + 15) & ~(size_t)15) + (size_t)WK * NBB * 256 * 4 +
-                     (size_t)(WK + 1) * 16 * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<WK, NBB>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<NBB, NORM, MR, GI, APT>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int blocks = w.N / 16 / NBB;
-  launch((w4_gemv_kernel<WK, NBB>), dim3(blocks), dim3(WK * 64), lds, s, w.tiles, w.scales, w.N,
-                     w.K, w.G, a, M, e);
+  const size_t lds = (size_t)M * (w.G * 128 + 8) * 2;
+  launch((w4_gemv_kernel<NBB, NORM, MR, GI, APT>), dim3(w.N / 16 / NBB), dim3(kGemvThreads), lds, s, w.tiles, w.scales,
+         w.N, w.K, w.G, a, M, e);
   return hipGetLastError();
 }
 
+// fused RMSNorm: K <= 2048, so at most 2 groups per wave
+template <int NBB>
+static hipError_t gemv_norm_rows(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+  if (M == 1) return gemv_launch<NBB, true, 1, 2, 1>(w, a, M, e, s);
+  if (M == 2) return gemv_launch<NBB, true, 2, 2, 1>(w, a, M, e, s);
+  if (M <= 4) return gemv_launch<NBB, true, 4, 2, 1>(w, a, M, e, s);
+  return gemv_launch<NBB, true, 8, 2, 1>(w, a, M, e, s);
+}
+
+template <int GI>
+static hipError_t gemv_a16(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+  const int apt = (M * (w.K / 8) + kGemvThreads - 1) / kGemvThreads;
+  if (apt <= 1) return gemv_launch<1, false, 1, GI, 1>(w, a, M, e, s);
+  if (apt <= 2) return gemv_launch<1, false, 1, GI, 2>(w, a, M, e, s);
+  if (apt <= 4) return gemv_launch<1, false, 1, GI, 4>(w, a, M, e, s);
+  if (apt <= 8) return gemv_launch<1, false, 1, GI, 8>(w, a, M, e, s);
+  return gemv_launch<1, false, 1, GI, 16>(w, a, M, e, s);
+}
+
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
-  if (M < 1 || M > 16) return hipErrorInvalidValue;
-  if (e.mode == EPI_SWIGLU) return gemv_launch<8, 2>(w, a, M, e, s);
-  return gemv_launch<8, 1>(w, a, M, e, s);
+  const bool norm = a.x32 != nullptr;
+  if (!gemv_supported(M, w.K, norm) || (!norm && e.mode == EPI_SWIGLU)) return hipErrorInvalidValue;
+  if (norm) return e.mode == EPI_SWIGLU ? gemv_norm_rows<2>(w, a, M, e, s) : gemv_norm_rows<1>(w, a, M, e, s);
+  return w.G <= 2 * kGemvWaves ? gemv_a16<2>(w, a, M, e, s) : gemv_a16<8>(w, a, M, e, s);
 }
 
 // ---------------------------------------------------------------- GEMM

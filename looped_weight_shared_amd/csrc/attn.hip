@@ -226,29 +226,41 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 }
 
 // ------------------------------------------------------------------ decode
-// A block (8 waves) covers up to 512 keys of the context 0..pos of one row's
-// lane for one head; wave w takes the 64-key chunk 8*blockIdx.x + w. The wave
-// first issues every K and V load of its chunk (32 KiB in flight for FP16 KV),
-// then builds Q = fp16(RoPE(q)) for its 8 dims from the raw QKV projection.
-// The wave whose chunk holds the new position also rotates/rounds (and, in
-// INT8 mode, quantizes) the new K and V, stores them in the cache and scores
-// that key from registers. Lanes are 16 per key (8 dims each) x 4 keys per
-// pass. Waves merge in LDS in wave order; a row whose context spans several
-// blocks gets its blocks merged in block order by attn_merge_kernel.
+// A block (2 waves) covers 128 keys of the context 0..pos of one row's lane
+// for one head; wave w takes the 64-key chunk 2*blockIdx.x + w. Lanes are 16
+// per key (8 dims each) x 4 keys per pass. Order of work, so that no wait
+// covers the cache reads:
+//   1. the row's q, k, v projections for this lane's 8 dims (and their RoPE
+//      partners) and the cos/sin of position pos;
+//   2. every K and V row of the chunk (positions < pos; addresses clamped,
+//      values outside the context replaced by zeros);
+//   3. Q = fp16(RoPE(q)); the wave whose chunk holds pos also rotates/rounds
+//      (INT8: quantizes) the new K and V, stores them in the cache and scores
+//      that key from registers; scores, softmax, P V.
+// The two waves merge in LDS and the block writes its softmax state (a
+// block beyond the row's context writes max = -inf); the parts are combined
+// in part order either by attn_merge_kernel or inside the O-projection GEMV.
 constexpr int kDecChunk = 64;
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 2;
 constexpr int kDecPart = kDecChunk * kDecWaves;  // keys per block
 
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S) {
   const int np = (S + kDecPart - 1) / kDecPart;
-  return (size_t)max_rows * H * np * (hd + 2);
+  return (size_t)max_rows * H * np * (hd + kAttnPartExtra);
+}
+
+int attn_decode_np_max(int S) { return (S + kDecPart - 1) / kDecPart; }
+
+int attn_decode_parts(int M, const RowMap& rm) {
+  int maxctx = 0;
+  for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1);
+  return (maxctx + kDecPart - 1) / kDecPart;
 }
 
 template <int HD, bool I8>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float* __restrict__ qkv, RowMap rm,
                                                                      const float* __restrict__ rope_cs, KvGeom kv,
-                                                                     int layer, float* __restrict__ part, int np_max,
-                                                                     uint16_t* __restrict__ o) {
+                                                                     int layer, float* __restrict__ part, int np_max) {
   constexpr int LPK = HD / 8;    // lanes per key
   constexpr int KPP = 64 / LPK;  // keys per pass
   constexpr int NP = kDecChunk / KPP;
@@ -258,7 +270,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
   const int pos = rm.row_pos[m], ctx = pos + 1;
   const int nparts = (ctx + kDecPart - 1) / kDecPart;
-  if (bp >= nparts) return;  // the whole block exits
+  float* dst = part + ((size_t)(m * kv.H + h) * np_max + bp) * (HD + kAttnPartExtra);
+  if (bp >= nparts) {  // beyond this row's context: an empty part
+    if (threadIdx.x == 0) {
+      dst[HD] = -INFINITY;
+      dst[HD + 1] = 0.f;
+    }
+    return;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int sub = ln % LPK, kg = ln / LPK, d0 = sub * 8;
   const int d = kv.H * HD;
@@ -268,41 +287,48 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   const int k0 = (bp * kDecWaves + wave) * kDecChunk;
   const bool active = k0 <= pos;
 
-  // ---- all loads of the chunk's cached keys (positions < pos): 8 dims per
-  // lane, fp16 (16 B) or int8 codes (8 B) plus the row scales
-  using Row = typename std::conditional<I8, uint2, u32x4_t>::type;
-  Row kr[NP], vr[NP];
-  float ks[I8 ? NP : 1], vs[I8 ? NP : 1];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int key = k0 + p * KPP + kg;
-    kr[p] = vr[p] = Row{};
-    if constexpr (I8) ks[p] = vs[p] = 1.f;
-    if (key < pos) {
-      kr[p] = *reinterpret_cast<const Row*>(cp.k + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
-      vr[p] = *reinterpret_cast<const Row*>(cp.v + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
-      if constexpr (I8) {
-        ks[p] = h2f(cp.ks[key]);
-        vs[p] = h2f(cp.vs[key]);
-      }
-    }
-  }
-
-  // ---- Q = fp16(RoPE(q)) for dims d0..d0+7 (pair partner is dim +-HALF)
-  const float* row = qkv + (size_t)m * 3 * d;
-  const float* cosr = rope_cs + (size_t)pos * HALF;
-  const float* sinr = rope_cs + (size_t)kv.S * HALF + (size_t)pos * HALF;
+  // ---- 1. projections of this row (8 dims + their RoPE partners) and cos/sin
   const bool lo = d0 < HALF;
   const int i0 = lo ? d0 : d0 - HALF;  // pair index of the first dim
-  float qv[8];
-  {
-    const float* qh = row + h * HD;
+  const float* row = qkv + (size_t)m * 3 * d;
+  const float4_t* q1p = reinterpret_cast<const float4_t*>(row + h * HD + i0);
+  const float4_t* q2p = reinterpret_cast<const float4_t*>(row + h * HD + i0 + HALF);
+  const float4_t* k1p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0);
+  const float4_t* k2p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0 + HALF);
+  const float4_t* vp = reinterpret_cast<const float4_t*>(row + 2 * d + h * HD + d0);
+  const float4_t* cp4 = reinterpret_cast<const float4_t*>(rope_cs + (size_t)pos * HALF + i0);
+  const float4_t* sp4 = reinterpret_cast<const float4_t*>(rope_cs + (size_t)kv.S * HALF + (size_t)pos * HALF + i0);
+  float4_t q1[2] = {q1p[0], q1p[1]}, q2[2] = {q2p[0], q2p[1]};
+  float4_t k1[2] = {k1p[0], k1p[1]}, k2[2] = {k2p[0], k2p[1]};
+  float4_t vv[2] = {vp[0], vp[1]};
+  float4_t cs[2] = {cp4[0], cp4[1]}, sn[2] = {sp4[0], sp4[1]};
+
+  // ---- 2. the chunk's cached keys and values (positions < pos)
+  using Row = typename std::conditional<I8, uint2, u32x4_t>::type;
+  Row kr[NP], vr[NP];
+  uint32_t ksr[I8 ? NP : 1], vsr[I8 ? NP : 1];  // raw fp16 scales
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      _Float16 r1, r2;
-      rope_pair(qh[i0 + j], qh[i0 + j + HALF], cosr[i0 + j], sinr[i0 + j], &r1, &r2);
-      qv[j] = (float)(lo ? r1 : r2);
+  for (int p = 0; p < NP; ++p) {
+    const int key = max(min(k0 + p * KPP + kg, pos - 1), 0);
+    kr[p] = *reinterpret_cast<const Row*>(cp.k + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
+    vr[p] = *reinterpret_cast<const Row*>(cp.v + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
+    if constexpr (I8) {
+      ksr[p] = cp.ks[key];
+      vsr[p] = cp.vs[key];
     }
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    asm volatile("" : "+v"(q1[i]), "+v"(q2[i]), "+v"(k1[i]), "+v"(k2[i]), "+v"(vv[i]), "+v"(cs[i]), "+v"(sn[i]));
+
+  // ---- 3. Q = fp16(RoPE(q)) for dims d0..d0+7 (pair partner is dim +-HALF)
+  float qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    _Float16 r1, r2;
+    rope_pair(q1[j >> 2][j & 3], q2[j >> 2][j & 3], cs[j >> 2][j & 3], sn[j >> 2][j & 3], &r1, &r2);
+    qv[j] = (float)(lo ? r1 : r2);
   }
   // ---- the new key/value (only the chunk that holds pos)
   const bool own = (pos >= k0) && (pos < k0 + kDecChunk);
@@ -310,15 +336,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
 #pragma unroll
   for (int j = 0; j < 8; ++j) kn[j] = vn[j] = 0.f;
   if (own) {
-    const float* kh = row + d + h * HD;
-    const float* vh = row + 2 * d + h * HD;
     _Float16 kf[8], vf[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       _Float16 r1, r2;
-      rope_pair(kh[i0 + j], kh[i0 + j + HALF], cosr[i0 + j], sinr[i0 + j], &r1, &r2);
+      rope_pair(k1[j >> 2][j & 3], k2[j >> 2][j & 3], cs[j >> 2][j & 3], sn[j >> 2][j & 3], &r1, &r2);
       kf[j] = lo ? r1 : r2;
-      vf[j] = (_Float16)vh[d0 + j];
+      vf[j] = (_Float16)vv[j >> 2][j & 3];
     }
     const bool writer = (kg == 0);
     if constexpr (I8) {
@@ -378,27 +402,25 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int key = k0 + p * KPP + kg;
-    float t = 0.f;
-    if (key < pos) {
-      if constexpr (I8) {
+    float t = 0.f, tn = 0.f;
+    if constexpr (I8) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w = j < 4 ? kr[p].x : kr[p].y;
-          t = fmaf(qv[j], (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF), t);
-        }
-      } else {
-        const half8_t kh8 = __builtin_bit_cast(half8_t, kr[p]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t = fmaf(qv[j], (float)kh8[j], t);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w = j < 4 ? kr[p].x : kr[p].y;
+        t = fmaf(qv[j], (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF), t);
       }
-    } else if (key == pos) {
+    } else {
+      const half8_t kh8 = __builtin_bit_cast(half8_t, kr[p]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t = fmaf(qv[j], kn[j], t);
+      for (int j = 0; j < 8; ++j) t = fmaf(qv[j], (float)kh8[j], t);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tn = fmaf(qv[j], kn[j], tn);
+    t = key < pos ? t : (key == pos ? tn : 0.f);
 #pragma unroll
     for (int off = LPK / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
     float kscale = ksn;
-    if constexpr (I8) kscale = key < pos ? ks[p] : ksn;
+    if constexpr (I8) kscale = key < pos ? h2f((uint16_t)ksr[p]) : ksn;
     sc[p] = key <= pos ? t * scale * kscale : -INFINITY;
     mx = fmaxf(mx, sc[p]);
   }
@@ -412,24 +434,23 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
       const int key = k0 + p * KPP + kg;
       const float pr = key <= pos ? expf(sc[p] - mx) : 0.f;
       if (sub == 0) lsum += pr;
-      if (key < pos) {
-        if constexpr (I8) {
-          const float pv = pr * vs[p];
+      float vrow[8];
+      if constexpr (I8) {
+        const float vsc = h2f((uint16_t)vsr[p]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t w = j < 4 ? vr[p].x : vr[p].y;
-            ov[j] = fmaf(pv, (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF), ov[j]);
-          }
-        } else {
-          const float pv = pr;
-          const half8_t vh8 = __builtin_bit_cast(half8_t, vr[p]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ov[j] = fmaf(pv, (float)vh8[j], ov[j]);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = j < 4 ? vr[p].x : vr[p].y;
+          vrow[j] = (float)(int8_t)((w >> (8 * (j & 3))) & 0xFF) * vsc;
         }
-      } else if (key == pos) {
-        const float pv = pr * vsn;
+      } else {
+        const half8_t vh8 = __builtin_bit_cast(half8_t, vr[p]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ov[j] = fmaf(pv, vn[j], ov[j]);
+        for (int j = 0; j < 8; ++j) vrow[j] = (float)vh8[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float vj = key < pos ? vrow[j] : (key == pos ? vn[j] * vsn : 0.f);
+        ov[j] = fmaf(pr, vj, ov[j]);
       }
     }
   }
@@ -459,64 +480,50 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
       num = fmaf(sw, red_o[w][tid], num);
       den = fmaf(sw, red_l[w], den);
     }
-    if (nparts == 1) {
-      o[(size_t)m * d + h * HD + tid] = f2h(num / den);
-    } else {
-      float* dst = part + ((size_t)(m * kv.H + h) * np_max + bp) * (HD + 2);
-      dst[tid] = num;
-      if (tid == 0) {
-        dst[HD] = bm;
-        dst[HD + 1] = den;
-      }
+    dst[tid] = num;
+    if (tid == 0) {
+      dst[HD] = bm;
+      dst[HD + 1] = den;
     }
   }
 }
 
-// Rows whose context spans several blocks: merge the block results in block order.
+// Combine the np parts of every (row, head) in part order into fp16 O.
 template <int HD>
-__global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict__ part, RowMap rm, int H, int np_max,
+__global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict__ part, int H, int np, int np_max,
                                                         uint16_t* __restrict__ o) {
   const int h = blockIdx.x, m = blockIdx.y;
-  const int nparts = (rm.row_pos[m] + 1 + kDecPart - 1) / kDecPart;
-  if (nparts < 2) return;
-  const float* base = part + (size_t)(m * H + h) * np_max * (HD + 2);
+  const float* base = part + (size_t)(m * H + h) * np_max * (HD + kAttnPartExtra);
   float gm = -INFINITY;
-  for (int q = 0; q < nparts; ++q) gm = fmaxf(gm, base[(size_t)q * (HD + 2) + HD]);
+  for (int q = 0; q < np; ++q) gm = fmaxf(gm, base[(size_t)q * (HD + kAttnPartExtra) + HD]);
   const int i = threadIdx.x;
   float num = 0.f, den = 0.f;
-  for (int q = 0; q < nparts; ++q) {
-    const float* pq = base + (size_t)q * (HD + 2);
-    const float w = expf(pq[HD] - gm);
-    num = fmaf(w, pq[i], num);
-    den = fmaf(w, pq[HD + 1], den);
+  for (int q = 0; q < np; ++q) {
+    const float* pq = base + (size_t)q * (HD + kAttnPartExtra);
+    attn_merge_step(gm, pq[HD], pq[HD + 1], pq[i], num, den);
   }
   o[(size_t)m * H * HD + h * HD + i] = f2h(num / den);
 }
 
 template <int HD, bool I8>
-static void decode_launch(dim3 grid, int used, const float* qkv, const RowMap& rm, const float* rope_cs,
-                          const KvGeom& kv, int layer, float* part, int np_max, uint16_t* o, hipStream_t s) {
-  launch((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part,
-                     np_max, o);
-  if (used > 1)
-    launch(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, rm, kv.H, np_max, o);
+static void decode_launch(dim3 grid, const float* qkv, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+                          int layer, float* part, int np_max, uint16_t* o, hipStream_t s) {
+  launch((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part, np_max);
+  if (o) launch(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, kv.H, (int)grid.x, np_max, o);
 }
 
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s) {
-  int maxctx = 0;
-  for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1);
-  const int np_max = (kv.S + kDecPart - 1) / kDecPart;
-  const int used = (maxctx + kDecPart - 1) / kDecPart;
-  dim3 grid(used, kv.H, M);
+  const int np_max = attn_decode_np_max(kv.S);
+  dim3 grid(attn_decode_parts(M, rm), kv.H, M);
   if (kv.hd == 128 && kv.int8)
-    decode_launch<128, true>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<128, true>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 128)
-    decode_launch<128, false>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<128, false>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 64 && kv.int8)
-    decode_launch<64, true>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<64, true>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 64)
-    decode_launch<64, false>(grid, used, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<64, false>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

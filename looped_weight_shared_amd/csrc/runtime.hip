@@ -160,7 +160,10 @@ struct KScope {
 tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, int M, const tl::Epi& e,
                  int* S_out, hipStream_t s) {
   *S_out = 1;
-  if (tl::gemv_supported(M, w.K, src.x32 != nullptr)) {
+  // the GEMV's fused RMSNorm reads x as is: pending split-K residual partials
+  // (left by a GEMM) must go through the RMSNorm kernel first
+  const bool pending = src.x32 && c->pend.part;
+  if (!pending && tl::gemv_supported(M, w.K, src)) {
     KScope k(c, kind, s);
     TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
     return TL_OK;
@@ -192,10 +195,22 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
               tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, &S, s);
   if (st != TL_OK) return st;
   const float* qkv = S > 1 ? c->gpart : c->qkv;
+  tl::ASrc osrc{c->o, nullptr, nullptr, 0.f};
   if (decode) {
-    // RoPE, new K/V into cache layer `layer`, single-query attention
+    if (S > 1) {
+      // the decode attention reads whole projections: sum a split GEMM's partials first
+      KScope k(c, TL_K_QKV, s);
+      TL_HIP(tl::launch_reduce_partials(c->gpart, S, M, 3 * d, c->qkv, 0, s));
+      qkv = c->qkv;
+    }
+    // RoPE, new K/V into cache layer `layer`, single-query attention in key
+    // parts; the O projection merges the parts itself when its GEMV can
+    tl::ASrc att{nullptr, nullptr, nullptr, 0.f, c->part, tl::attn_decode_parts(M, rm),
+                 tl::attn_decode_np_max(c->cfg.max_seq), c->cfg.head_dim};
+    const bool fuse = tl::gemv_supported(M, d, att);
     KScope k(c, TL_K_ATTN, s);
-    TL_HIP(tl::launch_attn_decode(qkv, M, rm, c->rope, c->kv, layer, c->part, c->o, s));
+    TL_HIP(tl::launch_attn_decode(qkv, M, rm, c->rope, c->kv, layer, c->part, fuse ? nullptr : c->o, s));
+    if (fuse) osrc = att;
   } else {
     // RoPE on q, k (summing the split-K partials); fp16 Q; K, V into cache layer `layer`
     {
@@ -206,8 +221,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
     TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
   }
   // x += O W_o^T (deferred to the next RMSNorm when K is split)
-  st = linear(c, TL_K_O, B.o, tl::ASrc{c->o, nullptr, nullptr, 0.f}, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d},
-              &S, s);
+  st = linear(c, TL_K_O, B.o, osrc, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, &S, s);
   if (st != TL_OK) return st;
   if (S > 1) c->pend = tl::Pending{c->gpart, S};
   // a = fp16(silu(h2 W_gate^T) * h2 W_up^T), h2 = fp16(RMSNorm(x))
@@ -626,7 +640,7 @@ tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_
   const tl::Packed p = packed_view(d_packed, N, K);
   const tl::Epi e{tl::EPI_STORE, d_C, nullptr, N};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (tl::gemv_supported(M, K, false)) {
+  if (tl::gemv_supported(M, K, tl::ASrc{d_A, nullptr, nullptr, 0.f})) {
     TL_HIP(tl::launch_w4_gemv(p, tl::ASrc{d_A, nullptr, nullptr, 0.f}, M, e, s));
     return TL_OK;
   }

@@ -95,4 +95,19 @@ __device__ __forceinline__ int kv_code(float x, float sf) {
   return (int)fminf(fmaxf(rintf(__fdiv_rn(x, sf)), -127.f), 127.f);
 }
 
+// Decode attention writes, per (row, head, key part), the part's softmax
+// state: weighted value sums [hd], then the running max and the sum of
+// weights, in a row of hd + kAttnPartExtra floats (16-byte aligned rows).
+// Parts are combined in part order by attn_merge_step; a part with max -inf
+// (beyond the row's context) is skipped. The merge kernel and the O-projection
+// GEMV both use this, so either path gives the same bits.
+constexpr int kAttnPartExtra = 4;
+__device__ __forceinline__ void attn_merge_step(float gm, float mp, float lp, float nump, float& num, float& den) {
+  if (mp != -INFINITY) {
+    const float w = expf(mp - gm);
+    num = fmaf(w, nump, num);
+    den = fmaf(w, lp, den);
+  }
+}
+
 }  // namespace tl

@@ -61,16 +61,20 @@ struct Epi {
 // Activation source of the matrix kernels: fp16 rows, or fp32 residual rows
 // normalised on the fly (h = fp16(gamma * x / sqrt(mean(x^2) + eps))).
 struct ASrc {
-  const uint16_t* a16;  // fp16 [M][K] (used when x32 is null)
+  const uint16_t* a16;  // fp16 [M][K] (used when x32 and att are null)
   const float* x32;     // fp32 [M][K] residual rows to RMS-normalise
   const uint16_t* gamma;
   float eps;
+  // decode attention parts to merge into fp16 A rows (K = H * att_hd)
+  const float* att = nullptr;
+  int att_np = 0, att_np_max = 0, att_hd = 0;
 };
 
 // C = A * W^T for M <= 8 rows (decode GEMV shape); K split across waves.
-// With a.x32 set the A operand is fp16(RMSNorm(x32) * gamma), which needs
-// ceil(K/128) <= 16; gemv_supported tells whether a shape can run here.
-bool gemv_supported(int M, int K, bool norm);
+// With a.x32 set the A operand is fp16(RMSNorm(x32) * gamma); with a.att
+// set it is the merged decode attention output. Both need K <= 2048 (and
+// att M * np <= 16); gemv_supported tells whether a call can run here.
+bool gemv_supported(int M, int K, const ASrc& a);
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s);
 // Launch plan of the prefill GEMM: row tile 16*mb, nbw n-blocks per wave,
 // gx column blocks x gy row tiles x S K-splits of gps groups each.
@@ -127,9 +131,14 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
                                uint16_t* o, hipStream_t s);
 // Single-query attention for M decode rows (one per lane) over each lane's
 // rows 0..row_pos[m], from the raw QKV projection qkv fp32 [M][3d]: applies
-// RoPE, writes the new K/V row into cache layer `layer`, attends, O fp16
-// [M][d]. part: scratch floats (used when a context exceeds 512 keys).
+// RoPE, writes the new K/V row into cache layer `layer` and attends in
+// parts of 128 keys: part receives, per (row, head, part), the part's softmax
+// state (np_max = ceil(S / 128) parts per (row, head), rows of hd + 4
+// floats). With o non-null the parts are also merged into O fp16 [M][d];
+// otherwise the O projection merges them (ASrc::att).
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
+int attn_decode_parts(int M, const RowMap& rm);  // parts written per (row, head) this call
+int attn_decode_np_max(int S);                  // part slots per (row, head)
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s);
 

@@ -70,11 +70,14 @@ __device__ __forceinline__ void lds_barrier() {
 // fp16 activation chunks per thread (fp16 input). All requests are
 // unconditional with clamped addresses, so the code between them is
 // straight-line and the compiler's waits stay exact.
-template <int NBB, bool NORM, int MR, int GI, int APT>
+enum GemvSrc { SRC_A16 = 0, SRC_NORM = 1, SRC_ATT = 2 };
+
+template <int NBB, int SRC, int MR, int GI, int APT>
 __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
                                                                const uint16_t* __restrict__ scales, int N, int K,
                                                                int G, ASrc a, int M, Epi e) {
   constexpr int WK = kGemvWaves;
+  constexpr bool NORM = SRC == SRC_NORM, ATT = SRC == SRC_ATT;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float red[WK * NBB * 256];
   __shared__ float nrm[WK][MR];
@@ -87,16 +90,29 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   const int Kp = G * 128;
 
   // ---- 1. activation requests
-  float4_t xv[NORM ? MR : 1];
+  float4_t xv[NORM ? MR : (ATT ? APT : 1)];
+  float2 ml[ATT ? APT : 1];
   uint2 gr = {0, 0};
-  u32x4_t av[NORM ? 1 : APT];
-  const int k4 = 4 * tid;  // NORM: this thread's 4 columns (K <= 2048)
+  u32x4_t av[SRC == SRC_A16 ? APT : 1];
+  const int k4 = 4 * tid;  // NORM/ATT: this thread's 4 columns (K <= 2048)
+  const int kc = min(k4, K - 4);
   const int chunks = K / 8, nch = M * chunks;
+  const int npairs = M * a.att_np;  // ATT: (row, part) pairs, row-major
   if constexpr (NORM) {
-    const int kc = min(k4, K - 4);
 #pragma unroll
     for (int m = 0; m < MR; ++m) xv[m] = *reinterpret_cast<const float4_t*>(a.x32 + (size_t)min(m, M - 1) * K + kc);
     gr = *reinterpret_cast<const uint2*>(a.gamma + kc);
+  } else if constexpr (ATT) {
+    const int H = K / a.att_hd, hh = kc / a.att_hd, i = kc - hh * a.att_hd;
+    const int stride = a.att_hd + kAttnPartExtra;
+#pragma unroll
+    for (int q = 0; q < APT; ++q) {
+      const int qq = min(q, npairs - 1);
+      const int m = qq / a.att_np, p = qq - m * a.att_np;
+      const float* b = a.att + ((size_t)(m * H + hh) * a.att_np_max + p) * stride;
+      xv[q] = *reinterpret_cast<const float4_t*>(b + i);
+      ml[q] = *reinterpret_cast<const float2*>(b + a.att_hd);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
@@ -105,6 +121,7 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
       av[i] = *reinterpret_cast<const u32x4_t*>(a.a16 + (size_t)m * K + kk);
     }
   }
+  asm volatile("" ::: "memory");  // activation requests strictly before the weight requests
   // ---- 2. weight requests
   u32x4_t wv[GI][NBB];
   uint32_t sc[GI][NBB];  // raw fp16 bits: converting at load time would force a wait
@@ -122,6 +139,9 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   if constexpr (NORM) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) asm volatile("" : "+v"(xv[m]));
+  } else if constexpr (ATT) {
+#pragma unroll
+    for (int q = 0; q < APT; ++q) asm volatile("" : "+v"(xv[q]), "+v"(ml[q]));
   } else {
 #pragma unroll
     for (int i = 0; i < APT; ++i) asm volatile("" : "+v"(av[i]));
@@ -152,6 +172,31 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
         h01.y = (_Float16)((xv[m][1] * rinv) * (float)gh[0].y);
         h23.x = (_Float16)((xv[m][2] * rinv) * (float)gh[1].x);
         h23.y = (_Float16)((xv[m][3] * rinv) * (float)gh[1].y);
+        const half2_t z2 = {0, 0};
+        *reinterpret_cast<half2_t*>(As + m * lda + k4) = kin ? h01 : z2;
+        *reinterpret_cast<half2_t*>(As + m * lda + k4 + 2) = kin ? h23 : z2;
+      }
+    }
+  } else if constexpr (ATT) {
+    // merge each row's parts in part order (attn_merge_step), as the merge kernel does
+    const bool kin = k4 < K;
+    for (int m = 0; m < M; ++m) {
+      float gm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < APT; ++q)
+        if (q < npairs && q / a.att_np == m) gm = fmaxf(gm, ml[q].x);
+      float num[4] = {0.f, 0.f, 0.f, 0.f}, den[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < APT; ++q)
+        if (q < npairs && q / a.att_np == m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) attn_merge_step(gm, ml[q].x, ml[q].y, xv[q][c], num[c], den[c]);
+      if (k4 < Kp) {
+        half2_t h01, h23;
+        h01.x = (_Float16)(num[0] / den[0]);
+        h01.y = (_Float16)(num[1] / den[1]);
+        h23.x = (_Float16)(num[2] / den[2]);
+        h23.y = (_Float16)(num[3] / den[3]);
         const half2_t z2 = {0, 0};
         *reinterpret_cast<half2_t*>(As + m * lda + k4) = kin ? h01 : z2;
         *reinterpret_cast<half2_t*>(As + m * lda + k4 + 2) = kin ? h23 : z2;
@@ -228,51 +273,65 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   }
 }
 
-bool gemv_supported(int M, int K, bool norm) {
+bool gemv_supported(int M, int K, const ASrc& a) {
   const int G = (K + 127) / 128;
   if (M < 1 || M > 8 || K < 8 || K % 8) return false;
-  if (norm) return K <= 4 * kGemvThreads;                       // one float4 per thread and row
+  if (a.x32) return K <= 4 * kGemvThreads;  // one float4 per thread and row
+  if (a.att)
+    return K <= 4 * kGemvThreads && a.att_hd >= 4 && a.att_hd % 4 == 0 && K % a.att_hd == 0 && a.att_np >= 1 &&
+           M * a.att_np <= 16;
   return G <= kGemvWaves * kGemvIt && M * (K / 8) <= kGemvThreads * kGemvAChunks;
 }
 
-template <int NBB, bool NORM, int MR, int GI, int APT>
+template <int NBB, int SRC, int MR, int GI, int APT>
 static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<NBB, NORM, MR, GI, APT>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<NBB, SRC, MR, GI, APT>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
   const size_t lds = (size_t)M * (w.G * 128 + 8) * 2;
-  launch((w4_gemv_kernel<NBB, NORM, MR, GI, APT>), dim3(w.N / 16 / NBB), dim3(kGemvThreads), lds, s, w.tiles, w.scales,
-         w.N, w.K, w.G, a, M, e);
+  launch((w4_gemv_kernel<NBB, SRC, MR, GI, APT>), dim3(w.N / 16 / NBB), dim3(kGemvThreads), lds, s, w.tiles,
+         w.scales, w.N, w.K, w.G, a, M, e);
   return hipGetLastError();
 }
 
 // fused RMSNorm: K <= 2048, so at most 2 groups per wave
 template <int NBB>
 static hipError_t gemv_norm_rows(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
-  if (M == 1) return gemv_launch<NBB, true, 1, 2, 1>(w, a, M, e, s);
-  if (M == 2) return gemv_launch<NBB, true, 2, 2, 1>(w, a, M, e, s);
-  if (M <= 4) return gemv_launch<NBB, true, 4, 2, 1>(w, a, M, e, s);
-  return gemv_launch<NBB, true, 8, 2, 1>(w, a, M, e, s);
+  if (M == 1) return gemv_launch<NBB, SRC_NORM, 1, 2, 1>(w, a, M, e, s);
+  if (M == 2) return gemv_launch<NBB, SRC_NORM, 2, 2, 1>(w, a, M, e, s);
+  if (M <= 4) return gemv_launch<NBB, SRC_NORM, 4, 2, 1>(w, a, M, e, s);
+  return gemv_launch<NBB, SRC_NORM, 8, 2, 1>(w, a, M, e, s);
+}
+
+// merged attention parts: K <= 2048; (row, part) pairs per thread
+static hipError_t gemv_att(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+  const int pairs = M * a.att_np;
+  if (pairs <= 1) return gemv_launch<1, SRC_ATT, 1, 2, 1>(w, a, M, e, s);
+  if (pairs <= 2) return gemv_launch<1, SRC_ATT, 1, 2, 2>(w, a, M, e, s);
+  if (pairs <= 4) return gemv_launch<1, SRC_ATT, 1, 2, 4>(w, a, M, e, s);
+  if (pairs <= 8) return gemv_launch<1, SRC_ATT, 1, 2, 8>(w, a, M, e, s);
+  return gemv_launch<1, SRC_ATT, 1, 2, 16>(w, a, M, e, s);
 }
 
 template <int GI>
 static hipError_t gemv_a16(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
   const int apt = (M * (w.K / 8) + kGemvThreads - 1) / kGemvThreads;
-  if (apt <= 1) return gemv_launch<1, false, 1, GI, 1>(w, a, M, e, s);
-  if (apt <= 2) return gemv_launch<1, false, 1, GI, 2>(w, a, M, e, s);
-  if (apt <= 4) return gemv_launch<1, false, 1, GI, 4>(w, a, M, e, s);
-  if (apt <= 8) return gemv_launch<1, false, 1, GI, 8>(w, a, M, e, s);
-  return gemv_launch<1, false, 1, GI, 16>(w, a, M, e, s);
+  if (apt <= 1) return gemv_launch<1, SRC_A16, 1, GI, 1>(w, a, M, e, s);
+  if (apt <= 2) return gemv_launch<1, SRC_A16, 1, GI, 2>(w, a, M, e, s);
+  if (apt <= 4) return gemv_launch<1, SRC_A16, 1, GI, 4>(w, a, M, e, s);
+  if (apt <= 8) return gemv_launch<1, SRC_A16, 1, GI, 8>(w, a, M, e, s);
+  return gemv_launch<1, SRC_A16, 1, GI, 16>(w, a, M, e, s);
 }
 
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
-  const bool norm = a.x32 != nullptr;
-  if (!gemv_supported(M, w.K, norm) || (!norm && e.mode == EPI_SWIGLU)) return hipErrorInvalidValue;
-  if (norm) return e.mode == EPI_SWIGLU ? gemv_norm_rows<2>(w, a, M, e, s) : gemv_norm_rows<1>(w, a, M, e, s);
+  if (!gemv_supported(M, w.K, a)) return hipErrorInvalidValue;
+  if (a.x32) return e.mode == EPI_SWIGLU ? gemv_norm_rows<2>(w, a, M, e, s) : gemv_norm_rows<1>(w, a, M, e, s);
+  if (e.mode == EPI_SWIGLU) return hipErrorInvalidValue;
+  if (a.att) return gemv_att(w, a, M, e, s);
   return w.G <= 2 * kGemvWaves ? gemv_a16<2>(w, a, M, e, s) : gemv_a16<8>(w, a, M, e, s);
 }
 

@@ -92,15 +92,16 @@ typedef struct {
   const tl_block* pre;         /* host array of n_pre blocks */
   tl_block loop;               /* the shared loop block */
   const uint16_t* final_norm;  /* fp16 [d_model] */
-  const uint16_t* head;        /* fp16 [vocab][d_model], used in place */
+  const uint16_t* head;        /* fp16 [vocab][d_model], repacked by tl_create */
 } tl_weights;
 
 typedef struct tl_ctx tl_ctx;
 
 /* ---- sizes ------------------------------------------------------------- */
 
-/* Repacked block weights, norms and RoPE table. Independent of max_loops:
- * the loop block is stored once however many times it runs. */
+/* Repacked block weights, the head in MFMA tile order and the RoPE table.
+ * Independent of max_loops: the loop block is stored once however many
+ * times it runs. */
 size_t tl_weights_ws_bytes(const tl_config* cfg);
 /* K and V of one lane for one effective layer:
  *   FP16: 2 * max_seq * n_heads * head_dim * 2
@@ -116,12 +117,15 @@ size_t tl_act_ws_bytes(const tl_config* cfg);
 
 /* Validates cfg and pointers, repacks every INT4 linear of the pre-blocks and
  * the loop block into d_weights_ws (so the canonical buffers may be freed
- * afterwards) and clears the per-lane state. embed, head and the norm gains
- * are read in place and must outlive the context. d_kv holds the caches of
+ * afterwards), copies the head into MFMA tile order there too, and clears
+ * the per-lane state. embed and the norm gains are read in place and must
+ * outlive the context. d_kv holds the caches of
  * all lanes; d_act_ws the activations. Every lane starts empty with L = 1.
+ * Pointers: embed, head and the norm gains 16-byte aligned; workspaces
+ * 256-byte aligned.
  * Errors: TL_E_INVAL (null/misaligned pointer, head_dim not 64 or 128,
- * d_model != n_heads*head_dim, any dimension not a multiple of 16,
- * group_size != 128), TL_E_RANGE (max_loops outside 1..64, n_lanes outside
+ * d_model != n_heads*head_dim, d_model not a multiple of 32 or above 2048,
+ * ffn_dim not a multiple of 16, group_size != 128), TL_E_RANGE (max_loops outside 1..64, n_lanes outside
  * 1..8, max_seq or max_tokens < 1), TL_E_HIP. */
 tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_ws, void* d_kv,
                     void* d_act_ws, void* stream, tl_ctx** out);

@@ -244,140 +244,147 @@ hipError_t launch_rope_kv(const float* qkv, int S, int M, const RowMap& rm, cons
 
 // ------------------------------------------------------------------ head
 // Final RMSNorm and head projection in one launch, plus per-block argmax
-// candidates. Block b owns vocab rows 64b..64b+63 (4 waves x 16 rows). Its
-// head rows are requested first (they do not depend on the activations), then
-// the block normalises the M <= 8 residual rows into LDS (z = fp16(gamma x /
-// rms)), and each wave walks K in 32-deep MFMA steps. Every block writes its
-// logits and, per row, its (max, lowest index) candidate.
-constexpr int kHeadSteps = 16;  // 32-deep k-steps of head rows in flight per wave
-constexpr int kHeadKpt = 8;     // residual elements per thread (d <= 2048) held in registers
+// candidates. Block b owns vocab rows 16b..16b+15; its 4 waves split the
+// d/32 MFMA k-steps into 4 contiguous quarters, so each wave streams one
+// contiguous run of 1 KiB tiles (the head is stored in tile order: lane l of
+// step s holds row l%16, columns 32s + 8(l/16)..+7). Order of work, so that
+// no wait covers the head stream: the residual rows and gamma are requested
+// first, then the first batch of tiles; the block normalises the M <= MR
+// rows into LDS (z = fp16(gamma x / rms)); then batches of kHeadBatch steps
+// are streamed double-buffered. The quarters are summed in wave order. Head
+// tiles are read non-temporally: streamed once, they should not displace the
+// loop-block weights from the caches. Each block writes its logits and, per
+// row, its (max, lowest index) candidate.
+constexpr int kHeadBatch = 4;  // k-steps per batch and wave (two batches in flight)
+constexpr int kHeadXpt = 8;    // residual elements per thread (d <= 2048)
 
+__device__ __forceinline__ void head_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MR, int PER>
 __global__ __launch_bounds__(256) void head_kernel(const float* __restrict__ x, int M, const uint16_t* __restrict__ gamma,
-                                                   float eps, const uint16_t* __restrict__ head, int V, int d,
+                                                   float eps, const uint8_t* __restrict__ tiles, int V, int d,
                                                    float* __restrict__ logits, RowMap rm, float* __restrict__ cval,
                                                    int* __restrict__ cidx) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int lda = d + 8;
   _Float16* Z = reinterpret_cast<_Float16*>(smem);
-  __shared__ float red[4][8];
-  __shared__ float bval[4][8];
-  __shared__ int bidx[4][8];
+  __shared__ float red[4][MR];
+  __shared__ float4_t qsum[4][64];
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int l16 = ln & 15, lq = ln >> 4;
-  const int nb = blockIdx.x * 4 + wave;
-  const int v = nb * 16 + l16;
-  const bool vrow = v < V;
-  const int nsteps = d / 32;
-  u32x4_t w[kHeadSteps];
-  auto load_w = [&](int s0) {
+  const int nb = blockIdx.x;
+  const int nsteps = d / 32, per = (nsteps + 3) / 4, sb = wave * per;  // per <= PER
+  const u32x4_t* tp = reinterpret_cast<const u32x4_t*>(tiles) + (size_t)nb * nsteps * 64 + ln;
+
+  // ---- residual rows and gamma: this thread's 8 columns k8 .. k8+7
+  const int k8 = kHeadXpt * tid, kc = min(k8, d - 8);
+  float4_t xv[MR][2];
 #pragma unroll
-    for (int j = 0; j < kHeadSteps; ++j) {
-      w[j] = (u32x4_t){0, 0, 0, 0};
-      if (vrow && s0 + j < nsteps)
-        w[j] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(head + (size_t)v * d + (s0 + j) * 32 + 8 * lq));
-    }
+  for (int m = 0; m < MR; ++m) {
+    const float4_t* xp = reinterpret_cast<const float4_t*>(x + (size_t)min(m, M - 1) * d + kc);
+    xv[m][0] = xp[0];
+    xv[m][1] = xp[1];
+  }
+  u32x4_t gr = *reinterpret_cast<const u32x4_t*>(gamma + kc);
+  asm volatile("" ::: "memory");
+
+  // ---- first batch of this wave's quarter
+  constexpr int NB = (PER + kHeadBatch - 1) / kHeadBatch;  // batches per wave
+  u32x4_t wbuf[2][kHeadBatch];
+  auto load_w = [&](u32x4_t (&w)[kHeadBatch], int s0) {
+#pragma unroll
+    for (int j = 0; j < kHeadBatch; ++j)
+      w[j] = __builtin_nontemporal_load(tp + (size_t)min(sb + min(s0 + j, per - 1), nsteps - 1) * 64);
   };
-  load_w(0);
-  // ---- z = fp16(RMSNorm(x)) for the M rows; x and gamma in one round trip
-  if (d <= kHeadKpt * 256) {
-    float xv[8][kHeadKpt], gv[kHeadKpt];
+  load_w(wbuf[0], 0);
+  asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < kHeadKpt; ++i) {
-      const int k = tid + 256 * i;
-      gv[i] = k < d ? h2f(gamma[k]) : 0.f;
+  for (int m = 0; m < MR; ++m) asm volatile("" : "+v"(xv[m][0]), "+v"(xv[m][1]));
+  asm volatile("" : "+v"(gr));
+
+  // ---- z = fp16(RMSNorm(x)) for the M rows
+  const bool kin = k8 < d;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) xv[m][i] = (m < M && k < d) ? x[(size_t)m * d + k] : 0.f;
-    }
+  for (int m = 0; m < MR; ++m) {
+    float a = 0.f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < M) {
-        float a = 0.f;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < kHeadKpt; ++i) a += xv[m][i] * xv[m][i];
-        a = wave_sum(a);
-        if (ln == 0) red[wave][m] = a;
-      }
-    }
-    __syncthreads();
+      for (int c = 0; c < 4; ++c) a = fmaf(xv[m][h][c], xv[m][h][c], a);
+    a = wave_sum(kin ? a : 0.f);
+    if (ln == 0) red[wave][m] = a;
+  }
+  head_lds_barrier();
+  const half8_t gh = __builtin_bit_cast(half8_t, gr);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < M) {
-        const float rinv = 1.0f / sqrtf((red[0][m] + red[1][m] + red[2][m] + red[3][m]) / (float)d + eps);
-#pragma unroll
-        for (int i = 0; i < kHeadKpt; ++i) {
-          const int k = tid + 256 * i;
-          if (k < d) Z[m * lda + k] = (_Float16)((xv[m][i] * rinv) * gv[i]);
-        }
-      }
-    }
-  } else {
-    for (int m = 0; m < M; ++m) {
-      const float* xr = x + (size_t)m * d;
-      float a = 0.f;
-      for (int k = tid; k < d; k += 256) a += xr[k] * xr[k];
-      a = wave_sum(a);
-      if (ln == 0) red[wave][m] = a;
-    }
-    __syncthreads();
-    for (int m = 0; m < M; ++m) {
+  for (int m = 0; m < MR; ++m) {
+    if (m < M && kin) {
       const float rinv = 1.0f / sqrtf((red[0][m] + red[1][m] + red[2][m] + red[3][m]) / (float)d + eps);
-      const float* xr = x + (size_t)m * d;
-      for (int k = tid; k < d; k += 256) Z[m * lda + k] = (_Float16)((xr[k] * rinv) * h2f(gamma[k]));
+      half8_t zv;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) zv[c] = (_Float16)((xv[m][c >> 2][c & 3] * rinv) * (float)gh[c]);
+      *reinterpret_cast<half8_t*>(Z + m * lda + k8) = zv;
     }
   }
-  __syncthreads();
+  head_lds_barrier();
+
+  // ---- stream the quarter, double-buffered; steps past it meet zero activations
   const bool arow = l16 < M;
   const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsteps; s0 += kHeadSteps) {
-    if (s0) load_w(s0);
+  auto consume = [&](const u32x4_t (&w)[kHeadBatch], int s0) {
 #pragma unroll
-    for (int j = 0; j < kHeadSteps; ++j) {
-      if (s0 + j < nsteps) {
-        const half8_t af = arow ? *reinterpret_cast<const half8_t*>(Z + l16 * lda + (s0 + j) * 32 + 8 * lq) : hz;
-        acc = mfma16(af, __builtin_bit_cast(half8_t, w[j]), acc);
-      }
+    for (int j = 0; j < kHeadBatch; ++j) {
+      const int st = sb + s0 + j;
+      const bool ok = arow && s0 + j < per && st < nsteps;
+      const half8_t z8 = *reinterpret_cast<const half8_t*>(Z + l16 * lda + min(st, nsteps - 1) * 32 + 8 * lq);
+      acc = mfma16(ok ? z8 : hz, __builtin_bit_cast(half8_t, w[j]), acc);
     }
+  };
+  // straight-line pipeline: batch b+1 is requested before batch b is consumed
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b + 1 < NB) load_w(wbuf[(b + 1) & 1], (b + 1) * kHeadBatch);
+    asm volatile("" ::: "memory");
+    consume(wbuf[b & 1], b * kHeadBatch);
   }
-  // ---- logits and per-row candidates; lane holds row m = 4lq + r, vocab v
+
+  // ---- quarters summed in wave order; logits and per-row candidates
+  qsum[wave][ln] = acc;
+  head_lds_barrier();
+  if (wave == 0) {
+    const float4_t t = ((qsum[0][ln] + qsum[1][ln]) + qsum[2][ln]) + qsum[3][ln];
+    const int v = nb * 16 + l16;
+    const int nblk = gridDim.x;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * lq + r;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    if (m < M && vrow) {
-      logits[(size_t)out_row(rm, m) * V + v] = acc[r];
-      bv = acc[r];
-      bi = v;
-    }
-    // max over the 16 lanes of this row group, ties to the lowest index
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lq + r;  // lane holds row m = 4lq + r, vocab v
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      if (m < M && v < V) {
+        logits[(size_t)out_row(rm, m) * V + v] = t[r];
+        bv = t[r];
+        bi = v;
+      }
+      // max over the 16 vocab rows, ties to the lowest index
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+      for (int o = 8; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (l16 == 0 && m < M) {
+        cval[(size_t)m * nblk + nb] = bv;
+        cidx[(size_t)m * nblk + nb] = bi;
       }
     }
-    if (l16 == 0 && m < 8) {
-      bval[wave][m] = bv;
-      bidx[wave][m] = bi;
-    }
-  }
-  __syncthreads();
-  const int nblk = gridDim.x;
-  if (tid < M) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int wv = 0; wv < 4; ++wv)
-      if (bval[wv][tid] > bv || (bval[wv][tid] == bv && bidx[wv][tid] < bi)) {
-        bv = bval[wv][tid];
-        bi = bidx[wv][tid];
-      }
-    cval[(size_t)tid * nblk + blockIdx.x] = bv;
-    cidx[(size_t)tid * nblk + blockIdx.x] = bi;
   }
 }
 
@@ -422,22 +429,42 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ c
   }
 }
 
-size_t head_scratch_bytes(int max_rows, int V) { return (size_t)max_rows * ((V + 63) / 64) * 8; }
+size_t head_scratch_bytes(int max_rows, int V) { return (size_t)max_rows * ((V + 15) / 16) * 8; }
 
-hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
-                       float* logits, const RowMap& rm, void* scratch, hipStream_t s) {
-  if (M < 1 || M > 8 || d % 32) return hipErrorInvalidValue;
+template <int PER>
+static void head_rows(dim3 g, size_t lds, hipStream_t s, const float* x, int M, const uint16_t* gamma, float eps,
+                      const uint8_t* t, int V, int d, float* logits, const RowMap& rm, float* cval, int* cidx) {
+  if (M == 1)
+    launch(head_kernel<1, PER>, g, dim3(256), lds, s, x, M, gamma, eps, t, V, d, logits, rm, cval, cidx);
+  else if (M == 2)
+    launch(head_kernel<2, PER>, g, dim3(256), lds, s, x, M, gamma, eps, t, V, d, logits, rm, cval, cidx);
+  else if (M <= 4)
+    launch(head_kernel<4, PER>, g, dim3(256), lds, s, x, M, gamma, eps, t, V, d, logits, rm, cval, cidx);
+  else
+    launch(head_kernel<8, PER>, g, dim3(256), lds, s, x, M, gamma, eps, t, V, d, logits, rm, cval, cidx);
+}
+
+hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint8_t* head_tiles, int V,
+                       int d, float* logits, const RowMap& rm, void* scratch, hipStream_t s) {
+  if (M < 1 || M > 8 || d % 32 || d > 256 * kHeadXpt) return hipErrorInvalidValue;
   const size_t lds = (size_t)M * (d + 8) * 2;
-  const int nblk = (V + 63) / 64;
+  const int nblk = (V + 15) / 16;
   float* cval = static_cast<float*>(scratch);
   int* cidx = reinterpret_cast<int*>(cval + (size_t)M * nblk);
-  launch(head_kernel, dim3(nblk), dim3(256), lds, s, x, M, gamma, eps, head, V, d, logits, rm, cval, cidx);
+  const int per = (d / 32 + 3) / 4;  // k-steps per wave
+  const dim3 g(nblk);
+  if (per <= 4)
+    head_rows<4>(g, lds, s, x, M, gamma, eps, head_tiles, V, d, logits, rm, cval, cidx);
+  else if (per <= 8)
+    head_rows<8>(g, lds, s, x, M, gamma, eps, head_tiles, V, d, logits, rm, cval, cidx);
+  else
+    head_rows<16>(g, lds, s, x, M, gamma, eps, head_tiles, V, d, logits, rm, cval, cidx);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s) {
   if (M < 1 || M > 8) return hipErrorInvalidValue;
-  const int nblk = (V + 63) / 64;
+  const int nblk = (V + 15) / 16;
   const float* cval = static_cast<const float*>(scratch);
   const int* cidx = reinterpret_cast<const int*>(cval + (size_t)M * nblk);
   launch(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next);

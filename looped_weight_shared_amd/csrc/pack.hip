@@ -93,4 +93,30 @@ hipError_t launch_unpack(const Packed& p, int8_t* q, uint16_t* scales, hipStream
   return hipGetLastError();
 }
 
+// FP16 head [V][d] -> tiles [ceil(V/16)][d/32][64 lanes][16 B]: lane l of
+// tile (nb, s) holds row 16nb + l%16, columns 32s + 8(l/16)..+7 -- the B
+// operand of one v_mfma_f32_16x16x32_f16 step, read by a wave as one
+// contiguous 1 KiB. Rows past V are zero.
+__global__ void pack_head_kernel(const uint16_t* __restrict__ head, int V, int d, uint8_t* __restrict__ dst,
+                                 size_t n_slots) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_slots) return;
+  const int nsteps = d / 32;
+  const int l = (int)(i & 63);
+  const size_t t = i >> 6;
+  const int st = (int)(t % nsteps);
+  const size_t nb = t / nsteps;
+  const size_t row = nb * 16 + (l & 15);
+  u32x4_t v = {0, 0, 0, 0};
+  if (row < (size_t)V) v = *reinterpret_cast<const u32x4_t*>(head + row * d + st * 32 + 8 * (l >> 4));
+  *reinterpret_cast<u32x4_t*>(dst + i * 16) = v;
+}
+
+hipError_t launch_pack_head(const uint16_t* head, int V, int d, uint8_t* dst, hipStream_t s) {
+  if (V < 1 || d < 32 || d % 32) return hipErrorInvalidValue;
+  const size_t n_slots = head_packed_bytes(V, d) / 16;
+  launch(pack_head_kernel, dim3((unsigned)((n_slots + 255) / 256)), dim3(256), 0, s, head, V, d, dst, n_slots);
+  return hipGetLastError();
+}
+
 }  // namespace tl

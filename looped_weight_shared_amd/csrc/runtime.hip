@@ -52,6 +52,7 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->head_dim != 64 && c->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
   if (c->n_heads < 1 || c->d_model != c->n_heads * c->head_dim) return *why = "d_model != n_heads*head_dim", false;
   if (c->d_model % 32 || c->ffn_dim < 16 || c->ffn_dim % 16) return *why = "d_model % 32 or ffn_dim % 16 != 0", false;
+  if (c->d_model > 2048) return *why = "d_model must be <= 2048 (one residual row per 256 threads in registers)", false;
   if (c->group_size != 128) return *why = "group_size must be 128", false;
   if (c->vocab < 1 || c->n_pre < 0) return *why = "vocab < 1 or n_pre < 0", false;
   if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8) return *why = "bad kv_dtype", false;
@@ -115,7 +116,7 @@ struct tl_ctx {
   tl_config cfg;
   std::vector<BlockW> blocks;  // n_pre pre-blocks, then the loop block
   const uint16_t* embed;
-  const uint16_t* head;
+  const uint8_t* head;  // head repacked in MFMA tile order
   const uint16_t* final_norm;
   float* rope;
   tl::KvGeom kv;
@@ -261,7 +262,8 @@ size_t tl_weights_ws_bytes(const tl_config* cfg) {
   tl_status st;
   std::string why;
   if (!check_cfg(cfg, &st, &why)) return 0;
-  return (size_t)(cfg->n_pre + 1) * block_bytes(cfg) + rope_bytes(cfg);
+  return (size_t)(cfg->n_pre + 1) * block_bytes(cfg) + al256(tl::head_packed_bytes(cfg->vocab, cfg->d_model)) +
+         rope_bytes(cfg);
 }
 
 size_t tl_kv_layer_bytes(const tl_config* cfg) {
@@ -297,12 +299,13 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   if (!d_weights_ws || !d_kv || !d_act_ws) return fail(TL_E_INVAL, "workspace pointer is NULL");
   if (!aligned(d_weights_ws, 256) || !aligned(d_kv, 256) || !aligned(d_act_ws, 256))
     return fail(TL_E_INVAL, "workspaces must be 256-byte aligned");
-  if (!aligned(w->embed, 16) || !aligned(w->head, 16)) return fail(TL_E_INVAL, "embed/head must be 16-byte aligned");
+  if (!aligned(w->embed, 16) || !aligned(w->head, 16) || !aligned(w->final_norm, 16))
+    return fail(TL_E_INVAL, "embed/head/final_norm must be 16-byte aligned");
   auto block_ok = [](const tl_block& b) {
     const tl_qlinear* ls[7] = {&b.wq, &b.wk, &b.wv, &b.wo, &b.w_gate, &b.w_up, &b.w_down};
     for (auto* l : ls)
       if (!l->qweight || !l->scales || !aligned(l->qweight, 4) || !aligned(l->scales, 2)) return false;
-    return b.attn_norm && b.mlp_norm;
+    return b.attn_norm && b.mlp_norm && aligned(b.attn_norm, 16) && aligned(b.mlp_norm, 16);
   };
   for (int i = 0; i < cfg->n_pre; ++i)
     if (!block_ok(w->pre[i])) return fail(TL_E_INVAL, "pre-block weight pointer missing or misaligned");
@@ -312,7 +315,7 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   tl_ctx* c = new tl_ctx();
   c->cfg = *cfg;
   c->embed = w->embed;
-  c->head = w->head;
+
   c->final_norm = w->final_norm;
   const int d = cfg->d_model, f = cfg->ffn_dim;
   uint8_t* p = static_cast<uint8_t*>(d_weights_ws);
@@ -352,6 +355,16 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
       return fail(TL_E_HIP, std::string("weight repack: ") + hipGetErrorString(e));
     }
     c->blocks.push_back(B);
+  }
+  // the head in MFMA tile order (streamed once per decode step)
+  {
+    c->head = p;
+    hipError_t e = tl::launch_pack_head(w->head, cfg->vocab, d, p, s);
+    p += al256(tl::head_packed_bytes(cfg->vocab, d));
+    if (e != hipSuccess) {
+      delete c;
+      return fail(TL_E_HIP, std::string("head repack: ") + hipGetErrorString(e));
+    }
   }
   // RoPE table: cos then sin of pos * base^(-2i/hd), computed in double.
   c->rope = reinterpret_cast<float*>(p);

@@ -41,6 +41,9 @@ struct Packed {
 inline size_t packed_tile_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 1024; }
 inline size_t packed_scale_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 32; }
 inline size_t packed_bytes(int N, int K) { return packed_tile_bytes(N, K) + packed_scale_bytes(N, K); }
+// FP16 head in MFMA tile order (see launch_pack_head).
+inline size_t head_packed_bytes(int V, int d) { return (size_t)((V + 15) / 16) * (d / 32) * 1024; }
+hipError_t launch_pack_head(const uint16_t* head, int V, int d, uint8_t* dst, hipStream_t s);
 
 // Repack a canonical [N][K/8] / [N][ceil(K/128)] linear into the packed
 // buffer of a (possibly fused) destination: source n-block b goes to
@@ -144,13 +147,13 @@ hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const f
 
 hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d,
                         float* x, hipStream_t s);
-// Final RMSNorm of the residual rows x [M][d] (M <= 8), logits against the
-// fp16 head [V][d] written at logits[out_row(m) * V] (out_row = the row's lane
-// in decode, m in prefill) and, if next != null, the greedy argmax of each row
-// into next[out_row(m)] (second small launch). scratch: head_scratch_bytes.
+// Final RMSNorm of the residual rows x [M][d] (M <= 8, d <= 2048), logits
+// against the head in tile order (launch_pack_head) written at
+// logits[out_row(m) * V] (out_row = the row's lane in decode, m in prefill),
+// and per 16-row block argmax candidates in scratch (head_scratch_bytes).
 size_t head_scratch_bytes(int max_rows, int V);
-hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint16_t* head, int V, int d,
-                       float* logits, const RowMap& rm, void* scratch, hipStream_t s);
+hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint8_t* head_tiles, int V,
+                       int d, float* logits, const RowMap& rm, void* scratch, hipStream_t s);
 // next[out_row(m)] = argmax of row m's logits, from the head's per-block
 // candidates in `scratch` (ties: lowest index).
 hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s);

@@ -25,19 +25,31 @@ constexpr int kTileBytes = 1024;
 constexpr int kGroup = 128;
 
 // 8 signed 4-bit values of one packed word -> 8 exact fp16 integers in
-// column order. OR-ing u into the mantissa of 1024.0h gives 1024 + u exactly;
-// subtracting 1032 gives q = u - 8 exactly (integers below 2048 are exact).
+// column order. The nibble pairs (0,4) and (2,6) of the word (the latter after
+// a shift by 8) sit at bits 0 and 16, where OR-ing them into the mantissa of
+// 1024.0h gives 1024 + u exactly; the pairs (1,5) and (3,7) sit at bits 4 and
+// 20, which gives 1024 + 16u exactly. One packed subtract of 1032, or one
+// packed fma by 1/16 minus 72, then gives q = u - 8 exactly (every
+// intermediate is an integer below 2048 or a power-of-two multiple of one).
+// The mask-and-or is one v_and_or_b32 (its constants come from registers:
+// this encoding cannot carry literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+}
 __device__ __forceinline__ half8_t dequant_word(uint32_t w) {
-  const uint32_t magic = 0x64006400u, mask = 0x000F000Fu;
-  uint32_t t0 = (w & mask) | magic;
-  uint32_t t1 = ((w >> 4) & mask) | magic;
-  uint32_t t2 = ((w >> 8) & mask) | magic;
-  uint32_t t3 = ((w >> 12) & mask) | magic;
+  const uint32_t magic = 0x64006400u, lo = 0x000F000Fu, hi = 0x00F000F0u;
+  const uint32_t w8 = w >> 8;
+  const half2_t t0 = __builtin_bit_cast(half2_t, and_or(w, lo, magic));   // 1024 + u, nibbles 0, 4
+  const half2_t t1 = __builtin_bit_cast(half2_t, and_or(w, hi, magic));   // 1024 + 16u, nibbles 1, 5
+  const half2_t t2 = __builtin_bit_cast(half2_t, and_or(w8, lo, magic));  // nibbles 2, 6
+  const half2_t t3 = __builtin_bit_cast(half2_t, and_or(w8, hi, magic));  // nibbles 3, 7
   const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  half2_t a0 = __builtin_bit_cast(half2_t, t0) + bias;
-  half2_t a1 = __builtin_bit_cast(half2_t, t1) + bias;
-  half2_t a2 = __builtin_bit_cast(half2_t, t2) + bias;
-  half2_t a3 = __builtin_bit_cast(half2_t, t3) + bias;
+  const half2_t k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t b72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const half2_t a0 = t0 + bias, a2 = t2 + bias;
+  const half2_t a1 = __builtin_elementwise_fma(t1, k16, b72), a3 = __builtin_elementwise_fma(t3, k16, b72);
   half8_t r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
   return r;
 }

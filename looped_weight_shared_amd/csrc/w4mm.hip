@@ -336,118 +336,36 @@ hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, h
 }
 
 // ---------------------------------------------------------------- GEMM
-// Every operand reaches LDS by global_load_lds (no staging registers), into a
-// ring of NST one-group stages. Stage layout (group g of the block's K range):
-//   A  : MB*4 blocks of 1 KiB; block (mb, s) holds at byte 16*l row
-//        m0 + 16mb + l%16, columns 128g + 32s + 8(l/16)..+7 -- exactly lane
-//        l's MFMA A operand, so each is one conflict-free ds_read_b128;
-//   B  : per wave, NBW weight tiles of 1 KiB in the packed layout (lane l's
-//        16 bytes are its four k-steps' B operands);
-//   Sc : per wave, NBW x 16 fp16 group scales.
-// The loop over groups is compact (not unrolled): issue group g+NST-1 into
-// the slot freed by group g-1, wait (compile-time vmcnt per look-ahead) until
-// group g's copies have landed, barrier, compute group g, barrier. Rows >= M
-// and columns >= K read in-bounds elements: those rows are never stored and
-// those columns meet zero weights.
-template <int MB, int NBW>
-struct GemmCfg {
-  static constexpr int kA = MB * 4 * 1024;
-  static constexpr int kB = 4 * NBW * 1024;
-  static constexpr int kSc = 4 * NBW * 32;
-  static constexpr int kSlot = kA + kB + kSc;
-  static constexpr int NST = (144 * 1024) / kSlot > 6 ? 6 : (144 * 1024) / kSlot;  // ring depth
-  static constexpr int OPS = MB + 2 * NBW;  // copies one wave issues per group
-};
-
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void plain_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-// wait until at most ahead*OPS copies of this wave are in flight, then barrier
-template <int OPS, int NST>
-__device__ __forceinline__ void stage_wait(int ahead) {
-  static_assert(NST <= 6, "ring depth");
-  switch (ahead) {
-    case 0: wait_vm_barrier<0>(); break;
-    case 1: wait_vm_barrier<1 * OPS>(); break;
-    case 2: wait_vm_barrier<(NST > 2 ? 2 : 0) * OPS>(); break;
-    case 3: wait_vm_barrier<(NST > 3 ? 3 : 0) * OPS>(); break;
-    case 4: wait_vm_barrier<(NST > 4 ? 4 : 0) * OPS>(); break;
-    default: wait_vm_barrier<(NST > 5 ? 5 : 0) * OPS>(); break;
-  }
-}
-
-// LDS reads of one wave written as asm that also waits for them: plain C++
-// loads (or a memory clobber) would make the compiler wait for every LDS copy
-// in flight, including the later stages'. Volatile asm keeps its order against
-// the stage barriers, which are volatile too.
-template <int MB>
-__device__ __forceinline__ void lds_frags(uint32_t addr, half8_t* f);
-template <>
-__device__ __forceinline__ void lds_frags<1>(uint32_t a, half8_t* f) {
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f[0]) : "v"(a));
-}
-template <>
-__device__ __forceinline__ void lds_frags<2>(uint32_t a, half8_t* f) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(f[0]), "=v"(f[1]) : "v"(a));
-}
-template <>
-__device__ __forceinline__ void lds_frags<4>(uint32_t a, half8_t* f) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\t"
-      "ds_read_b128 %2, %4 offset:8192\n\tds_read_b128 %3, %4 offset:12288\n\ts_waitcnt lgkmcnt(0)"
-      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]) : "v"(a));
-}
-template <>
-__device__ __forceinline__ void lds_frags<8>(uint32_t a, half8_t* f) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:4096\n\t"
-      "ds_read_b128 %2, %8 offset:8192\n\tds_read_b128 %3, %8 offset:12288\n\t"
-      "ds_read_b128 %4, %8 offset:16384\n\tds_read_b128 %5, %8 offset:20480\n\t"
-      "ds_read_b128 %6, %8 offset:24576\n\tds_read_b128 %7, %8 offset:28672\n\ts_waitcnt lgkmcnt(0)"
-      : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]), "=v"(f[4]), "=v"(f[5]), "=v"(f[6]), "=v"(f[7])
-      : "v"(a));
-}
-// NBW (1 or 2) weight tiles (16 B per lane, 1 KiB apart) and their scales
-// (2 bytes per lane at l16, 32 bytes apart).
-template <int NBW>
-__device__ __forceinline__ void lds_tiles(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s);
-template <>
-__device__ __forceinline__ void lds_tiles<1>(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(w[0]), "=v"(s[0]) : "v"(wa), "v"(sa));
-}
-template <>
-__device__ __forceinline__ void lds_tiles<2>(uint32_t wa, uint32_t sa, u32x4_t* w, uint32_t* s) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-      "ds_read_u16 %2, %5\n\tds_read_u16 %3, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
-      : "=v"(w[0]), "=v"(w[1]), "=v"(s[0]), "=v"(s[1]) : "v"(wa), "v"(sa));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
-}
-__device__ __forceinline__ void lds_copy16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
+// Prefill-shaped products (any M). A block of 4 waves computes a tile of
+// 16*MB rows x 64*NBW columns: the waves share the activation rows (staged
+// in LDS) and each owns NBW 16-column n-blocks, whose weight tiles and
+// scales it streams straight into registers. Every 128-column group's
+// activations (16 bytes per thread and m-block, in MFMA fragment order:
+// block (mb, s) of a stage holds at byte 16*l row m0 + 16mb + l%16, columns
+// 128g + 32s + 8(l/16)..+7) and weights are requested kGemmAhead groups before
+// use into a register ring. Per group g:
+//   - the activations of group g+1 are written to the other LDS stage;
+//   - group g is computed from LDS and the weight registers of group g
+//     (dequant in registers, v_mfma_f32_16x16x32_f16 into a per-group tile,
+//     scaled once per group in fp32);
+//   - group g + kGemmAhead is requested into the ring slot just freed; one
+//     barrier (LDS only).
+// At these sizes the loop is latency-bound, so the depth of the ring (not
+// the tile shape) sets the speed. Plain vector loads (LDS-DMA measured about
+// half the per-CU throughput); addresses clamped at the end of the K range
+// and out-of-range groups meeting zero weights, so the unrolled loop body is
+// straight-line code and the compiler's waits stay exact. Rows >= M and
+// columns >= K read in-bounds elements: those rows are never stored and those
+// columns meet zero weights. When the plan splits K over S blocks, each
+// writes an fp32 partial tile and the consumer sums the S partials in order.
+constexpr int kGemmAhead = 2;  // groups of loads in flight per wave (the loop is unrolled by it)
 
 template <int MB, int NBW>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int N, int K, int G,
                                                       const uint16_t* __restrict__ A, int M, Epi e, GemmPlan pl) {
-  using C = GemmCfg<MB, NBW>;
-  constexpr int NST = C::NST;
-  __shared__ __align__(16) uint8_t ring[NST * C::kSlot];
+  constexpr int kA = MB * 4 * 1024;  // one group's activation stage
+  __shared__ __align__(16) uint8_t As[2][kA];
   const int L = blockIdx.x;
   const int U = pl.gy * pl.S;
   const int xcd = L & 7, r = L >> 3;
@@ -463,27 +381,40 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
   const int nbw0 = (cb * 4 + wave) * NBW;
   const int m0 = my * 16 * MB;
 
-  // per-lane sources: A rows of the m-blocks this wave copies (wave w copies
-  // k-step s = w of every m-block), its weight tiles and scales
+  // this thread copies k-step s = wave of every m-block of a stage
   const uint16_t* arow[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) arow[i] = A + (size_t)min(m0 + i * 16 + l16, M - 1) * K;
   const int acol = 32 * wave + 8 * lq;
-  int nbc[NBW];
+  const u32x4_t* btile[NBW];
+  const uint16_t* bscale[NBW];
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) nbc[j] = min(nbw0 + j, NB - 1);
+  for (int j = 0; j < NBW; ++j) {
+    const size_t nb = (size_t)min(nbw0 + j, NB - 1) * G;
+    btile[j] = reinterpret_cast<const u32x4_t*>(tiles + nb * kTileBytes) + lane;
+    bscale[j] = scales + nb * 16 + l16;
+  }
 
-  auto issue = [&](int g) {
-    uint8_t* slot = ring + (g % NST) * C::kSlot;
-    const int col = min(g * 128 + acol, K - 8);
+  constexpr int D = kGemmAhead;
+  u32x4_t ar[D][MB];
+  u32x4_t br[D][NBW];
+  uint32_t bs[D][NBW];  // raw fp16 bits
+  auto load_a = [&](u32x4_t (&ra)[MB], int g) {
+    const int col = min(min(g, kg1 - 1) * 128 + acol, K - 8);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) lds_copy16(arow[i] + col, slot + (i * 4 + wave) * 1024);
+    for (int i = 0; i < MB; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + col);
+  };
+  auto load_b = [&](u32x4_t (&rb)[NBW], uint32_t (&rs)[NBW], int g) {
+    const int gc = min(g, kg1 - 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const size_t tile = (size_t)nbc[j] * G + g;
-      lds_copy16(tiles + tile * kTileBytes + lane * 16, slot + C::kA + (wave * NBW + j) * 1024);
-      if (lane < 2) lds_copy16(scales + tile * 16 + lane * 8, slot + C::kA + C::kB + (wave * NBW + j) * 32);
+      rb[j] = btile[j][(size_t)gc * 64];
+      rs[j] = bscale[j][(size_t)gc * 16];
     }
+  };
+  auto store_a = [&](const u32x4_t (&ra)[MB], int buf) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) *reinterpret_cast<u32x4_t*>(&As[buf][(i * 4 + wave) * 1024 + lane * 16]) = ra[i];
   };
 
   float4_t acc[MB][NBW];
@@ -492,17 +423,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int i = 0; i < NST - 1; ++i)
-    if (kg0 + i < kg1) issue(kg0 + i);
-#pragma unroll 1
-  for (int g = kg0; g < kg1; ++g) {
-    if (g + NST - 1 < kg1) issue(g + NST - 1);
-    stage_wait<C::OPS, NST>(min(NST - 1, kg1 - 1 - g));
-    const uint8_t* slot = ring + (g % NST) * C::kSlot;
-    u32x4_t bw[NBW];
-    uint32_t bsr[NBW];
-    lds_tiles<NBW>(lds_addr(slot + C::kA + wave * NBW * 1024 + lane * 16),
-                   lds_addr(slot + C::kA + C::kB + wave * NBW * 32 + l16 * 2), bw, bsr);
+  auto compute = [&](int buf, const u32x4_t (&bw)[NBW], const uint32_t (&bsc)[NBW], bool valid) {
     float4_t t[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -510,25 +431,45 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
       for (int j = 0; j < NBW; ++j) t[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8_t af[MB];
-      lds_frags<MB>(lds_addr(slot + s * 1024 + lane * 16), af);
-      half8_t bf[NBW];
+      half8_t af[MB], bf[NBW];
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) bf[j] = dequant_word(bw[j][s]);
+      for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const half8_t*>(&As[buf][(i * 4 + s) * 1024 + lane * 16]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int j = 0; j < NBW; ++j) bf[j] = dequant_word(valid ? bw[j][s] : 0x88888888u);  // 0x8: q = 0
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) t[mb][j] = mfma16(af[mb], bf[j], t[mb][j]);
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) t[i][j] = mfma16(af[i], bf[j], t[i][j]);
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const float sc = h2f((uint16_t)bsr[j]);
+      const float sc = h2f((uint16_t)bsc[j]);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) acc[i][j][rr] = fmaf(t[i][j][rr], sc, acc[i][j][rr]);
     }
-    plain_barrier();  // every wave is done with this slot before it is refilled
+  };
+
+  // prologue: groups kg0 .. kg0+D-1 requested; group kg0's activations staged
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    load_a(ar[k], kg0 + k);
+    load_b(br[k], bs[k], kg0 + k);
+  }
+  store_a(ar[0], 0);
+  lds_barrier();
+  // D groups per trip (D even), so every ring slot and LDS stage is static
+#pragma unroll 1
+  for (int g = kg0; g < kg1; g += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load_a(ar[k], g + k + D);                          // group g+k+D -> slot k (staged one step ago)
+      store_a(ar[(k + 1) % D], (k + 1) & 1);            // group g+k+1 -> LDS
+      compute(k & 1, br[k], bs[k], g + k < kg1);         // group g+k
+      load_b(br[k], bs[k], g + k + D);
+      lds_barrier();
+    }
   }
 
   // ---- split-K: publish this split's partial tile; the kernel that consumes
@@ -584,25 +525,27 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
   }
 }
 
+// Tile shape and K split. Sweeping every (rows, columns, split) on the
+// 407M shapes at M = 128 and 1024 put the best tile at 32 rows x 128
+// columns (2 x 2 MFMA tiles per wave) almost everywhere, the loop being
+// bound by latency and VALU rather than bytes: more blocks in flight beat
+// bigger tiles. Narrower columns only when the grid would stay below 256
+// blocks; a K split only until there are 384 blocks (partials cost the
+// consumer a read).
 GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu) {
-  GemmPlan p{};
   const int NB = N / 16, G = (K + 127) / 128;
+  GemmPlan p{};
+  p.mb = M <= 16 ? 1 : 2;
+  p.gy = (M + 16 * p.mb - 1) / (16 * p.mb);
   p.nbw = 2;
-  p.mb = M > 64 ? 8 : (M > 32 ? 4 : (M > 16 ? 2 : 1));
   p.gx = (NB + 4 * p.nbw - 1) / (4 * p.nbw);
-  auto gy = [&](int mb) { return (M + 16 * mb - 1) / (16 * mb); };
-  int S = 1;
-  if (swiglu) {
-    while (p.mb > 1 && p.gx * gy(p.mb) < 160) p.mb >>= 1;
-  } else {
-    const int tiles = p.gx * gy(p.mb);
-    while (S < kMaxSplitK && tiles * (S + 1) <= 256 && (G + S) / (S + 1) >= 1) {
-      const int gps_next = (G + S) / (S + 1);
-      if (gps_next < 1) break;
-      ++S;
-    }
+  if (!swiglu && p.gx * p.gy < 256) {
+    p.nbw = 1;
+    p.gx = (NB + 3) / 4;
   }
-  p.gy = gy(p.mb);
+  int S = 1;
+  if (!swiglu)
+    while (S < kMaxSplitK && p.gx * p.gy * S < 384 && G / (2 * S) >= 4) S *= 2;
   p.gps = (G + S - 1) / S;
   p.S = (G + p.gps - 1) / p.gps;
   p.blocks = ((p.gx + 7) / 8) * 8 * p.gy * p.S;

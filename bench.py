@@ -104,11 +104,12 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
     kf, kw = copy_bytes / cf, copy_bytes / cw
     d, f = 2048, 5632
     kernels = {
-        # dominant prefill kernel: gate/up GEMM at M=128 (the only <4, 2> instance of the bench)
-        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<4, 2>" in n,
+        # dominant prefill kernel: the gate/up GEMM at M=128, 32x128 tiles: 88 column blocks x 4
+        # row tiles = 352 blocks of 256 threads (the 256-token prompt's instance has 704)
+        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2>" in n and g == 352 * 256,
                          tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
-        # decode gate/up GEMV (the only <8, 2> GEMV instance)
-        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<8, 2>" in n,
+        # decode gate/up GEMV: the only two-n-block GEMV (fused RMSNorm, one row)
+        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1>" in n,
                          tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")

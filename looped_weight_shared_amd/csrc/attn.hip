@@ -46,27 +46,28 @@ __device__ __forceinline__ CachePtrs cache_ptrs(const KvGeom& kv, int lane, int 
   return c;
 }
 
-// 8 cache values of one row as fp16 (INT8 codes are exact in fp16).
-__device__ __forceinline__ u32x4_t load8_as_f16(const uint8_t* row, int d0, int int8) {
-  if (!int8) return *reinterpret_cast<const u32x4_t*>(row + d0 * 2);
-  const uint2 c = *reinterpret_cast<const uint2*>(row + d0);
-  half8_t h;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    h[j] = (_Float16)(float)(int8_t)((c.x >> (8 * j)) & 0xFF);
-    h[4 + j] = (_Float16)(float)(int8_t)((c.y >> (8 * j)) & 0xFF);
-  }
-  return __builtin_bit_cast(u32x4_t, h);
-}
 
 // ------------------------------------------------------------------ prefill
-template <int HD>
+__device__ __forceinline__ void attn_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// K/V tile t (keys 64t .. 64t+63) is requested into registers while tile t-1
+// is computed (raw: fp16 rows, or INT8 codes and scales, converted when
+// written to LDS so the request never waits), then written to LDS: K
+// row-major, V transposed. The block barriers wait on LDS only, so the next
+// tile's requests stay in flight across them.
+template <int HD, bool I8>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q, int M, int lane_id,
                                                            int p0, KvGeom kv, int layer, uint16_t* __restrict__ o) {
   constexpr int KS = HD / 32;     // k-steps of S = Q K^T
   constexpr int DB = HD / 16;     // 16-wide d blocks of O
   constexpr int LK = HD + 8;      // LDS row stride of the K tile (halves)
   constexpr int LV = 64 + 8;      // LDS row stride of the transposed V tile
+  constexpr int CPT = 64 * HD / 8 / 256;  // 8-element chunks of K (and of V) per thread and tile
+  using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
   __shared__ __align__(16) _Float16 Ks[64 * LK];
   __shared__ __align__(16) _Float16 Vt[HD * LV];
   __shared__ __align__(16) _Float16 Ps[4][2][16 * LV];  // P as fp16 high and low parts
@@ -80,16 +81,72 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   const int kend = p0 + min(q0 + 64, M);  // keys [0, kend) can be visible to this block
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const float scale = 1.0f / sqrtf((float)HD);
+  const int nkt = (kend + 63) / 64;
 
+  Raw kreg[CPT], vreg[CPT];
+  uint32_t kscr = 0, vscr = 0;  // raw fp16 scales (INT8), threads < 64
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
+      const size_t roff = (size_t)min(kt * 64 + kr, kend - 1) * HD * (I8 ? 1 : 2) + d0 * (I8 ? 1 : 2);
+      kreg[i] = *reinterpret_cast<const Raw*>(cp.k + roff);
+      vreg[i] = *reinterpret_cast<const Raw*>(cp.v + roff);
+    }
+    if constexpr (I8) {
+      const int key = min(kt * 64 + (tid & 63), kend - 1);
+      kscr = cp.ks[key];
+      vscr = cp.vs[key];
+    }
+  };
+  auto to_f16 = [&](const Raw& r) -> half8_t {
+    if constexpr (I8) {
+      half8_t hv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hv[j] = (_Float16)(float)(int8_t)((r.x >> (8 * j)) & 0xFF);
+        hv[4 + j] = (_Float16)(float)(int8_t)((r.y >> (8 * j)) & 0xFF);
+      }
+      return hv;
+    } else {
+      return __builtin_bit_cast(half8_t, r);
+    }
+  };
+  auto store_tile = [&](int kt) {
+    const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
+      const bool ok = kt * 64 + kr < kend;
+      *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
+      const half8_t vh = ok ? to_f16(vreg[i]) : hz;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + kr] = vh[j];
+    }
+    if (tid < 64) {
+      const bool ok = kt * 64 + tid < kend;
+      float a = 1.f, b = 1.f;
+      if constexpr (I8) {
+        a = ok ? h2f((uint16_t)kscr) : 0.f;
+        b = ok ? h2f((uint16_t)vscr) : 0.f;
+      }
+      ksc[tid] = a * scale;
+      vsc[tid] = b;
+    }
+  };
+
+  load_tile(0);
   // Q fragments (A operand of S): row q0 + 16*wave + l16, dims 32s + 8lq .. +7
   half8_t qf[KS];
   {
     const int qr = q0 + 16 * wave + l16;
+    const int qc = min(qr, M - 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      u32x4_t v = {0, 0, 0, 0};
-      if (qr < M) v = *reinterpret_cast<const u32x4_t*>(q + (size_t)qr * d + h * HD + 32 * s + 8 * lq);
-      qf[s] = __builtin_bit_cast(half8_t, v);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(q + (size_t)qc * d + h * HD + 32 * s + 8 * lq);
+      qf[s] = qr < M ? __builtin_bit_cast(half8_t, v) : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   float mrow[4], lrow[4];
@@ -103,35 +160,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
   const int qpos_base = p0 + q0 + 16 * wave + 4 * lq;  // + r
 
-  const int nkt = (kend + 63) / 64;
   for (int kt = 0; kt < nkt; ++kt) {
     const int key0 = kt * 64;
-    // ---- stage K (row-major) and V (transposed) for keys key0..key0+63
-    for (int c = tid; c < 64 * HD / 8; c += 256) {
-      const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const int key = key0 + kr;
-      u32x4_t kvv = {0, 0, 0, 0}, vvv = {0, 0, 0, 0};
-      if (key < kend) {
-        const size_t roff = (size_t)key * HD * (kv.int8 ? 1 : 2);
-        kvv = load8_as_f16(cp.k + roff, d0, kv.int8);
-        vvv = load8_as_f16(cp.v + roff, d0, kv.int8);
-      }
-      *reinterpret_cast<u32x4_t*>(&Ks[kr * LK + d0]) = kvv;
-      const half8_t vh = __builtin_bit_cast(half8_t, vvv);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + kr] = vh[j];
-    }
-    if (tid < 64) {
-      const int key = key0 + tid;
-      float a = 1.f, b = 1.f;
-      if (kv.int8) {
-        a = key < kend ? h2f(cp.ks[key]) : 0.f;
-        b = key < kend ? h2f(cp.vs[key]) : 0.f;
-      }
-      ksc[tid] = a * scale;
-      vsc[tid] = b;
-    }
-    __syncthreads();
+    store_tile(kt);
+    attn_lds_barrier();
+    load_tile(min(kt + 1, nkt - 1));  // the next tile is in flight during this tile's math
+    asm volatile("" ::: "memory");
 
     // ---- S = Q K^T for 16 rows x 64 keys (lane: rows 4lq+r, key 16kb + l16)
     float sv[4][4];
@@ -168,10 +202,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
       for (int b = 0; b < DB; ++b) oacc[b][r] *= alpha;
     }
-    // ---- P (value scale folded in) through LDS into A-operand order, split
-    // into an fp16 high part and the fp16 rounding of the remainder: the two
-    // MFMAs below then apply P with about 22 significant bits instead of 11,
-    // so the softmax weights are not rounded to fp16 before the weighted sum.
+    // ---- P (value scale folded in) through this wave's LDS region into
+    // A-operand order, split into an fp16 high part and the fp16 rounding of
+    // the remainder: the two MFMAs below then apply P with about 22
+    // significant bits instead of 11, so the softmax weights are not rounded
+    // to fp16 before the weighted sum.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const float vs = vsc[kb * 16 + l16];
@@ -183,7 +218,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         Ps[wave][1][(4 * lq + r) * LV + kb * 16 + l16] = (_Float16)(x - (float)hi);
       }
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's P writes land before its reads
     half8_t pa[2], pl[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -200,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
         oacc[b] = mfma16(pl[s], bf, oacc[b]);
       }
     }
-    __syncthreads();
+    attn_lds_barrier();  // every wave is done with this K/V tile before the next is written
   }
   // ---- normalise and store rows q0 + 16*wave + 4lq + r
 #pragma unroll
@@ -216,10 +251,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
 hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const KvGeom& kv, int layer,
                                uint16_t* o, hipStream_t s) {
   dim3 grid((M + 63) / 64, kv.H);
-  if (kv.hd == 128)
-    launch(attn_prefill_kernel<128>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+  if (kv.hd == 128 && kv.int8)
+    launch(attn_prefill_kernel<128, true>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+  else if (kv.hd == 128)
+    launch(attn_prefill_kernel<128, false>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+  else if (kv.hd == 64 && kv.int8)
+    launch(attn_prefill_kernel<64, true>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
   else if (kv.hd == 64)
-    launch(attn_prefill_kernel<64>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    launch(attn_prefill_kernel<64, false>, grid, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

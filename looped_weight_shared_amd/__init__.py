@@ -22,7 +22,7 @@ __all__ = [
     "TL_OK", "TL_E_INVAL", "TL_E_RANGE", "TL_E_STATE", "TL_E_HIP", "TL_E_UNSUPPORTED",
     "TL_KV_FP16", "TL_KV_INT8",
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
-    "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill",
+    "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
     "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
     "KERNEL_KINDS", "EXPORTED",
@@ -88,6 +88,7 @@ _SIGS = {
     "tl_length": (_i32, [_vp, _i32]),
     "tl_prefill": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
     "tl_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tl_set_graphs": (ctypes.c_int, [_vp, _i32]),
     "tl_last_error": (ctypes.c_char_p, []),
     "tl_qlinear_packed_bytes": (_sz, [_i32, _i32]),
     "tl_qlinear_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
@@ -170,6 +171,10 @@ def tl_destroy(ctx) -> None:
 
 def tl_set_loops(ctx, lane: int, loops: int) -> None:
     _check(lib.tl_set_loops(ctx, lane, loops))
+
+
+def tl_set_graphs(ctx, enable: bool) -> None:
+    _check(lib.tl_set_graphs(ctx, 1 if enable else 0))
 
 
 def tl_get_loops(ctx, lane: int) -> int:

@@ -132,6 +132,18 @@ struct tl_ctx {
   tl::Pending pend;  // residual partials not yet added to x
   void* hscr;        // head/argmax per-block candidates
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
+  // optional: prefill launch sequences captured as a HIP graph and replayed
+  // when a later call has the same shape and pointers (cuts host enqueue
+  // time; the GPU time per step is not lower than eager launches)
+  bool graphs = false;
+  hipStream_t cap_stream = nullptr;  // capture only; default priority
+  struct PrefillGraph {
+    bool valid = false;
+    int lane = -1, n = 0, p0 = 0, loops = 0;
+    const void *tokens = nullptr, *hidden = nullptr, *logits = nullptr, *next = nullptr;
+    hipGraphExec_t exec = nullptr;
+  } pg;
+  hipEvent_t pg_done = nullptr;  // recorded after each replay; waited on before the exec is destroyed
   // kernel timing window
   bool prof_on = false;
   std::vector<hipEvent_t> prof_ev;  // 2 per launch
@@ -147,6 +159,8 @@ namespace {
 
 // Sets the kind under which the launches inside the scope are timed while a
 // timing window is open (each launch records its own event pair).
+void drop_prefill_graph(tl_ctx* ctx);
+
 struct KScope {
   KScope(tl_ctx* ctx, int kind, hipStream_t) {
     tl::t_launch_timer = ctx->prof_on ? &ctx->timer : nullptr;
@@ -414,6 +428,9 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
 tl_status tl_destroy(tl_ctx* ctx) {
   if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
   for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
+  drop_prefill_graph(ctx);
+  if (ctx->pg_done) (void)hipEventDestroy(ctx->pg_done);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   delete ctx;
   return TL_OK;
 }
@@ -454,18 +471,15 @@ int32_t tl_length(const tl_ctx* ctx, int32_t lane) {
   return ctx->len[lane];
 }
 
-tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t n, float* d_hidden,
-                     float* d_logits, int32_t* d_next, void* stream) {
-  tl_status st = check_lane(ctx, lane);
-  if (st != TL_OK) return st;
-  if (!d_tokens) return fail(TL_E_INVAL, "d_tokens is NULL");
+}  // extern "C"
+
+namespace {
+
+// The launches of one prefill call (the state update is the caller's).
+tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n, float* d_hidden, float* d_logits,
+                          int32_t* d_next, int p0, int L, hipStream_t s) {
   const tl_config& C = ctx->cfg;
-  if (n < 1 || n > C.max_tokens) return fail(TL_E_RANGE, "n outside 1..max_tokens");
-  const int p0 = ctx->len[lane];
-  if (p0 + n > C.max_seq) return fail(TL_E_RANGE, "prefill would exceed max_seq");
-  const int L = ctx->loops[lane];
-  if (p0 > 0 && C.n_pre + L > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  tl_status st;
   tl::RowMap rm{};
   rm.per_row = 0;
   rm.lane = lane;
@@ -499,8 +513,80 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
       TL_HIP(tl::launch_argmax(1, C.vocab, one, ctx->hscr, d_next, s));
     }
   }
+  return TL_OK;
+}
+
+void drop_prefill_graph(tl_ctx* ctx) {
+  if (ctx->pg.exec) {
+    (void)hipEventSynchronize(ctx->pg_done);  // the last replay may still run
+    (void)hipGraphExecDestroy(ctx->pg.exec);
+  }
+  ctx->pg = tl_ctx::PrefillGraph{};
+}
+
+}  // namespace
+
+extern "C" {
+
+tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t n, float* d_hidden,
+                     float* d_logits, int32_t* d_next, void* stream) {
+  tl_status st = check_lane(ctx, lane);
+  if (st != TL_OK) return st;
+  if (!d_tokens) return fail(TL_E_INVAL, "d_tokens is NULL");
+  const tl_config& C = ctx->cfg;
+  if (n < 1 || n > C.max_tokens) return fail(TL_E_RANGE, "n outside 1..max_tokens");
+  const int p0 = ctx->len[lane];
+  if (p0 + n > C.max_seq) return fail(TL_E_RANGE, "prefill would exceed max_seq");
+  const int L = ctx->loops[lane];
+  if (p0 > 0 && C.n_pre + L > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!ctx->graphs || ctx->prof_on) {
+    st = enqueue_prefill(ctx, lane, d_tokens, n, d_hidden, d_logits, d_next, p0, L, s);
+    if (st != TL_OK) return st;
+  } else {
+    auto& g = ctx->pg;
+    const bool same = g.valid && g.lane == lane && g.n == n && g.p0 == p0 && g.loops == L && g.tokens == d_tokens &&
+                      g.hidden == d_hidden && g.logits == d_logits && g.next == d_next;
+    if (!same) {
+      drop_prefill_graph(ctx);
+      if (!ctx->cap_stream) TL_HIP(hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking));
+      if (!ctx->pg_done) TL_HIP(hipEventCreateWithFlags(&ctx->pg_done, hipEventDisableTiming));
+      hipGraph_t graph = nullptr;
+      TL_HIP(hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal));
+      st = enqueue_prefill(ctx, lane, d_tokens, n, d_hidden, d_logits, d_next, p0, L, ctx->cap_stream);
+      const hipError_t ce = hipStreamEndCapture(ctx->cap_stream, &graph);
+      if (st != TL_OK || ce != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st != TL_OK ? st : fail(TL_E_HIP, std::string("graph capture: ") + hipGetErrorString(ce));
+      }
+      const hipError_t ie = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (ie != hipSuccess) {
+        g.exec = nullptr;
+        return fail(TL_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(ie));
+      }
+      g.valid = true;
+      g.lane = lane;
+      g.n = n;
+      g.p0 = p0;
+      g.loops = L;
+      g.tokens = d_tokens;
+      g.hidden = d_hidden;
+      g.logits = d_logits;
+      g.next = d_next;
+    }
+    TL_HIP(hipGraphLaunch(g.exec, s));
+    TL_HIP(hipEventRecord(ctx->pg_done, s));
+  }
   ctx->len[lane] = p0 + n;
   ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
+  return TL_OK;
+}
+
+tl_status tl_set_graphs(tl_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  ctx->graphs = enable != 0;
+  if (!ctx->graphs) drop_prefill_graph(ctx);
   return TL_OK;
 }
 

@@ -1,0 +1,166 @@
+"""Prefill graph replay gives the same bits as eager launches.
+
+tl_prefill captures its launch sequence once per (lane, n, p0, L, pointers)
+and replays it. A replay must behave exactly like the eager call with the
+same arguments: it reads the token buffer as it is when the replay runs,
+writes the same outputs and KV rows, and leaves the lane in the same state.
+Each replay here is separated by the program's own eager work (output
+buffers poisoned with NaN, decode steps, synchronizations) and is checked
+against a context that launches eagerly.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.conftest import ensure_library
+
+pytestmark = pytest.mark.gpu
+tl = ensure_library()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _model(weights, graphs, **kw):
+    from looped_weight_shared_amd.model import Model
+    m = Model(weights, **kw)
+    m.set_graphs(graphs)
+    return m
+
+
+class Bufs:
+    """Fixed device buffers, so that repeated calls hit the cached graph."""
+
+    def __init__(self, shape, n, n_lanes=1):
+        torch = _torch()
+        self.tok = torch.zeros((n,), dtype=torch.int32, device="cuda")
+        self.hid = torch.empty((n, shape.d_model), dtype=torch.float32, device="cuda")
+        self.lg = torch.empty((shape.vocab,), dtype=torch.float32, device="cuda")
+        self.nx = torch.empty((1,), dtype=torch.int32, device="cuda")
+        self.dtok = torch.zeros((n_lanes,), dtype=torch.int32, device="cuda")
+        self.dhid = torch.empty((n_lanes, shape.d_model), dtype=torch.float32, device="cuda")
+        self.dlg = torch.empty((n_lanes, shape.vocab), dtype=torch.float32, device="cuda")
+        self.dnx = torch.empty((n_lanes,), dtype=torch.int32, device="cuda")
+
+    def poison(self):
+        for t in (self.hid, self.lg, self.dhid, self.dlg):
+            t.fill_(float("nan"))
+        self.nx.fill_(-1)
+        self.dnx.fill_(-1)
+
+
+def _prefill(m, b, tokens, lane=0):
+    torch = _torch()
+    n = len(tokens)
+    b.tok[:n].copy_(torch.from_numpy(np.asarray(tokens, dtype=np.int32)))
+    m.prefill(b.tok[:n], lane=lane, hidden=b.hid[:n], logits=b.lg, next_tok=b.nx)
+    torch.cuda.synchronize()
+    return b.hid[:n].cpu().numpy().copy(), b.lg.cpu().numpy().copy(), int(b.nx.item())
+
+
+def _step(m, b, token):
+    torch = _torch()
+    b.dtok.fill_(token)
+    m.decode_step(b.dtok, hidden=b.dhid, logits=b.dlg, next_tok=b.dnx)
+    torch.cuda.synchronize()
+    return b.dhid.cpu().numpy().copy(), b.dlg.cpu().numpy().copy()
+
+
+def _same(a, b):
+    assert len(a) == len(b)
+    for x, y in zip(a, b):
+        if isinstance(x, np.ndarray):
+            assert np.array_equal(x, y), "graph replay differs from eager launches"
+        else:
+            assert x == y
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    s = synth.SHAPES["tiny"]
+    return s, synth.make_weights(s, seed=3)
+
+
+def test_replays_match_eager_with_work_between(tiny):
+    s, w = tiny
+    kw = dict(max_seq=256, max_loops=4, max_tokens=96)
+    eager, graph = _model(w, False, **kw), _model(w, True, **kw)
+    be, bg = Bufs(s, 96), Bufs(s, 96)
+    prompt = synth.make_tokens(s.vocab, 80, seed=5)
+    for m in (eager, graph):
+        m.set_loops(0, 3)
+    ref = _prefill(eager, be, prompt)
+    ref_steps = [_step(eager, be, t) for t in (7, 11)]
+    for rep in range(4):
+        graph.reset(0)
+        bg.poison()
+        got = _prefill(graph, bg, prompt)          # rep 0 captures, later reps replay
+        _same(got, ref)
+        assert graph.length(0) == 80
+        for t, r in zip((7, 11), ref_steps):       # eager decode on the replayed cache
+            _same(_step(graph, bg, t), r)
+        assert graph.length(0) == 82
+    eager.close()
+    graph.close()
+
+
+def test_replay_reads_current_tokens(tiny):
+    """Same pointers, new token values: the replay must see the new ones."""
+    s, w = tiny
+    kw = dict(max_seq=128, max_loops=2, max_tokens=64)
+    eager, graph = _model(w, False, **kw), _model(w, True, **kw)
+    be, bg = Bufs(s, 64), Bufs(s, 64)
+    for seed in (1, 2, 3):
+        prompt = synth.make_tokens(s.vocab, 64, seed=seed)
+        eager.reset(0)
+        graph.reset(0)
+        bg.poison()
+        _same(_prefill(graph, bg, prompt), _prefill(eager, be, prompt))
+    eager.close()
+    graph.close()
+
+
+def test_changing_keys_recapture(tiny):
+    """Chunked prefill (p0 changes), another L, another lane and another n each
+    need their own capture; alternating between them must stay exact."""
+    s, w = tiny
+    kw = dict(max_seq=256, max_loops=4, n_lanes=2, max_tokens=64)
+    eager, graph = _model(w, False, **kw), _model(w, True, **kw)
+    be, bg = Bufs(s, 64, 2), Bufs(s, 64, 2)
+    toks = synth.make_tokens(s.vocab, 112, seed=9)
+    plan = [(0, 4, [toks[:64], toks[64:112]]),       # two chunks: p0 = 0, 64
+            (1, 2, [toks[:48]]),
+            (0, 1, [toks[:64], toks[64:100]]),
+            (0, 4, [toks[:64], toks[64:112]])]        # first key again
+    for lane, L, chunks in plan:
+        for m, b in ((eager, be), (graph, bg)):
+            m.reset(lane)
+            m.set_loops(lane, L)
+        for c in chunks:
+            bg.poison()
+            _same(_prefill(graph, bg, c, lane=lane), _prefill(eager, be, c, lane=lane))
+        assert graph.length(lane) == eager.length(lane) == sum(len(c) for c in chunks)
+    eager.close()
+    graph.close()
+
+
+def test_timing_window_launches_eagerly(tiny):
+    """Inside a timing window every kernel is timed, so prefill runs eagerly
+    even when a graph for the same call is cached; results stay identical."""
+    s, w = tiny
+    m = _model(w, True, max_seq=128, max_loops=2, max_tokens=32)
+    b = Bufs(s, 32)
+    prompt = synth.make_tokens(s.vocab, 32, seed=4)
+    m.set_loops(0, 2)
+    ref = _prefill(m, b, prompt)                      # captures
+    m.reset(0)
+    tl.tl_profile_begin(m.ctx, 1000)
+    got = _prefill(m, b, prompt)
+    prof = tl.tl_profile_end(m.ctx)
+    _same(got, ref)
+    assert prof["embed"][0] == 1 and prof["attn"][0] == s.n_pre + 2
+    m.reset(0)
+    _same(_prefill(m, b, prompt), ref)               # replay after the window
+    m.close()

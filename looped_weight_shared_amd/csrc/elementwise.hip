@@ -34,7 +34,12 @@ hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, con
 // (CH of them); every load is issued before the first store.
 constexpr int kMaxSplits = kMaxSplitK;
 
-template <int CH>
+// One block per row. Every load is issued first (clamped addresses, no
+// branches): the row of x, the SP pending split partials (SP = 0: none; a
+// power of two >= the actual count S, the extra ones read in bounds and
+// selected out), and the gains. x += the partials summed in split order,
+// then h = fp16(x * rinv * gamma).
+template <int CH, int SP>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pending pend, int M,
                                                       const uint16_t* __restrict__ g, float eps, int d,
                                                       uint16_t* __restrict__ h) {
@@ -42,45 +47,50 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pen
   const int m = blockIdx.x, tid = threadIdx.x;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
   const int nc = d / 4;
+  int cc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) cc[c] = min(tid + 256 * c, nc - 1);
   float4 v[CH];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int ci = tid + 256 * c;
-    v[c] = ci < nc ? xr[ci] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (pend.part) {
+  for (int c = 0; c < CH; ++c) v[c] = xr[cc[c]];
+  constexpr int SPN = SP > 0 ? SP : 1;
+  float4 p[CH][SPN];
+  if constexpr (SP > 0) {
     const float4* pp = reinterpret_cast<const float4*>(pend.part) + (size_t)m * nc;
     const size_t split = (size_t)M * nc;
-    float4 p[CH][kMaxSplits];
 #pragma unroll
     for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int s = 0; s < kMaxSplits; ++s) {
-        const int ci = tid + 256 * c;
-        p[c][s] = (ci < nc && s < pend.S) ? pp[s * split + ci] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int s = 0; s < SP; ++s) p[c][s] = pp[(size_t)min(s, pend.S - 1) * split + cc[c]];
+  }
+  uint2 gr[CH];
+  if (h) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) gr[c] = *reinterpret_cast<const uint2*>(g + 4 * cc[c]);
+  }
+  if constexpr (SP > 0) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       float4 a = p[c][0];
 #pragma unroll
-      for (int s = 1; s < kMaxSplits; ++s)
-        if (s < pend.S) {
-          a.x += p[c][s].x;
-          a.y += p[c][s].y;
-          a.z += p[c][s].z;
-          a.w += p[c][s].w;
-        }
+      for (int s = 1; s < SP; ++s) {
+        const bool on = s < pend.S;
+        a.x += on ? p[c][s].x : 0.f;
+        a.y += on ? p[c][s].y : 0.f;
+        a.z += on ? p[c][s].z : 0.f;
+        a.w += on ? p[c][s].w : 0.f;
+      }
       v[c].x += a.x;
       v[c].y += a.y;
       v[c].z += a.z;
       v[c].w += a.w;
-      const int ci = tid + 256 * c;
-      if (ci < nc) xr[ci] = v[c];
+      if (tid + 256 * c < nc) xr[cc[c]] = v[c];
     }
   }
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+  for (int c = 0; c < CH; ++c)
+    if (tid + 256 * c < nc) acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   acc = wave_sum(acc);
   if ((tid & 63) == 0) part[tid >> 6] = acc;
   __syncthreads();
@@ -92,27 +102,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pen
     const int ci = tid + 256 * c;
     if (ci >= nc) continue;
     const int k = ci * 4;
-    const uint2 gr = *reinterpret_cast<const uint2*>(g + k);
-    const float g0 = h2f(gr.x & 0xFFFF), g1 = h2f(gr.x >> 16), g2 = h2f(gr.y & 0xFFFF), g3 = h2f(gr.y >> 16);
+    const float g0 = h2f(gr[c].x & 0xFFFF), g1 = h2f(gr[c].x >> 16), g2 = h2f(gr[c].y & 0xFFFF), g3 = h2f(gr[c].y >> 16);
     const uint32_t lo = (uint32_t)f2h((v[c].x * rinv) * g0) | ((uint32_t)f2h((v[c].y * rinv) * g1) << 16);
     const uint32_t hi = (uint32_t)f2h((v[c].z * rinv) * g2) | ((uint32_t)f2h((v[c].w * rinv) * g3) << 16);
     *reinterpret_cast<uint2*>(h + (size_t)m * d + k) = make_uint2(lo, hi);
   }
 }
 
+template <int CH>
+static hipError_t rmsnorm_splits(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
+                                 hipStream_t s) {
+  const int S = pend.part ? pend.S : 0;
+  if (S == 0)
+    launch(rmsnorm_kernel<CH, 0>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else if (S <= 2)
+    launch(rmsnorm_kernel<CH, 2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else if (S <= 4)
+    launch(rmsnorm_kernel<CH, 4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else if (S <= 8)
+    launch(rmsnorm_kernel<CH, 8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  else
+    launch(rmsnorm_kernel<CH, 16>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
                           hipStream_t s) {
-  if (d % 4 || d > 8192 || pend.S > kMaxSplits) return hipErrorInvalidValue;
+  if (M < 1) return hipSuccess;
+  if (d % 4 || d < 4 || d > 8192 || (pend.part && (pend.S < 1 || pend.S > kMaxSplits))) return hipErrorInvalidValue;
   const int ch = (d / 4 + 255) / 256;
-  if (ch <= 1)
-    launch(rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
-  else if (ch <= 2)
-    launch(rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
-  else if (ch <= 4)
-    launch(rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
-  else
-    launch(rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
-  return hipGetLastError();
+  if (ch <= 1) return rmsnorm_splits<1>(x, pend, gamma, eps, M, d, h, s);
+  if (ch <= 2) return rmsnorm_splits<2>(x, pend, gamma, eps, M, d, h, s);
+  if (ch <= 4) return rmsnorm_splits<4>(x, pend, gamma, eps, M, d, h, s);
+  return rmsnorm_splits<8>(x, pend, gamma, eps, M, d, h, s);
 }
 
 // ------------------------------------------------------------------ INT8 KV quantizer

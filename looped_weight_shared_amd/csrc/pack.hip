@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t repack_word(uint32_t cw) {
 // One thread per packed word.
 __global__ void pack_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, int N, int K,
                             uint32_t* __restrict__ dst, uint16_t* __restrict__ dst_sc, int G, int nb_offset,
-                            int nb_stride) {
+                            int nb_stride, int perm_hd) {
   const int G_src = (K + 127) / 128;
   const long long total = (long long)(N / 16) * G_src * 256;  // words
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -41,7 +41,7 @@ __global__ void pack_kernel(const uint32_t* __restrict__ qw, const uint16_t* __r
   const long long tile = i >> 8;
   const int g = (int)(tile % G_src);
   const int nb = (int)(tile / G_src);
-  const int n = nb * 16 + (l & 15);
+  const int n = perm_hd ? qkv_natural_col(nb * 16 + (l & 15), perm_hd) : nb * 16 + (l & 15);
   const int k0 = g * 128 + 32 * s + 8 * (l >> 4);
   uint32_t w = 0x88888888u;  // all zeros
   if (k0 < K) w = repack_word(qw[(size_t)n * (K / 8) + k0 / 8]);
@@ -51,12 +51,13 @@ __global__ void pack_kernel(const uint32_t* __restrict__ qw, const uint16_t* __r
 }
 
 hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles,
-                       uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, hipStream_t s) {
+                       uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, int perm_hd, hipStream_t s) {
+  if (perm_hd && (perm_hd % 16 || N % perm_hd)) return hipErrorInvalidValue;
   const long long total = (long long)(N / 16) * ((K + 127) / 128) * 256;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   launch(pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, qweight, scales, N, K,
-                     reinterpret_cast<uint32_t*>(dst_tiles), dst_scales, dst_G, nb_offset, nb_stride);
+                     reinterpret_cast<uint32_t*>(dst_tiles), dst_scales, dst_G, nb_offset, nb_stride, perm_hd);
   return hipGetLastError();
 }
 

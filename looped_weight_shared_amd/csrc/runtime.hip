@@ -171,10 +171,13 @@ struct KScope {
 
 // Decode-shaped calls (M <= 8) use the split-K-in-block GEMV with the RMSNorm
 // fused; larger M uses the MFMA GEMM, whose K-split partials (if the plan
-// splits) are left for the consumer: *S_out receives the split count.
+// splits) are left for the consumer: *S_out receives the split count. An
+// unsplit GEMM uses *gemm_epi instead of e when one is given (*used_gemm_epi
+// tells whether it did).
 tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, int M, const tl::Epi& e,
-                 int* S_out, hipStream_t s) {
+                 int* S_out, hipStream_t s, const tl::Epi* gemm_epi = nullptr, bool* used_gemm_epi = nullptr) {
   *S_out = 1;
+  if (used_gemm_epi) *used_gemm_epi = false;
   // the GEMV's fused RMSNorm reads x as is: pending split-K residual partials
   // (left by a GEMM) must go through the RMSNorm kernel first
   const bool pending = src.x32 && c->pend.part;
@@ -191,9 +194,12 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
     c->pend = tl::Pending{nullptr, 1};
     A = c->h;
   }
+  const int S = tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
+  const bool alt = gemm_epi && S == 1;
   KScope k(c, kind, s);
-  TL_HIP(tl::launch_w4_gemm(w, A, M, e, c->gpart, s));
-  *S_out = tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
+  TL_HIP(tl::launch_w4_gemm(w, A, M, alt ? *gemm_epi : e, c->gpart, s));
+  *S_out = S;
+  if (used_gemm_epi) *used_gemm_epi = alt;
   return TL_OK;
 }
 
@@ -205,9 +211,22 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   const float eps = c->cfg.rms_eps;
   tl_status st;
   int S = 1;
-  // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T
-  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, M,
-              tl::Epi{tl::EPI_STORE, c->qkv, nullptr, 3 * d}, &S, s);
+  // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T (packed in RoPE-pair order).
+  // A prefill GEMM with unsplit K and an FP16 cache applies RoPE and writes
+  // Q and the K/V rows in its epilogue; otherwise qkv goes out in fp32.
+  tl::Epi eq{tl::EPI_STORE, c->qkv, nullptr, 3 * d};
+  eq.perm_hd = c->cfg.head_dim;
+  tl::Epi er = eq;
+  er.mode = tl::EPI_QKV_ROPE;
+  er.rope = c->rope;
+  er.qout = c->q;
+  er.kv = c->kv;
+  er.layer = layer;
+  er.lane = rm.lane;
+  er.p0 = rm.p0;
+  bool roped = false;
+  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, M, eq, &S, s,
+              (!decode && !c->kv.int8) ? &er : nullptr, &roped);
   if (st != TL_OK) return st;
   const float* qkv = S > 1 ? c->gpart : c->qkv;
   tl::ASrc osrc{c->o, nullptr, nullptr, 0.f};
@@ -228,7 +247,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
     if (fuse) osrc = att;
   } else {
     // RoPE on q, k (summing the split-K partials); fp16 Q; K, V into cache layer `layer`
-    {
+    if (!roped) {
       KScope k(c, TL_K_ROPE_KV, s);
       TL_HIP(tl::launch_rope_kv(qkv, S, M, rm, c->rope, c->kv, layer, c->q, s));
     }
@@ -343,9 +362,9 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
     p += al256(tl::packed_bytes(N, K));
     return pk;
   };
-  auto pack = [&](const tl_qlinear& l, int N, int K, const tl::Packed& dst, int off, int stride) {
+  auto pack = [&](const tl_qlinear& l, int N, int K, const tl::Packed& dst, int off, int stride, int perm = 0) {
     return tl::launch_pack(l.qweight, l.scales, N, K, const_cast<uint8_t*>(dst.tiles),
-                           const_cast<uint16_t*>(dst.scales), dst.G, off, stride, s);
+                           const_cast<uint16_t*>(dst.scales), dst.G, off, stride, perm, s);
   };
   for (int b = 0; b <= cfg->n_pre; ++b) {
     const tl_block& src = b < cfg->n_pre ? w->pre[b] : w->loop;
@@ -357,9 +376,11 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
     B.attn_norm = src.attn_norm;
     B.mlp_norm = src.mlp_norm;
     hipError_t e = hipSuccess;
-    if (e == hipSuccess) e = pack(src.wq, d, d, B.qkv, 0, 1);
-    if (e == hipSuccess) e = pack(src.wk, d, d, B.qkv, d / 16, 1);
-    if (e == hipSuccess) e = pack(src.wv, d, d, B.qkv, 2 * d / 16, 1);
+    // q, k, v rows of each head in RoPE-pair order (the QKV epilogues rely on it)
+    const int hd = cfg->head_dim;
+    if (e == hipSuccess) e = pack(src.wq, d, d, B.qkv, 0, 1, hd);
+    if (e == hipSuccess) e = pack(src.wk, d, d, B.qkv, d / 16, 1, hd);
+    if (e == hipSuccess) e = pack(src.wv, d, d, B.qkv, 2 * d / 16, 1, hd);
     if (e == hipSuccess) e = pack(src.wo, d, d, B.o, 0, 1);
     if (e == hipSuccess) e = pack(src.w_gate, f, d, B.gu, 0, 2);  // gate/up n-blocks interleaved
     if (e == hipSuccess) e = pack(src.w_up, f, d, B.gu, 1, 2);
@@ -704,7 +725,7 @@ tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, i
   if (!d_qweight || !d_scales || !d_packed || !aligned(d_packed, 256)) return fail(TL_E_INVAL, "bad pointer");
   uint8_t* t = static_cast<uint8_t*>(d_packed);
   TL_HIP(tl::launch_pack(d_qweight, d_scales, N, K, t, reinterpret_cast<uint16_t*>(t + tl::packed_tile_bytes(N, K)),
-                         (K + 127) / 128, 0, 1, reinterpret_cast<hipStream_t>(stream)));
+                         (K + 127) / 128, 0, 1, 0, reinterpret_cast<hipStream_t>(stream)));
   return TL_OK;
 }
 

@@ -92,6 +92,18 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // Rotary embedding of one pair (x1 = dim i, x2 = dim i + hd/2) by the angle
 // whose cos/sin are c, s; both results are rounded to fp16 (Q and K cast
 // points). Every kernel that rotates uses this one expression.
+// RoPE-pair packing of the QKV rows: within each head of hd rows, packed
+// row 16j + r holds natural row 8j + r (r < 8, first half of rotation pair
+// 8j + r) or hd/2 + 8j + r - 8 (r >= 8, its second half).
+__host__ __device__ __forceinline__ int rope_pair_row(int p, int hd) {
+  const int j = p >> 4, r = p & 15;
+  return r < 8 ? 8 * j + r : hd / 2 + 8 * j + (r - 8);
+}
+__host__ __device__ __forceinline__ int qkv_natural_col(int n, int hd) {
+  const int p = n % hd;
+  return n - p + rope_pair_row(p, hd);
+}
+
 __device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, _Float16* r1, _Float16* r2) {
   *r1 = (_Float16)(x1 * c - x2 * s);
   *r2 = (_Float16)(x2 * c + x1 * s);

@@ -47,18 +47,42 @@ hipError_t launch_pack_head(const uint16_t* head, int V, int d, uint8_t* dst, hi
 
 // Repack a canonical [N][K/8] / [N][ceil(K/128)] linear into the packed
 // buffer of a (possibly fused) destination: source n-block b goes to
-// destination n-block nb_offset + b * nb_stride.
+// destination n-block nb_offset + b * nb_stride. perm_hd > 0 (a multiple of
+// 16) stores the rows of every perm_hd-row head in RoPE-pair order
+// (qkv_natural_col): each n-block then holds 8 rotation pairs, the first
+// halves in its rows 0..7 and the second halves in rows 8..15.
 hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles,
-                       uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, hipStream_t s);
+                       uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, int perm_hd, hipStream_t s);
 hipError_t launch_unpack(const Packed& p, int8_t* q, uint16_t* scales, hipStream_t s);
 
+struct KvGeom {
+  uint8_t* base;        // start of all caches
+  size_t layer_bytes;   // one lane, one layer
+  int n_layers;         // layers per lane
+  int H, hd, S;         // heads, head_dim, max_seq
+  int int8;
+};
+
 // Epilogue of the W4 matrix kernels.
-enum EpiMode { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+//   STORE / RESID: fp32 out[m*ldo + n] = / += v;
+//   SWIGLU: fp16 out[m*ldo + c] = silu(gate) * up (gate/up n-blocks paired);
+//   QKV_ROPE (GEMM, unsplit K, FP16 cache, one lane's rows at p0 + m): the
+//     columns of a RoPE-pair packed QKV (perm_hd = head_dim) are rotated in
+//     registers (the pair partner sits 8 lanes away), rounded to fp16 and
+//     written as Q to qout [M][d] and as K, V rows into cache layer `layer`.
+// perm_hd > 0: the packed columns are in RoPE-pair order; STORE / RESID and
+// split partials write column qkv_natural_col(n).
+enum EpiMode { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV_ROPE = 3 };
 struct Epi {
   int mode;
-  float* out_f32;     // STORE: out[m*ldo + n]; RESID: out[m*ldo + n] += v
-  uint16_t* out_f16;  // SWIGLU: fp16 out[m*ldo + c], c = output column
+  float* out_f32;
+  uint16_t* out_f16;
   int ldo;
+  int perm_hd = 0;
+  const float* rope = nullptr;  // cos [S][hd/2] then sin [S][hd/2]
+  uint16_t* qout = nullptr;
+  KvGeom kv{};
+  int layer = 0, lane = 0, p0 = 0;
 };
 
 // Activation source of the matrix kernels: fp16 rows, or fp32 residual rows
@@ -113,14 +137,6 @@ struct RowMap {
   int lane, p0;
   int row_lane[8];
   int row_pos[8];
-};
-
-struct KvGeom {
-  uint8_t* base;        // start of all caches
-  size_t layer_bytes;   // one lane, one layer
-  int n_layers;         // layers per lane
-  int H, hd, S;         // heads, head_dim, max_seq
-  int int8;
 };
 
 // RoPE on q and k of qkv fp32 [M][3d] (the sum of S split-K partials, each

@@ -31,6 +31,7 @@ namespace tl {
 
 // ---------------------------------------------------------------- epilogue
 __device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float v) {
+  if (e.perm_hd) n = qkv_natural_col(n, e.perm_hd);
   if (e.mode == EPI_RESID)
     e.out_f32[(size_t)m * e.ldo + n] += v;
   else
@@ -328,7 +329,7 @@ static hipError_t gemv_a16(const Packed& w, const ASrc& a, int M, const Epi& e, 
 }
 
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
-  if (!gemv_supported(M, w.K, a)) return hipErrorInvalidValue;
+  if (!gemv_supported(M, w.K, a) || e.mode == EPI_QKV_ROPE) return hipErrorInvalidValue;
   if (a.x32) return e.mode == EPI_SWIGLU ? gemv_norm_rows<2>(w, a, M, e, s) : gemv_norm_rows<1>(w, a, M, e, s);
   if (e.mode == EPI_SWIGLU) return hipErrorInvalidValue;
   if (a.att) return gemv_att(w, a, M, e, s);
@@ -483,9 +484,53 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
         const int m = m0 + i * 16 + 4 * lq + rr;
         if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
-          if (nbw0 + j < NB) pl.part[((size_t)sp * M + m) * N + (nbw0 + j) * 16 + l16] = acc[i][j][rr];
+        for (int j = 0; j < NBW; ++j) {
+          const int n = (nbw0 + j) * 16 + l16;
+          if (nbw0 + j < NB) pl.part[((size_t)sp * M + m) * N + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)] = acc[i][j][rr];
+        }
       }
+    return;
+  }
+
+  // ---- QKV with RoPE, fp16 Q and the K/V cache rows (RoPE-pair packing:
+  // lane l16 < 8 holds the first half of rotation pair t, lane l16 + 8 the
+  // second half; both halves are rotated as rope_pair does)
+  if (e.mode == EPI_QKV_ROPE) {
+    const int hd = e.kv.hd, half = hd / 2, d = e.kv.H * hd;
+    uint8_t* base = e.kv.base + ((size_t)e.lane * e.kv.n_layers + e.layer) * e.kv.layer_bytes;
+    const size_t HS = (size_t)e.kv.H * e.kv.S;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int n = min(nbw0 + j, NB - 1) * 16 + l16;
+      const int sec = n / d, hh = (n - sec * d) / hd, p = n % hd;
+      const bool first = (p & 15) < 8;
+      const int t = 8 * (p >> 4) + (p & 7);
+      const int dim = first ? t : half + t;
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int m = m0 + i * 16 + 4 * lq + rr;
+          const int pos = e.p0 + min(m, M - 1);
+          const float v = acc[i][j][rr];
+          const float other = __shfl_xor(v, 8, 64);
+          float y = v;
+          if (sec < 2) {
+            const float c = e.rope[(size_t)pos * half + t];
+            const float sn = e.rope[(size_t)e.kv.S * half + (size_t)pos * half + t];
+            _Float16 y1, y2;
+            rope_pair(first ? v : other, first ? other : v, c, sn, &y1, &y2);
+            y = (float)(first ? y1 : y2);
+          }
+          const uint16_t hv = f2h(y);
+          if (m < M && nbw0 + j < NB) {
+            if (sec == 0)
+              e.qout[(size_t)m * d + hh * hd + dim] = hv;
+            else
+              reinterpret_cast<uint16_t*>(base)[(sec == 2 ? HS * hd : 0) + ((size_t)hh * e.kv.S + pos) * hd + dim] = hv;
+          }
+        }
+    }
     return;
   }
 
@@ -500,7 +545,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           const int n = min(nbw0 + j, NB - 1) * 16 + l16;
-          acc[i][j][rr] += e.out_f32[(size_t)m * e.ldo + n];
+          acc[i][j][rr] += e.out_f32[(size_t)m * e.ldo + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)];
         }
       }
   }
@@ -518,8 +563,10 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
-          if (nbw0 + j < NB) e.out_f32[(size_t)m * e.ldo + (nbw0 + j) * 16 + l16] = acc[i][j][rr];
+        for (int j = 0; j < NBW; ++j) {
+          const int n = (nbw0 + j) * 16 + l16;
+          if (nbw0 + j < NB) e.out_f32[(size_t)m * e.ldo + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)] = acc[i][j][rr];
+        }
       }
     }
   }
@@ -588,6 +635,8 @@ hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& 
   if (M < 1) return hipErrorInvalidValue;
   GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU);
   if (pl.S > 1 && !part) return hipErrorInvalidValue;
+  if (e.mode == EPI_QKV_ROPE && (pl.S > 1 || e.kv.int8 || e.perm_hd != e.kv.hd || w.N != 3 * e.kv.H * e.kv.hd))
+    return hipErrorInvalidValue;
   pl.part = part;
   if (pl.nbw == 2) {
     switch (pl.mb) {

@@ -190,6 +190,45 @@ tl_status tl_set_graphs(tl_ctx* ctx, int32_t enable);
 tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_active,
                          float* d_hidden, float* d_logits, int32_t* d_next, void* stream);
 
+/* ---- self-speculative decode -------------------------------------------
+ * Greedy generation on one lane where the same weights draft at a shallow
+ * depth and verify at the lane's own L ("Introduction" page, "What Makes It
+ * Different": draft and verify share the weights; "Current Status" page,
+ * speculative decode table: L=2 draft, L=8 verify; "Claims & Data Sources":
+ * draft_loops vs verify_loops). Each round:
+ *   1. drafts k = min(k_draft, max_seq - p - 1) tokens with cached decode
+ *      steps at draft_loops (p = tl_length(lane) at the round's start; the
+ *      first step consumes the round's input token at position p);
+ *   2. verifies the input token and the k drafts in one appended prefill at
+ *      p with the lane's L, taking every row's greedy token from the head;
+ *   3. accepts the drafts up to the first one that differs from the
+ *      verifier's token at its position, and emits them followed by the
+ *      verifier's token there (all k accepted: its token after the last
+ *      draft), i.e. 1..k+1 tokens, each the verifier's greedy choice.
+ * The cache is shared between draft and verify: the verify prefill rewrites
+ * the drafted positions at full depth and the lane's length is set back to
+ * just past the accepted ones. The host reads 2(k+1) token ids per round
+ * (one stream synchronisation per round).
+ * token: the lane's last token, not yet in the cache (as for
+ *   tl_decode_step). Exactly n_new tokens go to h_out (host int32 [n_new]);
+ *   afterwards the last of them is not in the cache (the next call's token)
+ *   and tl_length(lane) has grown by n_new.
+ * stats (may be NULL): rounds, drafted tokens, accepted drafts, tokens
+ * emitted (n_new unless an error stopped the call).
+ * Errors: TL_E_INVAL (bad lane, h_out NULL with n_new > 0), TL_E_RANGE
+ * (token outside the vocabulary, draft_loops outside 1..L, k_draft outside
+ * 1..min(7, max_tokens - 1), the lane reaching max_seq), TL_E_STATE (lane
+ * empty or deeper than its cache, or a timing window open). After an error
+ * the tokens emitted so far are in h_out and the lane holds them as above. */
+typedef struct {
+  int32_t rounds;
+  int32_t drafted;
+  int32_t accepted;
+  int32_t emitted;
+} tl_spec_stats;
+tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft_loops, int32_t k_draft,
+                         int32_t n_new, int32_t* h_out, tl_spec_stats* stats, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tl_last_error(void);
 

@@ -22,7 +22,7 @@ __all__ = [
     "TL_OK", "TL_E_INVAL", "TL_E_RANGE", "TL_E_STATE", "TL_E_HIP", "TL_E_UNSUPPORTED",
     "TL_KV_FP16", "TL_KV_INT8",
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
-    "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs",
+    "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs", "tl_spec_decode", "TlSpecStats",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
     "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
     "KERNEL_KINDS", "EXPORTED",
@@ -74,6 +74,10 @@ class TlWeights(ctypes.Structure):
                 ("final_norm", _vp), ("head", _vp)]
 
 
+class TlSpecStats(ctypes.Structure):
+    _fields_ = [("rounds", _i32), ("drafted", _i32), ("accepted", _i32), ("emitted", _i32)]
+
+
 _CFG = ctypes.POINTER(TlConfig)
 _SIGS = {
     "tl_weights_ws_bytes": (_sz, [_CFG]),
@@ -89,6 +93,8 @@ _SIGS = {
     "tl_prefill": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
     "tl_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tl_set_graphs": (ctypes.c_int, [_vp, _i32]),
+    "tl_spec_decode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                      ctypes.POINTER(TlSpecStats), _vp]),
     "tl_last_error": (ctypes.c_char_p, []),
     "tl_qlinear_packed_bytes": (_sz, [_i32, _i32]),
     "tl_qlinear_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
@@ -194,6 +200,20 @@ def tl_length(ctx, lane: int) -> int:
 def tl_prefill(ctx, lane: int, tokens, n: int, hidden=None, logits=None, next_tok=None, stream=None) -> None:
     _check(lib.tl_prefill(ctx, lane, _ptr(tokens), n, _ptr(hidden), _ptr(logits), _ptr(next_tok),
                           _stream(stream)))
+
+
+def tl_spec_decode(ctx, lane: int, token: int, draft_loops: int, k_draft: int, n_new: int, stream=None):
+    """Returns (tokens: list of n_new ints, TlSpecStats). On an error the
+    TLError carries the tokens emitted before it as .tokens."""
+    out = (_i32 * max(n_new, 1))()
+    st = TlSpecStats()
+    rc = lib.tl_spec_decode(ctx, lane, token, draft_loops, k_draft, n_new, out, ctypes.byref(st), _stream(stream))
+    toks = list(out[:n_new])
+    if rc != TL_OK:
+        err = TLError(rc, lib.tl_last_error().decode())
+        err.tokens = toks[:st.emitted]
+        raise err
+    return toks, st
 
 
 def tl_decode_step(ctx, tokens, active=None, hidden=None, logits=None, next_tok=None, stream=None) -> None:

@@ -87,8 +87,13 @@ size_t gemm_scratch_bytes(const tl_config* c) {
   return mx;
 }
 
+// Self-speculative decode drafts at most this many tokens per round, so the
+// verify prefill (draft + 1 rows) fits the head kernel's row limit.
+constexpr int kSpecMaxDraft = 7;
+int head_rows_cap(const tl_config* c) { return std::max(c->n_lanes, kSpecMaxDraft + 1); }
+
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -101,9 +106,12 @@ ActLayout act_layout(const tl_config* c) {
   L.o = off; off += al256(T * d * 2);
   L.a = off; off += al256(T * f * 2);
   L.part = off; off += al256(tl::attn_decode_scratch_floats(c->n_lanes, c->n_heads, c->head_dim, c->max_seq) * 4);
-  L.logits = off; off += al256((size_t)c->n_lanes * c->vocab * 4);
+  L.logits = off; off += al256((size_t)head_rows_cap(c) * c->vocab * 4);
   L.gpart = off; off += al256(gemm_scratch_bytes(c));
-  L.hscr = off; off += al256(tl::head_scratch_bytes(c->n_lanes, c->vocab));
+  L.hscr = off; off += al256(tl::head_scratch_bytes(head_rows_cap(c), c->vocab));
+  // speculative tokens: draft chain [kSpecMaxDraft + 2][n_lanes], verify
+  // tokens and verifier argmaxes [kSpecMaxDraft + 1] each
+  L.spec = off; off += al256(((size_t)(kSpecMaxDraft + 2) * c->n_lanes + 2 * (kSpecMaxDraft + 1)) * 4);
   L.total = off;
   return L;
 }
@@ -131,7 +139,11 @@ struct tl_ctx {
   float* gpart;      // split-K partial tiles of the prefill GEMM
   tl::Pending pend;  // residual partials not yet added to x
   void* hscr;        // head/argmax per-block candidates
+  int32_t* spec_chain;  // [kSpecMaxDraft + 2][n_lanes]
+  int32_t* spec_ver;    // [kSpecMaxDraft + 1]
+  int32_t* spec_next;   // [kSpecMaxDraft + 1]
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
+  int32_t spec_host[16];               // host side of the speculative token exchange
   // optional: prefill launch sequences captured as a HIP graph and replayed
   // when a later call has the same shape and pointers (cuts host enqueue
   // time; the GPU time per step is not lower than eager launches)
@@ -438,6 +450,9 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->logits = reinterpret_cast<float*>(ab + L.logits);
   c->gpart = reinterpret_cast<float*>(ab + L.gpart);
   c->hscr = ab + L.hscr;
+  c->spec_chain = reinterpret_cast<int32_t*>(ab + L.spec);
+  c->spec_ver = c->spec_chain + (size_t)(kSpecMaxDraft + 2) * cfg->n_lanes;
+  c->spec_next = c->spec_ver + (kSpecMaxDraft + 1);
   c->pend = tl::Pending{nullptr, 1};
   c->len.assign(cfg->n_lanes, 0);
   c->loops.assign(cfg->n_lanes, 1);
@@ -498,7 +513,7 @@ namespace {
 
 // The launches of one prefill call (the state update is the caller's).
 tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n, float* d_hidden, float* d_logits,
-                          int32_t* d_next, int p0, int L, hipStream_t s) {
+                          int32_t* d_next, int p0, int L, hipStream_t s, bool head_all_rows = false) {
   const tl_config& C = ctx->cfg;
   tl_status st;
   tl::RowMap rm{};
@@ -522,16 +537,19 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
     TL_HIP(hipMemcpyAsync(d_hidden, ctx->x, (size_t)n * d * 4, hipMemcpyDeviceToDevice, s));
   }
   if (d_logits || d_next) {
+    // the last row, or every row (n <= the head's row limit): logits row m
+    // at lg + m * vocab, argmax at d_next[m]
     float* lg = d_logits ? d_logits : ctx->logits;
     tl::RowMap one{};
+    const int rows = head_all_rows ? n : 1;
     {
       KScope k(ctx, TL_K_HEAD, s);
-      TL_HIP(tl::launch_head(ctx->x + (size_t)(n - 1) * d, 1, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg,
-                             one, ctx->hscr, s));
+      TL_HIP(tl::launch_head(ctx->x + (size_t)(n - rows) * d, rows, ctx->final_norm, C.rms_eps, ctx->head, C.vocab,
+                             d, lg, one, ctx->hscr, s));
     }
     if (d_next) {
       KScope k(ctx, TL_K_ARGMAX, s);
-      TL_HIP(tl::launch_argmax(1, C.vocab, one, ctx->hscr, d_next, s));
+      TL_HIP(tl::launch_argmax(rows, C.vocab, one, ctx->hscr, d_next, s));
     }
   }
   return TL_OK;
@@ -667,6 +685,98 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
     ctx->depth[l] = std::min(ctx->depth[l], C.n_pre + ctx->loops[l]);
   }
   return TL_OK;
+}
+
+// Self-speculative greedy decode of one lane: draft with cached decode steps
+// at draft_loops, verify with one appended prefill of the k + 1 tokens at
+// the lane's own L, every row's greedy token from the head; accept drafts up
+// to the first that differs from the verifier's token, then emit the
+// verifier's token there. The cache is shared: verification rewrites the
+// drafted positions at full depth and the length is set back past the
+// accepted ones.
+tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft_loops, int32_t k_draft,
+                         int32_t n_new, int32_t* h_out, tl_spec_stats* stats, void* stream) {
+  tl_status st = check_lane(ctx, lane);
+  if (st != TL_OK) return st;
+  const tl_config& C = ctx->cfg;
+  if (!h_out && n_new > 0) return fail(TL_E_INVAL, "h_out is NULL");
+  if (token < 0 || token >= C.vocab) return fail(TL_E_RANGE, "token outside 0..vocab-1");
+  const int Lv = ctx->loops[lane];
+  if (draft_loops < 1 || draft_loops > Lv) return fail(TL_E_RANGE, "draft_loops outside 1..L of the lane");
+  if (k_draft < 1 || k_draft > kSpecMaxDraft || k_draft + 1 > C.max_tokens)
+    return fail(TL_E_RANGE, "k_draft outside 1..min(7, max_tokens - 1)");
+  if (ctx->len[lane] < 1) return fail(TL_E_STATE, "speculative decode on a lane with no cached token");
+  if (C.n_pre + Lv > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
+  if (n_new > 0 && ctx->len[lane] >= C.max_seq) return fail(TL_E_RANGE, "lane is at max_seq");
+  if (ctx->prof_on) return fail(TL_E_STATE, "not inside a timing window");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  tl_spec_stats acc{0, 0, 0, 0};
+  const int nl = C.n_lanes;
+  std::vector<uint8_t> active(nl, 0);
+  active[lane] = 1;
+  int32_t* chain = ctx->spec_chain;  // row i: the token decode step i consumes, at [lane]
+  ctx->spec_host[0] = token;
+  TL_HIP(hipMemcpyAsync(chain + lane, ctx->spec_host, 4, hipMemcpyHostToDevice, s));
+  const int depth0 = ctx->depth[lane];
+  int emitted = 0;
+  while (emitted < n_new) {
+    const int p = ctx->len[lane];
+    if (p >= C.max_seq) {
+      st = fail(TL_E_RANGE, "lane reached max_seq");
+      break;
+    }
+    const int k = std::min(k_draft, C.max_seq - p - 1);  // positions p .. p+k must fit
+    // draft: k cached decode steps at draft_loops
+    ctx->loops[lane] = draft_loops;
+    for (int i = 0; i < k && st == TL_OK; ++i)
+      st = tl_decode_step(ctx, chain + (size_t)i * nl, active.data(), nullptr, nullptr, chain + (size_t)(i + 1) * nl,
+                          stream);
+    ctx->loops[lane] = Lv;
+    // verify: tokens t0..tk as one prefill at p with the head on every row
+    // (after a failure: the drafted rows are dropped the same way)
+    ctx->len[lane] = p;
+    ctx->depth[lane] = depth0;
+    if (st != TL_OK) break;
+    hipError_t he = hipMemcpy2DAsync(ctx->spec_ver, 4, chain + lane, (size_t)nl * 4, 4, k + 1,
+                                     hipMemcpyDeviceToDevice, s);
+    if (he != hipSuccess) {
+      st = fail(TL_E_HIP, std::string("hipMemcpy2DAsync: ") + hipGetErrorString(he));
+      break;
+    }
+    st = enqueue_prefill(ctx, lane, ctx->spec_ver, k + 1, nullptr, nullptr, ctx->spec_next, p, Lv, s, true);
+    if (st != TL_OK) break;
+    int32_t* hv = ctx->spec_host;  // [0, k]: t0..tk, [8, 8+k]: v0..vk
+    he = hipMemcpyAsync(hv, ctx->spec_ver, (size_t)(k + 1) * 4, hipMemcpyDeviceToHost, s);
+    if (he == hipSuccess) he = hipMemcpyAsync(hv + 8, ctx->spec_next, (size_t)(k + 1) * 4, hipMemcpyDeviceToHost, s);
+    if (he == hipSuccess) he = hipStreamSynchronize(s);
+    if (he != hipSuccess) {
+      st = fail(TL_E_HIP, std::string("reading the verify tokens: ") + hipGetErrorString(he));
+      break;
+    }
+    int a = 0;
+    while (a < k && hv[1 + a] == hv[8 + a]) ++a;
+    // emitted this round: t1..ta, then v_a; the cache keeps t0..t(r-1)
+    const int r = std::min(a + 1, n_new - emitted);
+    for (int j = 0; j < r; ++j) h_out[emitted + j] = j < a ? hv[1 + j] : hv[8 + a];
+    emitted += r;
+    ctx->len[lane] = p + r;
+    acc.rounds += 1;
+    acc.drafted += k;
+    acc.accepted += a;
+    // the next round starts from the last emitted token (not cached)
+    if (emitted < n_new) {
+      he = hipMemcpyAsync(chain + lane, ctx->spec_next + a, 4, hipMemcpyDeviceToDevice, s);
+      if (he != hipSuccess) {
+        st = fail(TL_E_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(he));
+        break;
+      }
+    }
+  }
+  ctx->loops[lane] = Lv;
+  ctx->depth[lane] = depth0;
+  acc.emitted = emitted;
+  if (stats) *stats = acc;
+  return st;
 }
 
 tl_status tl_profile_begin(tl_ctx* ctx, int32_t max_launches) {

@@ -14,7 +14,7 @@ import torch
 
 from . import (TL_KV_FP16, TlBlock, TlConfig, TlQLinear, TlWeights, tl_act_ws_bytes, tl_create,
                tl_decode_step, tl_destroy, tl_get_loops, tl_kv_bytes, tl_length, tl_prefill, tl_reset,
-               tl_set_graphs, tl_set_loops, tl_weights_ws_bytes)
+               tl_set_graphs, tl_set_loops, tl_spec_decode, tl_weights_ws_bytes)
 
 _LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
@@ -98,6 +98,10 @@ class Model:
 
     def prefill(self, tokens: torch.Tensor, lane=0, hidden=None, logits=None, next_tok=None, stream=None):
         tl_prefill(self.ctx, lane, tokens, int(tokens.numel()), hidden, logits, next_tok, stream)
+
+    def spec_decode(self, token: int, n_new: int, draft_loops: int, k_draft: int, lane=0, stream=None):
+        """Self-speculative greedy decode: (tokens, TlSpecStats)."""
+        return tl_spec_decode(self.ctx, lane, token, draft_loops, k_draft, n_new, stream)
 
     def decode_step(self, tokens: torch.Tensor, active=None, hidden=None, logits=None, next_tok=None,
                     stream=None):

@@ -22,14 +22,17 @@ Sources (the TinyLoop documentation pages):
     matched VRAM": per-token per-head symmetric INT8 with one FP16 scale;
     section "Key Runtime Switches" (TINYLOOP_DISABLE_KV_CACHE): the uncached
     recompute is the parity reference for cached decode.
+  * Self-speculative decode ("Introduction" page, "What Makes It Different";
+    "Current Status" page, speculative decode table): speculative.py.
 """
 from .int4 import pack_int4, unpack_int4, dequantize
 from .kvquant import kv_quantize, kv_dequantize, kv_cache_bytes
 from .model import (OracleModel, Cache, rmsnorm, rope_cos_sin, apply_rope, attention,
                     silu, fp16, forward, decode_step, generate_greedy, forward_uncached,
                     head_logits)
+from .speculative import speculative_greedy
 
 __all__ = ["pack_int4", "unpack_int4", "dequantize", "kv_quantize", "kv_dequantize",
            "kv_cache_bytes", "OracleModel", "Cache", "rmsnorm", "rope_cos_sin", "apply_rope",
            "attention", "silu", "fp16", "forward", "decode_step", "generate_greedy",
-           "forward_uncached", "head_logits"]
+           "forward_uncached", "head_logits", "speculative_greedy"]

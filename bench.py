@@ -288,6 +288,31 @@ def main():
                          "gemv_GBps": {k: round(v, 1) for k, v in gb.items()}}
         out["roofline_decode"] = rd
 
+        # ------------------------------------------------------------ self-speculative decode
+        # same prompt and depth; drafts at L=2 ("Current Status" page: L=2
+        # draft, L=8 verify). Wall clock (the call synchronises once per round).
+        spec = {}
+        for kd in (2, 4, 7):
+            m.reset(0)
+            m.prefill(ptoks, next_tok=bufs[0])
+            torch.cuda.synchronize()
+            t_first = int(bufs[0].item())
+            m.spec_decode(t_first, 8, draft_loops=2, k_draft=kd)      # warm-up
+            m.reset(0)
+            m.prefill(ptoks, next_tok=bufs[0])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            toks, st = m.spec_decode(t_first, D, draft_loops=2, k_draft=kd)
+            dt = time.perf_counter() - t0
+            spec[f"k{kd}"] = {"ms_per_token": round(dt * 1e3 / D, 4), "rounds": st.rounds,
+                              "drafted": st.drafted, "accepted": st.accepted,
+                              "speedup_vs_plain": round(ms_tok / (dt * 1e3 / D), 3)}
+            print(f"[bench] spec decode draft L=2 verify L={L} k={kd}: {dt * 1e3 / D:.4f} ms/token, "
+                  f"accepted {st.accepted}/{st.drafted}", file=sys.stderr, flush=True)
+        out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
+                              "note": "greedy; acceptance is a property of the weights (synthetic here)",
+                              **spec}
+
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:
         import oracle

@@ -7,7 +7,7 @@
 // read back as q * s in the prefill too (cached and uncached paths agree).
 //
 // Prefill: a block takes 64 queries of one head (4 waves x 16 rows) and walks
-// 64-key tiles up to its causal limit: K tile and transposed V tile staged in
+// 128-key tiles up to its causal limit: K tile and transposed V tile staged in
 // LDS, S = Q K^T and O += P V on v_mfma_f32_16x16x32_f16, online softmax in
 // fp32 (running max and sum per row). INT8 codes are exact in fp16, so the
 // MFMAs run on the codes and the per-key scales multiply the score columns
@@ -54,24 +54,29 @@ __device__ __forceinline__ void attn_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// K/V tile t (keys 64t .. 64t+63) is requested into registers while tile t-1
-// is computed (raw: fp16 rows, or INT8 codes and scales, converted when
-// written to LDS so the request never waits), then written to LDS: K
+// K/V tile t (keys KT*t .. KT*t + KT-1) is requested into registers while
+// tile t-1 is computed (raw: fp16 rows, or INT8 codes and scales, converted
+// when written to LDS so the request never waits), then written to LDS: K
 // row-major, V transposed. The block barriers wait on LDS only, so the next
-// tile's requests stay in flight across them.
+// tile's requests stay in flight across them. KT = 128 keys per tile: a
+// 128-token call takes one tile per block.
+constexpr int kAttnKT = 128;
 template <int HD, bool I8>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __restrict__ q, int M, int lane_id,
                                                            int p0, KvGeom kv, int layer, uint16_t* __restrict__ o) {
+  constexpr int KT = kAttnKT;     // keys per tile
+  constexpr int KB = KT / 16;     // 16-key blocks of S
+  constexpr int PS = KT / 32;     // k-steps of O += P V
   constexpr int KS = HD / 32;     // k-steps of S = Q K^T
   constexpr int DB = HD / 16;     // 16-wide d blocks of O
   constexpr int LK = HD + 8;      // LDS row stride of the K tile (halves)
-  constexpr int LV = 64 + 8;      // LDS row stride of the transposed V tile
-  constexpr int CPT = 64 * HD / 8 / 256;  // 8-element chunks of K (and of V) per thread and tile
+  constexpr int LV = KT + 8;      // LDS row stride of the transposed V tile
+  constexpr int CPT = KT * HD / 8 / 256;  // 8-element chunks of K (and of V) per thread and tile
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
-  __shared__ __align__(16) _Float16 Ks[64 * LK];
+  __shared__ __align__(16) _Float16 Ks[KT * LK];
   __shared__ __align__(16) _Float16 Vt[HD * LV];
   __shared__ __align__(16) _Float16 Ps[4][2][16 * LV];  // P as fp16 high and low parts
-  __shared__ float ksc[64], vsc[64];
+  __shared__ float ksc[KT], vsc[KT];
 
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int l16 = ln & 15, lq = ln >> 4;
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   const int kend = p0 + min(q0 + 64, M);  // keys [0, kend) can be visible to this block
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const float scale = 1.0f / sqrtf((float)HD);
-  const int nkt = (kend + 63) / 64;
+  const int nkt = (kend + KT - 1) / KT;
 
   Raw kreg[CPT], vreg[CPT];
   uint32_t kscr = 0, vscr = 0;  // raw fp16 scales (INT8), threads < 64
@@ -90,12 +95,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const size_t roff = (size_t)min(kt * 64 + kr, kend - 1) * HD * (I8 ? 1 : 2) + d0 * (I8 ? 1 : 2);
+      const size_t roff = (size_t)min(kt * KT + kr, kend - 1) * HD * (I8 ? 1 : 2) + d0 * (I8 ? 1 : 2);
       kreg[i] = *reinterpret_cast<const Raw*>(cp.k + roff);
       vreg[i] = *reinterpret_cast<const Raw*>(cp.v + roff);
     }
     if constexpr (I8) {
-      const int key = min(kt * 64 + (tid & 63), kend - 1);
+      const int key = min(kt * KT + (tid & (KT - 1)), kend - 1);
       kscr = cp.ks[key];
       vscr = cp.vs[key];
     }
@@ -119,14 +124,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const bool ok = kt * 64 + kr < kend;
+      const bool ok = kt * KT + kr < kend;
       *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
       const half8_t vh = ok ? to_f16(vreg[i]) : hz;
 #pragma unroll
       for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + kr] = vh[j];
     }
-    if (tid < 64) {
-      const bool ok = kt * 64 + tid < kend;
+    if (tid < KT) {
+      const bool ok = kt * KT + tid < kend;
       float a = 1.f, b = 1.f;
       if constexpr (I8) {
         a = ok ? h2f((uint16_t)kscr) : 0.f;
@@ -161,16 +166,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   const int qpos_base = p0 + q0 + 16 * wave + 4 * lq;  // + r
 
   for (int kt = 0; kt < nkt; ++kt) {
-    const int key0 = kt * 64;
+    const int key0 = kt * KT;
     store_tile(kt);
     attn_lds_barrier();
     load_tile(min(kt + 1, nkt - 1));  // the next tile is in flight during this tile's math
     asm volatile("" ::: "memory");
 
-    // ---- S = Q K^T for 16 rows x 64 keys (lane: rows 4lq+r, key 16kb + l16)
-    float sv[4][4];
+    // ---- S = Q K^T for 16 rows x KT keys (lane: rows 4lq+r, key 16kb + l16)
+    float sv[KB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -185,13 +190,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     // ---- online softmax per row
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float mx = fmaxf(fmaxf(sv[0][r], sv[1][r]), fmaxf(sv[2][r], sv[3][r]));
+      float mx = sv[0][r];
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, sv[kb][r]);
       mx = row16_max(mx);
       const float mnew = fmaxf(mrow[r], mx);
       const float alpha = expf(mrow[r] - mnew);  // 0 on the first tile (mrow = -inf)
       float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const float p = expf(sv[kb][r] - mnew);
         ps += p;
         sv[kb][r] = p;
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     // significant bits instead of 11, so the softmax weights are not rounded
     // to fp16 before the weighted sum.
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const float vs = vsc[kb * 16 + l16];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -219,9 +226,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's P writes land before its reads
-    half8_t pa[2], pl[2];
+    half8_t pa[PS], pl[PS];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < PS; ++s) {
       pa[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][0][l16 * LV + 32 * s + 8 * lq]);
       pl[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][1][l16 * LV + 32 * s + 8 * lq]);
     }
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < PS; ++s) {
         const half8_t bf = *reinterpret_cast<const half8_t*>(&Vt[(b * 16 + l16) * LV + 32 * s + 8 * lq]);
         oacc[b] = mfma16(pa[s], bf, oacc[b]);
         oacc[b] = mfma16(pl[s], bf, oacc[b]);

@@ -71,6 +71,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   constexpr int DB = HD / 16;     // 16-wide d blocks of O
   constexpr int LK = HD + 8;      // LDS row stride of the K tile (halves)
   constexpr int LV = KT + 8;      // LDS row stride of the transposed V tile
+  // Vt row d holds its 8-key chunks in swizzled order: chunk c at slot
+  // c ^ ((d / 8) % NC). The transposing writes (a wave writes one dim of 16
+  // rows 8 apart) then spread over the banks instead of piling onto two,
+  // and an MFMA fragment (8 consecutive keys of one row) stays contiguous.
+  constexpr int NC = KT / 8;
   constexpr int CPT = KT * HD / 8 / 256;  // 8-element chunks of K (and of V) per thread and tile
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
   __shared__ __align__(16) _Float16 Ks[KT * LK];
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
       *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
       const half8_t vh = ok ? to_f16(vreg[i]) : hz;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + kr] = vh[j];
+      for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + 8 * ((kr >> 3) ^ ((d0 >> 3) & (NC - 1))) + (kr & 7)] = vh[j];
     }
     if (tid < KT) {
       const bool ok = kt * KT + tid < kend;
@@ -237,7 +242,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int s = 0; s < PS; ++s) {
-        const half8_t bf = *reinterpret_cast<const half8_t*>(&Vt[(b * 16 + l16) * LV + 32 * s + 8 * lq]);
+        const int vr = b * 16 + l16;
+        const half8_t bf =
+            *reinterpret_cast<const half8_t*>(&Vt[vr * LV + 8 * ((4 * s + lq) ^ ((vr >> 3) & (NC - 1)))]);
         oacc[b] = mfma16(pa[s], bf, oacc[b]);
         oacc[b] = mfma16(pl[s], bf, oacc[b]);
       }

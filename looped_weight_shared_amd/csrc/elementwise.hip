@@ -410,8 +410,9 @@ __global__ __launch_bounds__(256) void head_kernel(const float* __restrict__ x, 
   }
 }
 
-// Greedy next token of each row from the head blocks' candidates, scanned in
-// block order with ties to the lowest index.
+// Greedy next token of each row from the head blocks' candidates: the
+// largest logit, ties to the lowest index (a total order, so the result does
+// not depend on the scan order).
 __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ cval, const int* __restrict__ cidx,
                                                      int nblk, RowMap rm, int32_t* __restrict__ next) {
   __shared__ float bv_s[4];
@@ -419,12 +420,26 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ c
   const int m = blockIdx.x, tid = threadIdx.x;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int b = tid; b < nblk; b += 256) {
-    const float cv = cval[(size_t)m * nblk + b];
-    const int ci = cidx[(size_t)m * nblk + b];
-    if (cv > bv || (cv == bv && ci < bi)) {
-      bv = cv;
-      bi = ci;
+  // kArgPer candidates per thread are requested before any is compared
+  // (clamped indices, out-of-range ones dropped), so the scan costs one
+  // round trip per 256 * kArgPer candidates
+  constexpr int kArgPer = 16;
+  for (int base = 0; base < nblk; base += 256 * kArgPer) {
+    float cv[kArgPer];
+    int ci[kArgPer];
+#pragma unroll
+    for (int j = 0; j < kArgPer; ++j) {
+      const int b = min(base + tid + 256 * j, nblk - 1);
+      cv[j] = cval[(size_t)m * nblk + b];
+      ci[j] = cidx[(size_t)m * nblk + b];
+    }
+#pragma unroll
+    for (int j = 0; j < kArgPer; ++j) {
+      const bool in = base + tid + 256 * j < nblk;
+      if (in && (cv[j] > bv || (cv[j] == bv && ci[j] < bi))) {
+        bv = cv[j];
+        bi = ci[j];
+      }
     }
   }
 #pragma unroll

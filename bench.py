@@ -84,7 +84,7 @@ def _pmc_dispatches(d, counter):
 
 def ingest_pmc(fetch_dir, write_dir, copy_mib):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --steps 3 --warmup 1 --no-cpu --decode-steps 4 --copy-mib <copy_mib>`, one with
+    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --decode-steps 4 --copy-mib <copy_mib>`, one with
     FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
     for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
@@ -113,7 +113,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
                          tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    run = "bench.py --steps 3 --warmup 1 --no-cpu --decode-steps 4 --copy-mib %d" % copy_mib
+    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --decode-steps 4 --copy-mib %d" % copy_mib
     data = {"commands": [
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,
@@ -151,6 +151,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -292,7 +293,7 @@ def main():
         # same prompt and depth; drafts at L=2 ("Current Status" page: L=2
         # draft, L=8 verify). Wall clock (the call synchronises once per round).
         spec = {}
-        for kd in (2, 4, 7):
+        for kd in (() if args.no_spec else (2, 4, 7)):
             m.reset(0)
             m.prefill(ptoks, next_tok=bufs[0])
             torch.cuda.synchronize()
@@ -309,9 +310,10 @@ def main():
                               "speedup_vs_plain": round(ms_tok / (dt * 1e3 / D), 3)}
             print(f"[bench] spec decode draft L=2 verify L={L} k={kd}: {dt * 1e3 / D:.4f} ms/token, "
                   f"accepted {st.accepted}/{st.drafted}", file=sys.stderr, flush=True)
-        out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
-                              "note": "greedy; acceptance is a property of the weights (synthetic here)",
-                              **spec}
+        if spec:
+            out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
+                                  "note": "greedy; acceptance is a property of the weights (synthetic here)",
+                                  **spec}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:

@@ -71,12 +71,14 @@ def apply_rope(x, cos, sin):
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def attention(Q, K, V, q_pos):
+def attention(Q, K, V, q_pos, window=0):
     """Causal softmax attention per head.
 
     Q [n][H][hd]; K, V [S][H][hd] hold cache rows 0..S-1; query m sees keys
-    j <= q_pos[m]. Scores are scaled by 1/sqrt(hd); softmax subtracts the row
-    maximum. Returns [n][H][hd].
+    j <= q_pos[m], and with window W > 0 only keys j > q_pos[m] - W (the
+    last W cached tokens: "Performance and Memory" page, "Sliding-Window
+    Cache"; 0 means the full cache). Scores are scaled by 1/sqrt(hd); softmax
+    subtracts the row maximum. Returns [n][H][hd].
     """
     n, H, hd = Q.shape
     S = K.shape[0]
@@ -85,6 +87,8 @@ def attention(Q, K, V, q_pos):
     Vh = np.ascontiguousarray(V.transpose(1, 0, 2))          # H S hd
     scores = np.matmul(Qh, Kh) / math.sqrt(hd)               # H n S
     masked = np.arange(S)[None, :] > np.asarray(q_pos)[:, None]
+    if window > 0:
+        masked |= np.arange(S)[None, :] <= np.asarray(q_pos)[:, None] - window
     scores[:, masked] = -np.inf
     scores -= scores.max(axis=-1, keepdims=True)
     p = np.exp(scores)
@@ -133,10 +137,11 @@ class Cache:
     depth[t] is the number of effective layers token t was computed through.
     """
 
-    def __init__(self, shape, max_seq, kv_int8=False):
+    def __init__(self, shape, max_seq, kv_int8=False, window=0):
         self.shape = shape
         self.max_seq = max_seq
         self.kv_int8 = kv_int8
+        self.window = window  # cache_window: > 0 keeps only the last `window` tokens visible
         self.length = 0
         self.k, self.v = {}, {}
         self.kq, self.ks, self.vq, self.vs = {}, {}, {}, {}
@@ -184,7 +189,7 @@ def _block_forward(x, B, cache, layer, positions, s, casts):
     else:
         cache.write(layer, positions, K, V)
     Kall, Vall = cache.read(layer, int(positions[-1]) + 1)
-    O = c(attention(Q, Kall, Vall, positions)).reshape(n, H * hd)
+    O = c(attention(Q, Kall, Vall, positions, cache.window)).reshape(n, H * hd)
     x = x + O @ B["wo"].T
     h2 = c(rmsnorm(x, B["mlp_norm"], s.rms_eps))
     a = c(silu(h2 @ B["w_gate"].T) * (h2 @ B["w_up"].T))
@@ -199,7 +204,7 @@ def head_logits(model, x_rows, casts=True):
 
 
 def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False,
-            max_seq=None, kv_int8=False):
+            max_seq=None, kv_int8=False, window=0):
     """Append `tokens` to a lane at its current length and run all n_pre + L layers.
 
     Returns a dict with the final residual rows 'hidden' [n][d] (before the
@@ -212,7 +217,7 @@ def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False
     if L < 1:
         raise ValueError("L must be >= 1")
     if cache is None:
-        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8)
+        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8, window=window)
     p0 = cache.length
     if p0 + n > cache.max_seq:
         raise ValueError("sequence exceeds max_seq")
@@ -251,13 +256,13 @@ def forward_uncached(model, tokens, L, casts=True, kv_int8=False):
                    kv_int8=kv_int8)
 
 
-def generate_greedy(model, prompt, L, steps, max_seq, kv_int8=False, casts=True):
+def generate_greedy(model, prompt, L, steps, max_seq, kv_int8=False, casts=True, window=0):
     """Prefill the prompt, then `steps` cached decode steps, greedy (argmax).
 
     Returns (tokens generated: steps + 1 of them, list of logits per call:
     the prefill's last position then one per decode step, the cache).
     """
-    r = forward(model, prompt, L, cache=Cache(model.shape, max_seq, kv_int8), casts=casts)
+    r = forward(model, prompt, L, cache=Cache(model.shape, max_seq, kv_int8, window), casts=casts)
     cache = r["cache"]
     logits = [r["logits"]]
     toks = [int(np.argmax(r["logits"]))]

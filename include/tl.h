@@ -61,11 +61,18 @@ typedef struct {
   int32_t group_size;   /* INT4 scale group along K; must be 128 */
   float rope_base;      /* rotary base, e.g. 10000 */
   float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
-  int32_t max_seq;      /* KV rows per lane and effective layer */
+  int32_t max_seq;      /* positions per lane (KV rows per lane and layer unless windowed) */
   int32_t max_loops;    /* largest L; KV layers per lane = n_pre + max_loops */
   int32_t n_lanes;      /* independent sequences (each with its own L and KV) */
   int32_t kv_dtype;     /* tl_kv_dtype */
   int32_t max_tokens;   /* largest token count of one tl_prefill call */
+  /* Sliding-window cache ("Performance and Memory" page, "Sliding-Window
+   * Cache"): 0 keeps the full cache; W > 0 keeps only the last W cached
+   * tokens, i.e. a query at position q attends to positions q-W+1 .. q. The
+   * cache then holds a ring of min(max_seq, W + max_tokens) rows per lane,
+   * layer and head (position p in row p mod that), so KV memory no longer
+   * grows with max_seq; positions still run up to max_seq. */
+  int32_t cache_window;
 } tl_config;
 
 /* One INT4 linear layer in the canonical layout (device pointers):
@@ -103,10 +110,14 @@ typedef struct tl_ctx tl_ctx;
  * Independent of max_loops: the loop block is stored once however many
  * times it runs. */
 size_t tl_weights_ws_bytes(const tl_config* cfg);
-/* K and V of one lane for one effective layer:
- *   FP16: 2 * max_seq * n_heads * head_dim * 2
- *   INT8: 2 * max_seq * n_heads * (head_dim + 2)   (codes + one fp16 scale
- *         per token and head, "Performance and Memory" page, INT8-KV). */
+/* K and V of one lane for one effective layer, with R = max_seq rows (or,
+ * with cache_window W > 0, R = min(max_seq, W + max_tokens) ring rows):
+ *   FP16: 2 * R * n_heads * head_dim * 2
+ *   INT8: 2 * R * n_heads * (head_dim + 2)   (codes + one fp16 scale
+ *         per token and head, "Performance and Memory" page, INT8-KV).
+ * Layout per layer: K then V planes [n_heads][R][head_dim] (INT8: codes, then
+ * fp16 scales [n_heads][R]); position p lives in row p (p mod R with a
+ * window). 0 for an invalid config. */
 size_t tl_kv_layer_bytes(const tl_config* cfg);
 /* n_lanes * (n_pre + max_loops) * tl_kv_layer_bytes. */
 size_t tl_kv_bytes(const tl_config* cfg);

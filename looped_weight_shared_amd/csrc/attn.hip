@@ -31,16 +31,16 @@ struct CachePtrs {
 
 __device__ __forceinline__ CachePtrs cache_ptrs(const KvGeom& kv, int lane, int layer, int h) {
   const uint8_t* base = kv.base + ((size_t)lane * kv.n_layers + layer) * kv.layer_bytes;
-  const size_t HS = (size_t)kv.H * kv.S;
+  const size_t HS = (size_t)kv.H * kv.cap;
   CachePtrs c;
   if (kv.int8) {
-    c.k = base + (size_t)h * kv.S * kv.hd;
-    c.ks = reinterpret_cast<const uint16_t*>(base + HS * kv.hd) + (size_t)h * kv.S;
-    c.v = base + HS * kv.hd + HS * 2 + (size_t)h * kv.S * kv.hd;
-    c.vs = reinterpret_cast<const uint16_t*>(base + 2 * HS * kv.hd + HS * 2) + (size_t)h * kv.S;
+    c.k = base + (size_t)h * kv.cap * kv.hd;
+    c.ks = reinterpret_cast<const uint16_t*>(base + HS * kv.hd) + (size_t)h * kv.cap;
+    c.v = base + HS * kv.hd + HS * 2 + (size_t)h * kv.cap * kv.hd;
+    c.vs = reinterpret_cast<const uint16_t*>(base + 2 * HS * kv.hd + HS * 2) + (size_t)h * kv.cap;
   } else {
-    c.k = base + (size_t)h * kv.S * kv.hd * 2;
-    c.v = base + HS * kv.hd * 2 + (size_t)h * kv.S * kv.hd * 2;
+    c.k = base + (size_t)h * kv.cap * kv.hd * 2;
+    c.v = base + HS * kv.hd * 2 + (size_t)h * kv.cap * kv.hd * 2;
     c.ks = c.vs = nullptr;
   }
   return c;
@@ -88,10 +88,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * 64;
   const int d = kv.H * HD;
-  const int kend = p0 + min(q0 + 64, M);  // keys [0, kend) can be visible to this block
+  const int kend = p0 + min(q0 + 64, M);  // keys [kbeg, kend) can be visible to this block
+  const int kbeg = kv_first(kv, p0 + q0);  // the window of the block's first query
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const float scale = 1.0f / sqrtf((float)HD);
   const int nkt = (kend + KT - 1) / KT;
+  const int kt0 = kbeg / KT;
 
   Raw kreg[CPT], vreg[CPT];
   uint32_t kscr = 0, vscr = 0;  // raw fp16 scales (INT8), threads < 64
@@ -100,14 +102,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const size_t roff = (size_t)min(kt * KT + kr, kend - 1) * HD * (I8 ? 1 : 2) + d0 * (I8 ? 1 : 2);
+      const int key = min(max(kt * KT + kr, kbeg), kend - 1);
+      const size_t roff = (size_t)kv_slot(kv, key) * HD * (I8 ? 1 : 2) + d0 * (I8 ? 1 : 2);
       kreg[i] = *reinterpret_cast<const Raw*>(cp.k + roff);
       vreg[i] = *reinterpret_cast<const Raw*>(cp.v + roff);
     }
     if constexpr (I8) {
-      const int key = min(kt * KT + (tid & (KT - 1)), kend - 1);
-      kscr = cp.ks[key];
-      vscr = cp.vs[key];
+      const int key = min(max(kt * KT + (tid & (KT - 1)), kbeg), kend - 1);
+      kscr = cp.ks[kv_slot(kv, key)];
+      vscr = cp.vs[kv_slot(kv, key)];
     }
   };
   auto to_f16 = [&](const Raw& r) -> half8_t {
@@ -129,14 +132,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const bool ok = kt * KT + kr < kend;
+      const bool ok = kt * KT + kr < kend && kt * KT + kr >= kbeg;
       *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
       const half8_t vh = ok ? to_f16(vreg[i]) : hz;
 #pragma unroll
       for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + 8 * ((kr >> 3) ^ ((d0 >> 3) & (NC - 1))) + (kr & 7)] = vh[j];
     }
     if (tid < KT) {
-      const bool ok = kt * KT + tid < kend;
+      const bool ok = kt * KT + tid < kend && kt * KT + tid >= kbeg;
       float a = 1.f, b = 1.f;
       if constexpr (I8) {
         a = ok ? h2f((uint16_t)kscr) : 0.f;
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     }
   };
 
-  load_tile(0);
+  load_tile(kt0);
   // Q fragments (A operand of S): row q0 + 16*wave + l16, dims 32s + 8lq .. +7
   half8_t qf[KS];
   {
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
   for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
   const int qpos_base = p0 + q0 + 16 * wave + 4 * lq;  // + r
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = kt0; kt < nkt; ++kt) {
     const int key0 = kt * KT;
     store_tile(kt);
     attn_lds_barrier();
@@ -190,7 +193,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
       const int key = key0 + kb * 16 + l16;
       const float ks = ksc[kb * 16 + l16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[kb][r] = (key <= qpos_base + r) ? t[r] * ks : -INFINITY;
+      for (int r = 0; r < 4; ++r)
+        sv[kb][r] = (key <= qpos_base + r && key >= kv_first(kv, qpos_base + r)) ? t[r] * ks : -INFINITY;
     }
     // ---- online softmax per row
 #pragma unroll
@@ -304,9 +308,9 @@ size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S) {
 
 int attn_decode_np_max(int S) { return (S + kDecPart - 1) / kDecPart; }
 
-int attn_decode_parts(int M, const RowMap& rm) {
+int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv) {
   int maxctx = 0;
-  for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1);
+  for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1 - kv_first(kv, rm.row_pos[m]));
   return (maxctx + kDecPart - 1) / kDecPart;
 }
 
@@ -321,8 +325,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   __shared__ float red_o[kDecWaves][HD];
   __shared__ float red_m[kDecWaves], red_l[kDecWaves];
   const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
-  const int pos = rm.row_pos[m], ctx = pos + 1;
-  const int nparts = (ctx + kDecPart - 1) / kDecPart;
+  const int pos = rm.row_pos[m];
+  const int kbeg = kv_first(kv, pos);  // keys kbeg .. pos are visible
+  const int nparts = (pos + 1 - kbeg + kDecPart - 1) / kDecPart;
   float* dst = part + ((size_t)(m * kv.H + h) * np_max + bp) * (HD + kAttnPartExtra);
   if (bp >= nparts) {  // beyond this row's context: an empty part
     if (threadIdx.x == 0) {
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   const int lane_id = rm.row_lane[m];
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const int rowb = I8 ? HD : 2 * HD;
-  const int k0 = (bp * kDecWaves + wave) * kDecChunk;
+  const int k0 = kbeg + (bp * kDecWaves + wave) * kDecChunk;
   const bool active = k0 <= pos;
 
   // ---- 1. projections of this row (8 dims + their RoPE partners) and cos/sin
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   uint32_t ksr[I8 ? NP : 1], vsr[I8 ? NP : 1];  // raw fp16 scales
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int key = max(min(k0 + p * KPP + kg, pos - 1), 0);
+    const int key = kv_slot(kv, max(min(k0 + p * KPP + kg, pos - 1), kbeg));
     kr[p] = *reinterpret_cast<const Row*>(cp.k + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
     vr[p] = *reinterpret_cast<const Row*>(cp.v + (size_t)key * rowb + d0 * (I8 ? 1 : 2));
     if constexpr (I8) {
@@ -423,13 +428,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
         vw[j >> 2] |= ((uint32_t)(qvv & 0xFF)) << (8 * (j & 3));
       }
       if (writer) {
-        uint8_t* K = const_cast<uint8_t*>(cp.k) + (size_t)pos * rowb + d0;
-        uint8_t* V = const_cast<uint8_t*>(cp.v) + (size_t)pos * rowb + d0;
+        const int ps = kv_slot(kv, pos);
+        uint8_t* K = const_cast<uint8_t*>(cp.k) + (size_t)ps * rowb + d0;
+        uint8_t* V = const_cast<uint8_t*>(cp.v) + (size_t)ps * rowb + d0;
         *reinterpret_cast<uint2*>(K) = make_uint2(kw[0], kw[1]);
         *reinterpret_cast<uint2*>(V) = make_uint2(vw[0], vw[1]);
         if (sub == 0) {
-          const_cast<uint16_t*>(cp.ks)[pos] = __builtin_bit_cast(uint16_t, s16k);
-          const_cast<uint16_t*>(cp.vs)[pos] = __builtin_bit_cast(uint16_t, s16v);
+          const_cast<uint16_t*>(cp.ks)[ps] = __builtin_bit_cast(uint16_t, s16k);
+          const_cast<uint16_t*>(cp.vs)[ps] = __builtin_bit_cast(uint16_t, s16v);
         }
       }
     } else {
@@ -442,8 +448,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
         vn[j] = (float)vf[j];
       }
       if (writer) {
-        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.k) + (size_t)pos * rowb + d0 * 2) = kh8;
-        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.v) + (size_t)pos * rowb + d0 * 2) = vh8;
+        const int ps = kv_slot(kv, pos);
+        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.k) + (size_t)ps * rowb + d0 * 2) = kh8;
+        *reinterpret_cast<half8_t*>(const_cast<uint8_t*>(cp.v) + (size_t)ps * rowb + d0 * 2) = vh8;
       }
     }
   }
@@ -568,7 +575,7 @@ static void decode_launch(dim3 grid, const float* qkv, const RowMap& rm, const f
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s) {
   const int np_max = attn_decode_np_max(kv.S);
-  dim3 grid(attn_decode_parts(M, rm), kv.H, M);
+  dim3 grid(attn_decode_parts(M, rm, kv), kv.H, M);
   if (kv.hd == 128 && kv.int8)
     decode_launch<128, true>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 128)

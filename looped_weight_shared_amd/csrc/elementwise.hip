@@ -223,8 +223,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     qout[(size_t)m * d + h * hd + ln + half] = __builtin_bit_cast(uint16_t, Q2);
   }
   uint8_t* base = kv.base + ((size_t)lane * kv.n_layers + layer) * kv.layer_bytes;
-  const size_t HS = (size_t)kv.H * kv.S;
-  const size_t rowi = (size_t)h * kv.S + pos;
+  const size_t HS = (size_t)kv.H * kv.cap;
+  const size_t rowi = (size_t)h * kv.cap + kv_slot(kv, pos);
   if (!kv.int8) {
     uint16_t* K = reinterpret_cast<uint16_t*>(base) + rowi * hd;
     uint16_t* V = reinterpret_cast<uint16_t*>(base) + HS * hd + rowi * hd;

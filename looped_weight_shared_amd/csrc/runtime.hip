@@ -61,6 +61,7 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->max_loops < 1 || c->max_loops > 64) return *why = "max_loops must be in 1..64", false;
   if (c->n_lanes < 1 || c->n_lanes > 8) return *why = "n_lanes must be in 1..8", false;
   if (c->max_seq < 1 || c->max_tokens < 1) return *why = "max_seq and max_tokens must be >= 1", false;
+  if (c->cache_window < 0) return *why = "cache_window must be >= 0", false;
   *st = TL_OK;
   return true;
 }
@@ -69,6 +70,13 @@ size_t block_bytes(const tl_config* c) {
   const int d = c->d_model, f = c->ffn_dim;
   return al256(tl::packed_bytes(3 * d, d)) + al256(tl::packed_bytes(d, d)) + al256(tl::packed_bytes(2 * f, d)) +
          al256(tl::packed_bytes(d, f));
+}
+// Cache rows per (lane, layer, head): max_seq, or with a window W a ring of
+// W + max_tokens rows (a prefill chunk never overwrites a row one of its own
+// queries still sees) when that is shorter.
+int kv_rows(const tl_config* c) {
+  if (c->cache_window <= 0) return c->max_seq;
+  return (int)std::min<long long>(c->max_seq, (long long)c->cache_window + c->max_tokens);
 }
 size_t rope_bytes(const tl_config* c) { return al256((size_t)2 * c->max_seq * (c->head_dim / 2) * 4); }
 
@@ -251,7 +259,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
     }
     // RoPE, new K/V into cache layer `layer`, single-query attention in key
     // parts; the O projection merges the parts itself when its GEMV can
-    tl::ASrc att{nullptr, nullptr, nullptr, 0.f, c->part, tl::attn_decode_parts(M, rm),
+    tl::ASrc att{nullptr, nullptr, nullptr, 0.f, c->part, tl::attn_decode_parts(M, rm, c->kv),
                  tl::attn_decode_np_max(c->cfg.max_seq), c->cfg.head_dim};
     const bool fuse = tl::gemv_supported(M, d, att);
     KScope k(c, TL_K_ATTN, s);
@@ -315,7 +323,7 @@ size_t tl_kv_layer_bytes(const tl_config* cfg) {
   tl_status st;
   std::string why;
   if (!check_cfg(cfg, &st, &why)) return 0;
-  const size_t rows = (size_t)cfg->max_seq * cfg->n_heads;
+  const size_t rows = (size_t)kv_rows(cfg) * cfg->n_heads;
   if (cfg->kv_dtype == TL_KV_INT8) return 2 * rows * (cfg->head_dim + 2);
   return 2 * rows * cfg->head_dim * 2;
 }
@@ -437,6 +445,8 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->kv.H = cfg->n_heads;
   c->kv.hd = cfg->head_dim;
   c->kv.S = cfg->max_seq;
+  c->kv.cap = kv_rows(cfg);
+  c->kv.window = cfg->cache_window;
   c->kv.int8 = cfg->kv_dtype == TL_KV_INT8;
   const ActLayout L = act_layout(cfg);
   uint8_t* ab = static_cast<uint8_t*>(d_act_ws);

@@ -59,9 +59,17 @@ struct KvGeom {
   uint8_t* base;        // start of all caches
   size_t layer_bytes;   // one lane, one layer
   int n_layers;         // layers per lane
-  int H, hd, S;         // heads, head_dim, max_seq
+  int H, hd, S;         // heads, head_dim, max_seq (positions; RoPE table rows)
   int int8;
+  int cap;              // cache rows per (lane, layer, head): S, or the window's ring
+  int window;           // 0: full cache; W: queries see the last W positions
 };
+// Cache row of position pos (a ring when windowed) and the first position
+// a query at pos sees.
+__host__ __device__ inline int kv_slot(const KvGeom& kv, int pos) { return kv.window ? pos % kv.cap : pos; }
+__host__ __device__ inline int kv_first(const KvGeom& kv, int pos) {
+  return kv.window ? (pos - kv.window + 1 > 0 ? pos - kv.window + 1 : 0) : 0;
+}
 
 // Epilogue of the W4 matrix kernels.
 //   STORE / RESID: fp32 out[m*ldo + n] = / += v;
@@ -156,7 +164,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 // floats). With o non-null the parts are also merged into O fp16 [M][d];
 // otherwise the O projection merges them (ASrc::att).
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
-int attn_decode_parts(int M, const RowMap& rm);  // parts written per (row, head) this call
+int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv);  // parts written per (row, head) this call
 int attn_decode_np_max(int S);                  // part slots per (row, head)
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s);

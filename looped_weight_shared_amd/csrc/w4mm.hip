@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
   if (e.mode == EPI_QKV_ROPE) {
     const int hd = e.kv.hd, half = hd / 2, d = e.kv.H * hd;
     uint8_t* base = e.kv.base + ((size_t)e.lane * e.kv.n_layers + e.layer) * e.kv.layer_bytes;
-    const size_t HS = (size_t)e.kv.H * e.kv.S;
+    const size_t HS = (size_t)e.kv.H * e.kv.cap;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int n = min(nbw0 + j, NB - 1) * 16 + l16;
@@ -527,7 +527,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
             if (sec == 0)
               e.qout[(size_t)m * d + hh * hd + dim] = hv;
             else
-              reinterpret_cast<uint16_t*>(base)[(sec == 2 ? HS * hd : 0) + ((size_t)hh * e.kv.S + pos) * hd + dim] = hv;
+              reinterpret_cast<uint16_t*>(base)[(sec == 2 ? HS * hd : 0) +
+                                                ((size_t)hh * e.kv.cap + kv_slot(e.kv, pos)) * hd + dim] = hv;
           }
         }
     }

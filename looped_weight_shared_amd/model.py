@@ -19,13 +19,14 @@ from . import (TL_KV_FP16, TlBlock, TlConfig, TlQLinear, TlWeights, tl_act_ws_by
 _LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
-def make_config(shape, max_seq, max_loops, n_lanes=1, kv_dtype=TL_KV_FP16, max_tokens=None) -> TlConfig:
+def make_config(shape, max_seq, max_loops, n_lanes=1, kv_dtype=TL_KV_FP16, max_tokens=None,
+                cache_window=0) -> TlConfig:
     """TlConfig from a shape object with vocab/d_model/n_heads/... attributes."""
     return TlConfig(vocab=shape.vocab, d_model=shape.d_model, n_heads=shape.n_heads,
                     head_dim=shape.head_dim, ffn_dim=shape.ffn_dim, n_pre=shape.n_pre,
                     group_size=shape.group_size, rope_base=shape.rope_base, rms_eps=shape.rms_eps,
                     max_seq=max_seq, max_loops=max_loops, n_lanes=n_lanes, kv_dtype=kv_dtype,
-                    max_tokens=max_tokens or max_seq)
+                    max_tokens=max_tokens or max_seq, cache_window=cache_window)
 
 
 def device_bytes(nbytes: int, device="cuda") -> torch.Tensor:
@@ -48,9 +49,10 @@ class Model:
     """A tl_ctx over synthetic canonical weights (dict as produced by synth.make_weights)."""
 
     def __init__(self, weights: dict, max_seq: int, max_loops: int, n_lanes: int = 1,
-                 kv_dtype: int = TL_KV_FP16, max_tokens: int | None = None, device="cuda"):
+                 kv_dtype: int = TL_KV_FP16, max_tokens: int | None = None, device="cuda",
+                 cache_window: int = 0):
         self.shape = weights["shape"]
-        self.cfg = make_config(self.shape, max_seq, max_loops, n_lanes, kv_dtype, max_tokens)
+        self.cfg = make_config(self.shape, max_seq, max_loops, n_lanes, kv_dtype, max_tokens, cache_window)
         self.device = device
         keep = []
 

@@ -24,6 +24,8 @@ Sources (the TinyLoop documentation pages):
     recompute is the parity reference for cached decode.
   * Self-speculative decode ("Introduction" page, "What Makes It Different";
     "Current Status" page, speculative decode table): speculative.py.
+  * Per-iteration residual-norm safety check ("Current Status" page,
+    architecture-unique features table): safety.py.
 """
 from .int4 import pack_int4, unpack_int4, dequantize
 from .kvquant import kv_quantize, kv_dequantize, kv_cache_bytes
@@ -31,8 +33,9 @@ from .model import (OracleModel, Cache, rmsnorm, rope_cos_sin, apply_rope, atten
                     silu, fp16, forward, decode_step, generate_greedy, forward_uncached,
                     head_logits)
 from .speculative import speculative_greedy
+from .safety import safety_trip
 
 __all__ = ["pack_int4", "unpack_int4", "dequantize", "kv_quantize", "kv_dequantize",
            "kv_cache_bytes", "OracleModel", "Cache", "rmsnorm", "rope_cos_sin", "apply_rope",
            "attention", "silu", "fp16", "forward", "decode_step", "generate_greedy",
-           "forward_uncached", "head_logits", "speculative_greedy"]
+           "forward_uncached", "head_logits", "speculative_greedy", "safety_trip"]

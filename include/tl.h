@@ -49,7 +49,8 @@ typedef enum {
   TL_E_RANGE = 2,        /* L, token count or sequence length out of range */
   TL_E_STATE = 3,        /* call not valid in the lane's current state */
   TL_E_HIP = 4,          /* a HIP runtime call failed */
-  TL_E_UNSUPPORTED = 5   /* valid request this build does not implement */
+  TL_E_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  TL_E_SAFETY = 6        /* the residual-norm safety check tripped (tl_set_safety) */
 } tl_status;
 
 typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1 } tl_kv_dtype;
@@ -240,6 +241,26 @@ typedef struct {
 tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft_loops, int32_t k_draft,
                          int32_t n_new, int32_t* h_out, tl_spec_stats* stats, void* stream);
 
+/* ---- per-iteration safety check ----------------------------------------
+ * "Current Status" page, architecture-unique features table: the residual
+ * stream's L2 norm is checked after every loop iteration and the forward is
+ * stopped when it exceeds a threshold (L checkpoints per token). With
+ * max_norm > 0, tl_prefill, tl_decode_step and tl_spec_decode compute, after
+ * each loop iteration (not after pre-blocks), every row's ||x||_2 (x plus any
+ * pending split partials) in one small kernel, and at the end of the call
+ * read the first (iteration, row) whose norm is not <= max_norm (NaN trips
+ * too); if there is one the call returns TL_E_SAFETY. The call's work is
+ * complete when it reports (outputs written, lane length advanced, except
+ * that tl_spec_decode drops a tripped round), so the caller decides: reset
+ * the lane, lower L, or stop. Costs one launch per loop iteration plus one
+ * stream synchronisation per call; prefill graph replay is not used while
+ * it is on. max_norm 0 switches it off (the default).
+ * Errors: TL_E_INVAL (ctx NULL), TL_E_RANGE (max_norm < 0 or NaN). */
+tl_status tl_set_safety(tl_ctx* ctx, float max_norm);
+/* The last trip since tl_set_safety: loop iteration (0-based) and row (the
+ * call's row in prefill, the lane in decode), or -1, -1 if none. */
+tl_status tl_safety_last(const tl_ctx* ctx, int32_t* iteration, int32_t* row);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* tl_last_error(void);
 
@@ -255,7 +276,7 @@ const char* tl_last_error(void);
  * row scatter of decode hidden states; plain memory copies are not timed). */
 typedef enum {
   TL_K_EMBED = 0, TL_K_NORM, TL_K_QKV, TL_K_ROPE_KV, TL_K_ATTN, TL_K_O, TL_K_GATE_UP, TL_K_DOWN,
-  TL_K_HEAD, TL_K_ARGMAX, TL_K_COPY, TL_K_COUNT
+  TL_K_HEAD, TL_K_ARGMAX, TL_K_COPY, TL_K_SAFETY, TL_K_COUNT
 } tl_kernel_kind;
 /* Errors: TL_E_STATE if a window is already open, TL_E_RANGE for
  * max_launches outside 1..1000000, TL_E_HIP if events cannot be created. */

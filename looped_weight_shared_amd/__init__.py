@@ -19,7 +19,8 @@ import torch  # noqa: F401  (must precede the CDLL below)
 
 __all__ = [
     "TLError", "TlConfig", "TlQLinear", "TlBlock", "TlWeights", "lib", "LIB_PATH",
-    "TL_OK", "TL_E_INVAL", "TL_E_RANGE", "TL_E_STATE", "TL_E_HIP", "TL_E_UNSUPPORTED",
+    "TL_OK", "TL_E_INVAL", "TL_E_RANGE", "TL_E_STATE", "TL_E_HIP", "TL_E_UNSUPPORTED", "TL_E_SAFETY",
+    "tl_set_safety", "tl_safety_last",
     "TL_KV_FP16", "TL_KV_INT8",
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs", "tl_spec_decode", "TlSpecStats",
@@ -46,7 +47,7 @@ if len(_hip_runtimes()) > 1:
     raise ImportError("two HIP runtimes are mapped (libtl.so was loaded before torch): "
                       + ", ".join(_hip_runtimes()))
 
-TL_OK, TL_E_INVAL, TL_E_RANGE, TL_E_STATE, TL_E_HIP, TL_E_UNSUPPORTED = range(6)
+TL_OK, TL_E_INVAL, TL_E_RANGE, TL_E_STATE, TL_E_HIP, TL_E_UNSUPPORTED, TL_E_SAFETY = range(7)
 TL_KV_FP16, TL_KV_INT8 = 0, 1
 
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -93,6 +94,8 @@ _SIGS = {
     "tl_prefill": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
     "tl_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tl_set_graphs": (ctypes.c_int, [_vp, _i32]),
+    "tl_set_safety": (ctypes.c_int, [_vp, _f32]),
+    "tl_safety_last": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "tl_spec_decode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                       ctypes.POINTER(TlSpecStats), _vp]),
     "tl_last_error": (ctypes.c_char_p, []),
@@ -179,6 +182,17 @@ def tl_set_loops(ctx, lane: int, loops: int) -> None:
     _check(lib.tl_set_loops(ctx, lane, loops))
 
 
+def tl_set_safety(ctx, max_norm: float) -> None:
+    _check(lib.tl_set_safety(ctx, max_norm))
+
+
+def tl_safety_last(ctx):
+    """(iteration, row) of the last trip, or (-1, -1)."""
+    it, row = _i32(), _i32()
+    _check(lib.tl_safety_last(ctx, ctypes.byref(it), ctypes.byref(row)))
+    return it.value, row.value
+
+
 def tl_set_graphs(ctx, enable: bool) -> None:
     _check(lib.tl_set_graphs(ctx, 1 if enable else 0))
 
@@ -248,7 +262,8 @@ def tl_kv_quantize_rows(x, rows: int, hd: int, q, s, stream=None) -> None:
     _check(lib.tl_kv_quantize_rows(_ptr(x), rows, hd, _ptr(q), _ptr(s), _stream(stream)))
 
 
-KERNEL_KINDS = ("embed", "norm", "qkv", "rope_kv", "attn", "o", "gate_up", "down", "head", "argmax", "copy")
+KERNEL_KINDS = ("embed", "norm", "qkv", "rope_kv", "attn", "o", "gate_up", "down", "head", "argmax", "copy",
+                "safety")
 
 
 def tl_profile_begin(ctx, max_launches: int) -> None:

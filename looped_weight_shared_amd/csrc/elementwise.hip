@@ -508,6 +508,47 @@ hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, in
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ safety check
+// Residual L2 norm of each row (x plus any pending split partials, x itself
+// untouched); a row whose norm is not <= max_norm (NaN included) records
+// code_base + row with an atomic min, so the first (iteration, row) wins.
+__global__ __launch_bounds__(256) void safety_check_kernel(const float* __restrict__ x, Pending pend, int M, int d,
+                                                          float max_norm, int code_base, int* __restrict__ result) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)m * d;
+  float acc = 0.f;
+  for (int k = tid; k < d; k += 256) {
+    float v = xr[k];
+    if (pend.part)
+      for (int s = 0; s < pend.S; ++s) v += pend.part[((size_t)s * M + m) * d + k];
+    acc = fmaf(v, v, acc);
+  }
+  acc = wave_sum(acc);
+  if ((tid & 63) == 0) part[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const float nrm = sqrtf(part[0] + part[1] + part[2] + part[3]);
+    if (!(nrm <= max_norm)) atomicMin(result, code_base + m);
+  }
+}
+
+__global__ void safety_reset_kernel(int* result) {
+  if (threadIdx.x == 0) *result = 0x7fffffff;
+}
+
+hipError_t launch_safety_reset(int* result, hipStream_t s) {
+  launch(safety_reset_kernel, dim3(1), dim3(64), 0, s, result);
+  return hipGetLastError();
+}
+
+hipError_t launch_safety_check(const float* x, Pending pend, int M, int d, float max_norm, int code_base, int* result,
+                               hipStream_t s) {
+  if (M < 1) return hipSuccess;
+  launch(safety_check_kernel, dim3(M), dim3(256), 0, s, x, pend, M, d, max_norm, code_base, result);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ scatter
 __global__ void scatter_rows_kernel(const float* __restrict__ src, int d, RowMap rm, float* __restrict__ dst) {
   const int m = blockIdx.x;

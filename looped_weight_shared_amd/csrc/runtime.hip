@@ -101,7 +101,7 @@ constexpr int kSpecMaxDraft = 7;
 int head_rows_cap(const tl_config* c) { return std::max(c->n_lanes, kSpecMaxDraft + 1); }
 
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -120,6 +120,7 @@ ActLayout act_layout(const tl_config* c) {
   // speculative tokens: draft chain [kSpecMaxDraft + 2][n_lanes], verify
   // tokens and verifier argmaxes [kSpecMaxDraft + 1] each
   L.spec = off; off += al256(((size_t)(kSpecMaxDraft + 2) * c->n_lanes + 2 * (kSpecMaxDraft + 1)) * 4);
+  L.safety = off; off += al256(4);  // first tripped (iteration, row) code of the safety check
   L.total = off;
   return L;
 }
@@ -150,6 +151,11 @@ struct tl_ctx {
   int32_t* spec_chain;  // [kSpecMaxDraft + 2][n_lanes]
   int32_t* spec_ver;    // [kSpecMaxDraft + 1]
   int32_t* spec_next;   // [kSpecMaxDraft + 1]
+  // per-iteration residual-norm check (off while safety_max <= 0)
+  float safety_max = 0.f;
+  int* safety_res = nullptr;
+  int32_t safety_host = 0x7fffffff;
+  int safety_iter = -1, safety_row = -1;  // last trip reported
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
   int32_t spec_host[16];               // host side of the speculative token exchange
   // optional: prefill launch sequences captured as a HIP graph and replayed
@@ -463,6 +469,7 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->spec_chain = reinterpret_cast<int32_t*>(ab + L.spec);
   c->spec_ver = c->spec_chain + (size_t)(kSpecMaxDraft + 2) * cfg->n_lanes;
   c->spec_next = c->spec_ver + (kSpecMaxDraft + 1);
+  c->safety_res = reinterpret_cast<int*>(ab + L.safety);
   c->pend = tl::Pending{nullptr, 1};
   c->len.assign(cfg->n_lanes, 0);
   c->loops.assign(cfg->n_lanes, 1);
@@ -531,6 +538,11 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   rm.lane = lane;
   rm.p0 = p0;
   const int d = C.d_model;
+  const bool safe = ctx->safety_max > 0.f;
+  if (safe) {
+    KScope k(ctx, TL_K_SAFETY, s);
+    TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
+  }
   {
     KScope k(ctx, TL_K_EMBED, s);
     TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
@@ -539,6 +551,11 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
     const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
     st = run_layer(ctx, B, layer, n, rm, false, s);
     if (st != TL_OK) return st;
+    if (safe && layer >= C.n_pre) {
+      KScope k(ctx, TL_K_SAFETY, s);
+      TL_HIP(tl::launch_safety_check(ctx->x, ctx->pend, n, d, ctx->safety_max, (layer - C.n_pre) << tl::kSafetyRowBits,
+                                     ctx->safety_res, s));
+    }
   }
   st = resolve(ctx, n, s);
   if (st != TL_OK) return st;
@@ -565,6 +582,21 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   return TL_OK;
 }
 
+// Reads the safety check's result (one synchronisation of the stream). rows,
+// if given, maps a result row to the lane reported.
+tl_status safety_verdict(tl_ctx* ctx, hipStream_t s, const std::vector<int>* rows) {
+  hipError_t e = hipMemcpyAsync(&ctx->safety_host, ctx->safety_res, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(TL_E_HIP, std::string("reading the safety check: ") + hipGetErrorString(e));
+  const int code = ctx->safety_host;
+  if (code == 0x7fffffff) return TL_OK;
+  const int it = code >> tl::kSafetyRowBits, row = code & ((1 << tl::kSafetyRowBits) - 1);
+  ctx->safety_iter = it;
+  ctx->safety_row = rows ? (*rows)[row] : row;
+  return fail(TL_E_SAFETY, "residual norm above the safety threshold after loop iteration " + std::to_string(it) +
+                               (rows ? " on lane " : " on row ") + std::to_string(ctx->safety_row));
+}
+
 void drop_prefill_graph(tl_ctx* ctx) {
   if (ctx->pg.exec) {
     (void)hipEventSynchronize(ctx->pg_done);  // the last replay may still run
@@ -589,7 +621,7 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   const int L = ctx->loops[lane];
   if (p0 > 0 && C.n_pre + L > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!ctx->graphs || ctx->prof_on) {
+  if (!ctx->graphs || ctx->prof_on || ctx->safety_max > 0.f) {
     st = enqueue_prefill(ctx, lane, d_tokens, n, d_hidden, d_logits, d_next, p0, L, s);
     if (st != TL_OK) return st;
   } else {
@@ -629,6 +661,22 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   }
   ctx->len[lane] = p0 + n;
   ctx->depth[lane] = std::min(ctx->depth[lane], C.n_pre + L);
+  if (ctx->safety_max > 0.f) return safety_verdict(ctx, s, nullptr);
+  return TL_OK;
+}
+
+tl_status tl_set_safety(tl_ctx* ctx, float max_norm) {
+  if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
+  if (!(max_norm >= 0.f)) return fail(TL_E_RANGE, "max_norm must be >= 0 (0: off)");
+  ctx->safety_max = max_norm;
+  ctx->safety_iter = ctx->safety_row = -1;
+  return TL_OK;
+}
+
+tl_status tl_safety_last(const tl_ctx* ctx, int32_t* iteration, int32_t* row) {
+  if (!ctx || !iteration || !row) return fail(TL_E_INVAL, "NULL argument");
+  *iteration = ctx->safety_iter;
+  *row = ctx->safety_row;
   return TL_OK;
 }
 
@@ -663,6 +711,11 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int d = C.d_model;
+  const bool safe = ctx->safety_max > 0.f;
+  if (safe) {
+    KScope k(ctx, TL_K_SAFETY, s);
+    TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
+  }
   {
     KScope k(ctx, TL_K_EMBED, s);
     TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
@@ -674,6 +727,11 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
     const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
     tl_status st = run_layer(ctx, B, layer, Ml, rm, true, s);
     if (st != TL_OK) return st;
+    if (safe && layer >= C.n_pre) {
+      KScope k(ctx, TL_K_SAFETY, s);
+      TL_HIP(tl::launch_safety_check(ctx->x, ctx->pend, Ml, d, ctx->safety_max,
+                                     (layer - C.n_pre) << tl::kSafetyRowBits, ctx->safety_res, s));
+    }
   }
   if (d_logits || d_next) {
     float* lg = d_logits ? d_logits : ctx->logits;
@@ -694,6 +752,7 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
     ctx->len[l] += 1;
     ctx->depth[l] = std::min(ctx->depth[l], C.n_pre + ctx->loops[l]);
   }
+  if (safe) return safety_verdict(ctx, s, &rows);
   return TL_OK;
 }
 
@@ -762,6 +821,10 @@ tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft
     if (he != hipSuccess) {
       st = fail(TL_E_HIP, std::string("reading the verify tokens: ") + hipGetErrorString(he));
       break;
+    }
+    if (ctx->safety_max > 0.f) {  // the verify pass tripped the check: keep nothing of this round
+      st = safety_verdict(ctx, s, nullptr);
+      if (st != TL_OK) break;
     }
     int a = 0;
     while (a < k && hv[1 + a] == hv[8 + a]) ++a;

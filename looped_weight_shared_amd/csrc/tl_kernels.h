@@ -184,6 +184,13 @@ hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, in
 // dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
 
+// Per-iteration residual-norm check: result = min(result, code_base + m) for
+// each row m of x (+ pending partials) whose L2 norm is not <= max_norm.
+constexpr int kSafetyRowBits = 20;  // code = iteration << kSafetyRowBits | row
+hipError_t launch_safety_reset(int* result, hipStream_t s);
+hipError_t launch_safety_check(const float* x, Pending pend, int M, int d, float max_norm, int code_base, int* result,
+                               hipStream_t s);
+
 hipError_t launch_kv_quantize_rows(const uint16_t* x, int rows, int hd, int8_t* q, uint16_t* sc,
                                    hipStream_t s);
 

@@ -14,7 +14,7 @@ import torch
 
 from . import (TL_KV_FP16, TlBlock, TlConfig, TlQLinear, TlWeights, tl_act_ws_bytes, tl_create,
                tl_decode_step, tl_destroy, tl_get_loops, tl_kv_bytes, tl_length, tl_prefill, tl_reset,
-               tl_set_graphs, tl_set_loops, tl_spec_decode, tl_weights_ws_bytes)
+               tl_safety_last, tl_set_graphs, tl_set_loops, tl_set_safety, tl_spec_decode, tl_weights_ws_bytes)
 
 _LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
@@ -85,6 +85,12 @@ class Model:
     # -- forwarding -------------------------------------------------------
     def set_loops(self, lane, loops):
         tl_set_loops(self.ctx, lane, loops)
+
+    def set_safety(self, max_norm: float):
+        tl_set_safety(self.ctx, max_norm)
+
+    def safety_last(self):
+        return tl_safety_last(self.ctx)
 
     def set_graphs(self, enable: bool):
         tl_set_graphs(self.ctx, enable)

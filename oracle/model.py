@@ -137,11 +137,17 @@ class Cache:
     depth[t] is the number of effective layers token t was computed through.
     """
 
-    def __init__(self, shape, max_seq, kv_int8=False, window=0):
+    def __init__(self, shape, max_seq, kv_int8=False, window=0, store_h=False):
         self.shape = shape
         self.max_seq = max_seq
         self.kv_int8 = kv_int8
         self.window = window  # cache_window: > 0 keeps only the last `window` tokens visible
+        # store-h: keep the block's normed input h per position instead of K/V
+        # and rebuild K, V from it with the block's own W_k, W_v when read
+        self.store_h = store_h
+        if store_h and kv_int8:
+            raise ValueError("store-h keeps FP16 h rows; INT8 K/V does not apply")
+        self.h = {}
         self.length = 0
         self.k, self.v = {}, {}
         self.kq, self.ks, self.vq, self.vs = {}, {}, {}, {}
@@ -167,6 +173,11 @@ class Cache:
     def read(self, layer, upto):
         return self.k[layer][:upto], self.v[layer][:upto]
 
+    def write_h(self, layer, pos, h):
+        if layer not in self.h:
+            self.h[layer] = np.zeros((self.max_seq, self.shape.d_model), dtype=np.float64)
+        self.h[layer][pos] = h
+
 
 def _block_forward(x, B, cache, layer, positions, s, casts):
     """One pre-norm block on residual rows x [n][d] at absolute positions."""
@@ -179,6 +190,22 @@ def _block_forward(x, B, cache, layer, positions, s, casts):
     v = (h @ B["wv"].T).reshape(n, H, hd)
     cos, sin = rope_cos_sin(positions, hd, s.rope_base)
     Q, K, V = c(apply_rope(q, cos, sin)), c(apply_rope(k, cos, sin)), c(v)
+    if cache.store_h:
+        # store-h ("Current Status" page, KV-cache table; "Claims & Data
+        # Sources": h-mode KV reconstruction from the shared W_k / W_v): the
+        # cache keeps h; K and V of every visible position are rebuilt from it
+        upto = int(positions[-1]) + 1
+        cache.write_h(layer, positions, h)
+        hall = cache.h[layer][:upto]
+        ka = (hall @ B["wk"].T).reshape(upto, H, hd)
+        va = (hall @ B["wv"].T).reshape(upto, H, hd)
+        ca, sa = rope_cos_sin(np.arange(upto), hd, s.rope_base)
+        Kall, Vall = c(apply_rope(ka, ca, sa)), c(va)
+        O = c(attention(Q, Kall, Vall, positions, cache.window)).reshape(n, H * hd)
+        x = x + O @ B["wo"].T
+        h2 = c(rmsnorm(x, B["mlp_norm"], s.rms_eps))
+        a = c(silu(h2 @ B["w_gate"].T) * (h2 @ B["w_up"].T))
+        return x + a @ B["w_down"].T
     if cache.kv_int8:
         if not casts:
             raise ValueError("INT8 KV quantizes FP16 rows; it needs the FP16 cast points")
@@ -204,7 +231,7 @@ def head_logits(model, x_rows, casts=True):
 
 
 def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False,
-            max_seq=None, kv_int8=False, window=0):
+            max_seq=None, kv_int8=False, window=0, store_h=False):
     """Append `tokens` to a lane at its current length and run all n_pre + L layers.
 
     Returns a dict with the final residual rows 'hidden' [n][d] (before the
@@ -217,7 +244,7 @@ def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False
     if L < 1:
         raise ValueError("L must be >= 1")
     if cache is None:
-        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8, window=window)
+        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8, window=window, store_h=store_h)
     p0 = cache.length
     if p0 + n > cache.max_seq:
         raise ValueError("sequence exceeds max_seq")

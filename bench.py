@@ -84,7 +84,7 @@ def _pmc_dispatches(d, counter):
 
 def ingest_pmc(fetch_dir, write_dir, copy_mib):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --decode-steps 4 --copy-mib <copy_mib>`, one with
+    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --decode-steps 4 --copy-mib <copy_mib>`, one with
     FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
     for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
@@ -113,7 +113,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
                          tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --decode-steps 4 --copy-mib %d" % copy_mib
+    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --decode-steps 4 --copy-mib %d" % copy_mib
     data = {"commands": [
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,
@@ -152,6 +152,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
+    ap.add_argument("--no-storeh", action="store_true", help="skip the store-h (TL_KV_H16) leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -172,6 +173,7 @@ def main():
 
     import synth
     import looped_weight_shared_amd as tl
+    from looped_weight_shared_amd import model as mod
     from looped_weight_shared_amd.model import Model
 
     torch.cuda.set_device(0)
@@ -303,13 +305,51 @@ def main():
             m.prefill(ptoks, next_tok=bufs[0])
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            toks, st = m.spec_decode(t_first, D, draft_loops=2, k_draft=kd)
+            _, st = m.spec_decode(t_first, D, draft_loops=2, k_draft=kd)
             dt = time.perf_counter() - t0
             spec[f"k{kd}"] = {"ms_per_token": round(dt * 1e3 / D, 4), "rounds": st.rounds,
                               "drafted": st.drafted, "accepted": st.accepted,
                               "speedup_vs_plain": round(ms_tok / (dt * 1e3 / D), 3)}
             print(f"[bench] spec decode draft L=2 verify L={L} k={kd}: {dt * 1e3 / D:.4f} ms/token, "
                   f"accepted {st.accepted}/{st.drafted}", file=sys.stderr, flush=True)
+        # ------------------------------------------------------------ store-h cache
+        # same prompt/steps with h kept per position and K/V rebuilt per layer
+        if not args.no_storeh:
+            mh = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=tl.TL_KV_H16,
+                       max_tokens=max(SEQ, args.prompt))
+            mh.set_loops(0, L)
+
+            def prefill_h():
+                mh.reset(0)
+                mh.prefill(toks)
+            for _ in range(3):
+                prefill_h()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                prefill_h()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_pre_h = e0.elapsed_time(e1) / 10
+            mh.reset(0)
+            mh.prefill(ptoks, next_tok=bufs[0])
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for t in range(D):
+                mh.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_tok_h = e0.elapsed_time(e1) / D
+            kvb = {k: tl.tl_kv_layer_bytes(mod.make_config(s, 2048, L, kv_dtype=v))
+                   for k, v in (("fp16", tl.TL_KV_FP16), ("h16", tl.TL_KV_H16))}
+            mh.close()
+            out["store_h"] = {"kv_bytes_per_lane_layer": kvb, "kv_saving": round(1 - kvb["h16"] / kvb["fp16"], 3),
+                              "prefill_ms_seq128": round(ms_pre_h, 4), "decode_ms_per_token": round(ms_tok_h, 4),
+                              "note": "prefill bit-identical to FP16 K/V; decode rebuilds K/V of the context every layer"}
+            print(f"[bench] store-h: prefill {ms_pre_h:.3f} ms/step, decode {ms_tok_h:.4f} ms/token, "
+                  f"KV bytes {kvb['h16']} vs {kvb['fp16']}", file=sys.stderr, flush=True)
+
         if spec:
             out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
                                   "note": "greedy; acceptance is a property of the weights (synthetic here)",

@@ -53,7 +53,17 @@ typedef enum {
   TL_E_SAFETY = 6        /* the residual-norm safety check tripped (tl_set_safety) */
 } tl_status;
 
-typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1 } tl_kv_dtype;
+/* TL_KV_H16 (store-h: "Current Status" page, KV-cache table; "Claims & Data
+ * Sources": h-mode KV reconstruction from the shared W_k / W_v): each layer's
+ * cache keeps the block's normed attention input h = fp16(RMSNorm(x)) per
+ * position, half the bytes of FP16 K and V; every call rebuilds K and V of
+ * the visible positions with the block's own W_k, W_v (one W4 GEMM per
+ * layer, RoPE in its epilogue) into a one-layer FP16 scratch that attention
+ * then reads. Prefill results are bit-identical to TL_KV_FP16 (the same
+ * GEMM arithmetic produces K and V either way); decode differs from it only
+ * in rounding (its stored K/V rows come from the decode GEMV there). Not
+ * combinable with cache_window. */
+typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1, TL_KV_H16 = 2 } tl_kv_dtype;
 
 /* Model shape and runtime limits. */
 typedef struct {
@@ -116,6 +126,7 @@ size_t tl_weights_ws_bytes(const tl_config* cfg);
  *   FP16: 2 * R * n_heads * head_dim * 2
  *   INT8: 2 * R * n_heads * (head_dim + 2)   (codes + one fp16 scale
  *         per token and head, "Performance and Memory" page, INT8-KV).
+ *   H16:  max_seq * d_model * 2               (h rows [max_seq][d_model]).
  * Layout per layer: K then V planes [n_heads][R][head_dim] (INT8: codes, then
  * fp16 scales [n_heads][R]); position p lives in row p (p mod R with a
  * window). 0 for an invalid config. */

@@ -508,6 +508,25 @@ hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, in
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ store-h rows
+// h row m (fp16 [d]) -> the h cache of its lane and layer at its position.
+__global__ void store_h_kernel(const uint16_t* __restrict__ h, int d, RowMap rm, uint8_t* __restrict__ base,
+                               size_t layer_bytes, int n_layers, int layer) {
+  const int m = blockIdx.x;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(base + ((size_t)row_lane(rm, m) * n_layers + layer) * layer_bytes) +
+                  (size_t)row_pos(rm, m) * d;
+  const uint4* src4 = reinterpret_cast<const uint4*>(h + (size_t)m * d);
+  uint4* dst4 = reinterpret_cast<uint4*>(dst);
+  for (int k = threadIdx.x; k < d / 8; k += blockDim.x) dst4[k] = src4[k];
+}
+
+hipError_t launch_store_h(const uint16_t* h, int M, int d, const RowMap& rm, uint8_t* base, size_t layer_bytes,
+                          int n_layers, int layer, hipStream_t s) {
+  if (d % 8) return hipErrorInvalidValue;
+  launch(store_h_kernel, dim3(M), dim3(256), 0, s, h, d, rm, base, layer_bytes, n_layers, layer);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ safety check
 // Residual L2 norm of each row (x plus any pending split partials, x itself
 // untouched); a row whose norm is not <= max_norm (NaN included) records

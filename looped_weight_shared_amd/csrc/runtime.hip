@@ -55,13 +55,18 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->d_model > 2048) return *why = "d_model must be <= 2048 (one residual row per 256 threads in registers)", false;
   if (c->group_size != 128) return *why = "group_size must be 128", false;
   if (c->vocab < 1 || c->n_pre < 0) return *why = "vocab < 1 or n_pre < 0", false;
-  if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8) return *why = "bad kv_dtype", false;
+  if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8 && c->kv_dtype != TL_KV_H16)
+    return *why = "bad kv_dtype", false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return *why = "bad rms_eps or rope_base", false;
   *st = TL_E_RANGE;
   if (c->max_loops < 1 || c->max_loops > 64) return *why = "max_loops must be in 1..64", false;
   if (c->n_lanes < 1 || c->n_lanes > 8) return *why = "n_lanes must be in 1..8", false;
   if (c->max_seq < 1 || c->max_tokens < 1) return *why = "max_seq and max_tokens must be >= 1", false;
   if (c->cache_window < 0) return *why = "cache_window must be >= 0", false;
+  if (c->kv_dtype == TL_KV_H16 && c->cache_window > 0) {
+    *st = TL_E_UNSUPPORTED;
+    return *why = "store-h (TL_KV_H16) does not combine with cache_window", false;
+  }
   *st = TL_OK;
   return true;
 }
@@ -101,7 +106,7 @@ constexpr int kSpecMaxDraft = 7;
 int head_rows_cap(const tl_config* c) { return std::max(c->n_lanes, kSpecMaxDraft + 1); }
 
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, hkv, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -121,6 +126,9 @@ ActLayout act_layout(const tl_config* c) {
   // tokens and verifier argmaxes [kSpecMaxDraft + 1] each
   L.spec = off; off += al256(((size_t)(kSpecMaxDraft + 2) * c->n_lanes + 2 * (kSpecMaxDraft + 1)) * 4);
   L.safety = off; off += al256(4);  // first tripped (iteration, row) code of the safety check
+  // store-h: K/V rebuilt for one layer, FP16 [lane][K|V][H][max_seq][hd]
+  L.hkv = off;
+  if (c->kv_dtype == TL_KV_H16) off += al256((size_t)c->n_lanes * 2 * c->max_seq * c->d_model * 2);
   L.total = off;
   return L;
 }
@@ -151,6 +159,11 @@ struct tl_ctx {
   int32_t* spec_chain;  // [kSpecMaxDraft + 2][n_lanes]
   int32_t* spec_ver;    // [kSpecMaxDraft + 1]
   int32_t* spec_next;   // [kSpecMaxDraft + 1]
+  // store-h: h cache [lane][layer][max_seq][d] (in d_kv); kv then describes the scratch
+  bool hmode = false;
+  uint8_t* hc_base = nullptr;
+  size_t hc_layer_bytes = 0;
+  int hc_layers = 0;
   // per-iteration residual-norm check (off while safety_max <= 0)
   float safety_max = 0.f;
   int* safety_res = nullptr;
@@ -197,9 +210,9 @@ struct KScope {
 
 // Decode-shaped calls (M <= 8) use the split-K-in-block GEMV with the RMSNorm
 // fused; larger M uses the MFMA GEMM, whose K-split partials (if the plan
-// splits) are left for the consumer: *S_out receives the split count. An
-// unsplit GEMM uses *gemm_epi instead of e when one is given (*used_gemm_epi
-// tells whether it did).
+// splits) are left for the consumer: *S_out receives the split count. The
+// GEMM uses *gemm_epi instead of e when one is given (an epilogue that needs
+// K unsplit: the plan then never splits); *used_gemm_epi tells whether it did.
 tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, int M, const tl::Epi& e,
                  int* S_out, hipStream_t s, const tl::Epi* gemm_epi = nullptr, bool* used_gemm_epi = nullptr) {
   *S_out = 1;
@@ -220,8 +233,8 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
     c->pend = tl::Pending{nullptr, 1};
     A = c->h;
   }
-  const int S = tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
-  const bool alt = gemm_epi && S == 1;
+  const bool alt = gemm_epi != nullptr;
+  const int S = alt ? 1 : tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
   KScope k(c, kind, s);
   TL_HIP(tl::launch_w4_gemm(w, A, M, alt ? *gemm_epi : e, c->gpart, s));
   *S_out = S;
@@ -231,12 +244,80 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
 
 // One effective layer over M rows (prefill rows of one lane, or the first M
 // decode rows).
+// Store-h attention input of one layer (TL_KV_H16; "Current Status" page,
+// KV-cache table: Store-h; "Claims & Data Sources": h-mode KV reconstruction
+// from the shared W_k / W_v):
+//   1. h = fp16(RMSNorm(x)) (pending split partials summed), each row also
+//      stored at its position in its lane's h cache for this layer;
+//   2. prefill: Q = fp16(RoPE(h W_q^T)) by the Q section of the packed QKV
+//      (GEMM, RoPE epilogue); decode: q, k, v of the new rows (GEMV) for the
+//      decode attention, which rotates them itself;
+//   3. K, V of the lane's positions 0 .. end-1 (prefill: through the new
+//      rows; decode: the cached ones) rebuilt from the h cache by the K/V
+//      section (GEMM with the RoPE epilogue, K never split) into the scratch
+//      that c->kv describes, one slot per lane.
+tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowMap& rm, bool decode, hipStream_t s) {
+  const int d = c->cfg.d_model, hd = c->cfg.head_dim;
+  {
+    KScope k(c, TL_K_NORM, s);
+    TL_HIP(tl::launch_rmsnorm(c->x, c->pend, B.attn_norm, c->cfg.rms_eps, M, d, c->h, s));
+    c->pend = tl::Pending{nullptr, 1};
+  }
+  {
+    KScope k(c, TL_K_COPY, s);
+    TL_HIP(tl::launch_store_h(c->h, M, d, rm, c->hc_base, c->hc_layer_bytes, c->hc_layers, layer, s));
+  }
+  const int nbd = d / 16;  // n-blocks per section
+  const tl::Packed qsec{B.qkv.tiles, B.qkv.scales, d, d, B.qkv.G};
+  const tl::Packed kvsec{B.qkv.tiles + (size_t)nbd * B.qkv.G * 1024,  // 1 KiB tiles
+                         B.qkv.scales + (size_t)nbd * B.qkv.G * 16, 2 * d, d, B.qkv.G};
+  tl::Epi er{tl::EPI_QKV_ROPE, nullptr, nullptr, 0};
+  er.perm_hd = hd;
+  er.rope = c->rope;
+  er.qout = c->q;
+  er.kv = c->kv;
+  er.layer = 0;
+  if (decode) {
+    tl::Epi eq{tl::EPI_STORE, c->qkv, nullptr, 3 * d};
+    eq.perm_hd = hd;
+    KScope k(c, TL_K_QKV, s);
+    TL_HIP(tl::launch_w4_gemv(B.qkv, tl::ASrc{c->h, nullptr, nullptr, 0.f}, M, eq, s));
+  } else {
+    er.lane = rm.lane;
+    er.p0 = rm.p0;
+    KScope k(c, TL_K_QKV, s);
+    TL_HIP(tl::launch_w4_gemm(qsec, c->h, M, er, c->gpart, s));
+  }
+  // rebuild, per lane: rows are positions 0 .. end-1 of the lane's h cache
+  er.sec_base = 1;
+  er.p0 = 0;
+  const int nrows = decode ? M : 1;
+  for (int m = 0; m < nrows; ++m) {
+    const int lane = decode ? rm.row_lane[m] : rm.lane;
+    const int end = decode ? rm.row_pos[m] : rm.p0 + M;
+    if (end < 1) continue;
+    er.lane = lane;
+    const uint16_t* hrows =
+        reinterpret_cast<const uint16_t*>(c->hc_base + ((size_t)lane * c->hc_layers + layer) * c->hc_layer_bytes);
+    KScope k(c, TL_K_ROPE_KV, s);
+    TL_HIP(tl::launch_w4_gemm(kvsec, hrows, end, er, c->gpart, s));
+  }
+  return TL_OK;
+}
+
 tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowMap& rm, bool decode,
                     hipStream_t s) {
   const int d = c->cfg.d_model, f = c->cfg.ffn_dim;
   const float eps = c->cfg.rms_eps;
   tl_status st;
   int S = 1;
+  tl::ASrc osrc{c->o, nullptr, nullptr, 0.f};
+  // store-h: attention reads the rebuilt scratch as cache layer 0
+  const int alayer = c->hmode ? 0 : layer;
+  if (c->hmode) {
+    st = hmode_qkv(c, B, layer, M, rm, decode, s);
+    if (st != TL_OK) return st;
+  }
   // h = fp16(RMSNorm(x)); [q;k;v] = h W_qkv^T (packed in RoPE-pair order).
   // A prefill GEMM with unsplit K and an FP16 cache applies RoPE and writes
   // Q and the K/V rows in its epilogue; otherwise qkv goes out in fp32.
@@ -250,12 +331,13 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   er.layer = layer;
   er.lane = rm.lane;
   er.p0 = rm.p0;
-  bool roped = false;
-  st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, M, eq, &S, s,
-              (!decode && !c->kv.int8) ? &er : nullptr, &roped);
-  if (st != TL_OK) return st;
+  bool roped = c->hmode;  // store-h: Q (prefill) or q, k, v (decode) are done
+  if (!c->hmode) {
+    st = linear(c, TL_K_QKV, B.qkv, tl::ASrc{nullptr, c->x, B.attn_norm, eps}, M, eq, &S, s,
+                (!decode && !c->kv.int8) ? &er : nullptr, &roped);
+    if (st != TL_OK) return st;
+  }
   const float* qkv = S > 1 ? c->gpart : c->qkv;
-  tl::ASrc osrc{c->o, nullptr, nullptr, 0.f};
   if (decode) {
     if (S > 1) {
       // the decode attention reads whole projections: sum a split GEMM's partials first
@@ -269,7 +351,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
                  tl::attn_decode_np_max(c->cfg.max_seq), c->cfg.head_dim};
     const bool fuse = tl::gemv_supported(M, d, att);
     KScope k(c, TL_K_ATTN, s);
-    TL_HIP(tl::launch_attn_decode(qkv, M, rm, c->rope, c->kv, layer, c->part, fuse ? nullptr : c->o, s));
+    TL_HIP(tl::launch_attn_decode(qkv, M, rm, c->rope, c->kv, alayer, c->part, fuse ? nullptr : c->o, s));
     if (fuse) osrc = att;
   } else {
     // RoPE on q, k (summing the split-K partials); fp16 Q; K, V into cache layer `layer`
@@ -278,7 +360,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
       TL_HIP(tl::launch_rope_kv(qkv, S, M, rm, c->rope, c->kv, layer, c->q, s));
     }
     KScope k(c, TL_K_ATTN, s);
-    TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, layer, c->o, s));
+    TL_HIP(tl::launch_attn_prefill(c->q, M, rm.lane, rm.p0, c->kv, alayer, c->o, s));
   }
   // x += O W_o^T (deferred to the next RMSNorm when K is split)
   st = linear(c, TL_K_O, B.o, osrc, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, &S, s);
@@ -331,6 +413,7 @@ size_t tl_kv_layer_bytes(const tl_config* cfg) {
   if (!check_cfg(cfg, &st, &why)) return 0;
   const size_t rows = (size_t)kv_rows(cfg) * cfg->n_heads;
   if (cfg->kv_dtype == TL_KV_INT8) return 2 * rows * (cfg->head_dim + 2);
+  if (cfg->kv_dtype == TL_KV_H16) return (size_t)cfg->max_seq * cfg->d_model * 2;
   return 2 * rows * cfg->head_dim * 2;
 }
 
@@ -445,9 +528,18 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
       return fail(TL_E_HIP, std::string("rope table upload: ") + hipGetErrorString(e));
     }
   }
+  c->hmode = cfg->kv_dtype == TL_KV_H16;
   c->kv.base = static_cast<uint8_t*>(d_kv);
   c->kv.layer_bytes = tl_kv_layer_bytes(cfg);
   c->kv.n_layers = cfg->n_pre + cfg->max_loops;
+  if (c->hmode) {  // d_kv holds h rows; attention reads the rebuilt one-layer scratch
+    c->hc_base = static_cast<uint8_t*>(d_kv);
+    c->hc_layer_bytes = tl_kv_layer_bytes(cfg);
+    c->hc_layers = cfg->n_pre + cfg->max_loops;
+    c->kv.base = static_cast<uint8_t*>(d_act_ws) + act_layout(cfg).hkv;
+    c->kv.layer_bytes = (size_t)2 * cfg->max_seq * cfg->d_model * 2;
+    c->kv.n_layers = 1;
+  }
   c->kv.H = cfg->n_heads;
   c->kv.hd = cfg->head_dim;
   c->kv.S = cfg->max_seq;

@@ -74,10 +74,12 @@ __host__ __device__ inline int kv_first(const KvGeom& kv, int pos) {
 // Epilogue of the W4 matrix kernels.
 //   STORE / RESID: fp32 out[m*ldo + n] = / += v;
 //   SWIGLU: fp16 out[m*ldo + c] = silu(gate) * up (gate/up n-blocks paired);
-//   QKV_ROPE (GEMM, unsplit K, FP16 cache, one lane's rows at p0 + m): the
-//     columns of a RoPE-pair packed QKV (perm_hd = head_dim) are rotated in
-//     registers (the pair partner sits 8 lanes away), rounded to fp16 and
+//   QKV_ROPE (GEMM, K never split, FP16 cache, one lane's rows at p0 + m):
+//     the columns of a RoPE-pair packed QKV (perm_hd = head_dim) are rotated
+//     in registers (the pair partner sits 8 lanes away), rounded to fp16 and
 //     written as Q to qout [M][d] and as K, V rows into cache layer `layer`.
+//     The weight may be a section view: its column n belongs to section
+//     sec_base + n / d (0 Q, 1 K, 2 V).
 // perm_hd > 0: the packed columns are in RoPE-pair order; STORE / RESID and
 // split partials write column qkv_natural_col(n).
 enum EpiMode { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV_ROPE = 3 };
@@ -91,6 +93,7 @@ struct Epi {
   uint16_t* qout = nullptr;
   KvGeom kv{};
   int layer = 0, lane = 0, p0 = 0;
+  int sec_base = 0;
 };
 
 // Activation source of the matrix kernels: fp16 rows, or fp32 residual rows
@@ -118,7 +121,8 @@ struct GemmPlan {
   float* part;  // S > 1: fp32 partial tiles [S][M][N], summed by the consumer
 };
 constexpr int kMaxSplitK = 16;  // consumers sum at most this many partials
-GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu);
+// swiglu: gate/up pairs per wave and no K split; unsplit: no K split
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit = false);
 size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu);
 // C = A * W^T for any M (prefill GEMM shape); A fp16 [M][K]. When the plan
 // splits K (S > 1, never for SwiGLU) the kernel writes the S partials to
@@ -183,6 +187,11 @@ hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, 
 hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s);
 // dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
+
+// Store-h: fp16 h rows [M][d] -> h cache [lane][layer][pos][d] at each row's
+// lane and position.
+hipError_t launch_store_h(const uint16_t* h, int M, int d, const RowMap& rm, uint8_t* base, size_t layer_bytes,
+                          int n_layers, int layer, hipStream_t s);
 
 // Per-iteration residual-norm check: result = min(result, code_base + m) for
 // each row m of x (+ pending partials) whose L2 norm is not <= max_norm.

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int n = min(nbw0 + j, NB - 1) * 16 + l16;
-      const int sec = n / d, hh = (n - sec * d) / hd, p = n % hd;
+      const int sec = e.sec_base + n / d, hh = (n % d) / hd, p = n % hd;
       const bool first = (p & 15) < 8;
       const int t = 8 * (p >> 4) + (p & 7);
       const int dim = first ? t : half + t;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 // bigger tiles. Narrower columns only when the grid would stay below 256
 // blocks; a K split only until there are 384 blocks (partials cost the
 // consumer a read).
-GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu) {
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit) {
   const int NB = N / 16, G = (K + 127) / 128;
   GemmPlan p{};
   p.mb = M <= 16 ? 1 : 2;
@@ -592,7 +592,7 @@ GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu) {
     p.gx = (NB + 3) / 4;
   }
   int S = 1;
-  if (!swiglu)
+  if (!swiglu && !unsplit)
     while (S < kMaxSplitK && p.gx * p.gy * S < 384 && G / (2 * S) >= 4) S *= 2;
   p.gps = (G + S - 1) / S;
   p.S = (G + p.gps - 1) / p.gps;
@@ -601,7 +601,7 @@ GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu) {
 }
 
 size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu) {
-  const GemmPlan p = plan_w4_gemm(N, K, M, swiglu);
+  const GemmPlan p = plan_w4_gemm(N, K, M, swiglu, false);
   if (p.S == 1) return 0;
   return (size_t)p.S * M * N * 4;
 }
@@ -634,10 +634,13 @@ static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const E
 
 hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s) {
   if (M < 1) return hipErrorInvalidValue;
-  GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU);
+  GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU, e.mode == EPI_QKV_ROPE);
   if (pl.S > 1 && !part) return hipErrorInvalidValue;
-  if (e.mode == EPI_QKV_ROPE && (pl.S > 1 || e.kv.int8 || e.perm_hd != e.kv.hd || w.N != 3 * e.kv.H * e.kv.hd))
-    return hipErrorInvalidValue;
+  if (e.mode == EPI_QKV_ROPE) {
+    const int d = e.kv.H * e.kv.hd;
+    if (e.kv.int8 || e.perm_hd != e.kv.hd || w.N % d || e.sec_base < 0 || e.sec_base + w.N / d > 3)
+      return hipErrorInvalidValue;
+  }
   pl.part = part;
   if (pl.nbw == 2) {
     switch (pl.mb) {

@@ -106,3 +106,15 @@ def test_window_bounds_kv_memory():
     assert win * 2048 == full * (256 + 64)
     assert tl.tl_kv_layer_bytes(make_config(s, 2048, 4, max_tokens=64, cache_window=4096)) == full
     assert tl.tl_kv_layer_bytes(make_config(s, 2048, 4, max_tokens=64, cache_window=-1)) == 0
+
+
+def test_store_h_halves_kv_memory():
+    """TL_KV_H16 keeps h [max_seq][d_model] per layer: half of FP16 K and V
+    ("Current Status" page, KV-cache table: Store-h); not with a window."""
+    import synth
+    from looped_weight_shared_amd.model import make_config
+    s = synth.SHAPES["m407"]
+    fp16 = tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_FP16))
+    h16 = tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H16))
+    assert 2 * h16 == fp16 and h16 == 2048 * 2048 * 2
+    assert tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H16, cache_window=64)) == 0

@@ -103,11 +103,16 @@ def silu(z):
 
 
 class OracleModel:
-    """Dequantized float64 weights of the pre-blocks, the loop block, embed and head."""
+    """Dequantized float64 weights of the pre-blocks, the loop block, embed and head.
 
-    def __init__(self, weights: dict):
+    fp16_body=True rounds every block weight q * s to float16 once, as the
+    FP16 body keeps them ("Performance and Memory" page, "FP16 body cache":
+    body weights dequantized to persistent FP16 at load time)."""
+
+    def __init__(self, weights: dict, fp16_body: bool = False):
         s = weights["shape"]
         self.shape = s
+        self.fp16_body = fp16_body
         self.embed = np.asarray(weights["embed"], dtype=np.float16)
         self.pre = [self._block(b) for b in weights["pre"]]
         self.loop = self._block(weights["loop"])
@@ -118,6 +123,8 @@ class OracleModel:
     def _block(self, b):
         g = self.shape.group_size
         out = {name: dequantize(b[name]["qweight"], b[name]["scales"], g) for name in _LINEARS}
+        if self.fp16_body:
+            out = {name: w.astype(np.float16).astype(np.float64) for name, w in out.items()}
         out["attn_norm"] = np.asarray(b["attn_norm"], dtype=np.float16).astype(np.float64)
         out["mlp_norm"] = np.asarray(b["mlp_norm"], dtype=np.float16).astype(np.float64)
         return out

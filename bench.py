@@ -84,7 +84,7 @@ def _pmc_dispatches(d, counter):
 
 def ingest_pmc(fetch_dir, write_dir, copy_mib):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --decode-steps 4 --copy-mib <copy_mib>`, one with
+    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --decode-steps 4 --copy-mib <copy_mib>`, one with
     FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
     for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
@@ -106,14 +106,14 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
     kernels = {
         # dominant prefill kernel: the gate/up GEMM at M=128, 32x128 tiles: 88 column blocks x 4
         # row tiles = 352 blocks of 256 threads (the 256-token prompt's instance has 704)
-        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2>" in n and g == 352 * 256,
+        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2, false>" in n and g == 352 * 256,
                          tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
         # decode gate/up GEMV: the only two-n-block GEMV (fused RMSNorm, one row)
-        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1>" in n,
+        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1, false>" in n,
                          tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --decode-steps 4 --copy-mib %d" % copy_mib
+    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --decode-steps 4 --copy-mib %d" % copy_mib
     data = {"commands": [
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,
@@ -153,6 +153,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
     ap.add_argument("--no-storeh", action="store_true", help="skip the store-h (TL_KV_H16) leg")
+    ap.add_argument("--no-fp16body", action="store_true", help="skip the FP16-body leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -349,6 +350,44 @@ def main():
                               "note": "prefill bit-identical to FP16 K/V; decode rebuilds K/V of the context every layer"}
             print(f"[bench] store-h: prefill {ms_pre_h:.3f} ms/step, decode {ms_tok_h:.4f} ms/token, "
                   f"KV bytes {kvb['h16']} vs {kvb['fp16']}", file=sys.stderr, flush=True)
+
+        # ------------------------------------------------------------ FP16 body
+        # the same steps with the block weights dequantized once to fp16
+        if not args.no_fp16body:
+            mf = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=tl.TL_KV_FP16,
+                       max_tokens=max(SEQ, args.prompt), fp16_body=True)
+            mf.set_loops(0, L)
+
+            def prefill_f():
+                mf.reset(0)
+                mf.prefill(toks)
+            for _ in range(3):
+                prefill_f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                prefill_f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_pre_f = e0.elapsed_time(e1) / 20
+            mf.reset(0)
+            mf.prefill(ptoks, next_tok=bufs[0])
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for t in range(D):
+                mf.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_tok_f = e0.elapsed_time(e1) / D
+            wsb = {k: tl.tl_weights_ws_bytes(mod.make_config(s, 2048, L, fp16_body=v)) for k, v in (("w4", 0), ("fp16", 1))}
+            mf.close()
+            out["fp16_body"] = {"weights_ws_bytes": wsb, "prefill_ms_seq128": round(ms_pre_f, 4),
+                                "prefill_speedup_w4_over_fp16": round(ms_pre_f / ms_step, 3),
+                                "decode_ms_per_token": round(ms_tok_f, 4),
+                                "decode_speedup_w4_over_fp16": round(ms_tok_f / ms_tok, 3)}
+            print(f"[bench] FP16 body: prefill {ms_pre_f:.3f} ms/step, decode {ms_tok_f:.4f} ms/token, "
+                  f"weights {wsb['fp16']} vs {wsb['w4']} B", file=sys.stderr, flush=True)
 
         if spec:
             out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,

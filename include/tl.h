@@ -84,6 +84,12 @@ typedef struct {
    * layer and head (position p in row p mod that), so KV memory no longer
    * grows with max_seq; positions still run up to max_seq. */
   int32_t cache_window;
+  /* FP16 body ("Performance and Memory" page, "FP16 body cache" and "Key
+   * Runtime Switches": body weights dequantized to persistent FP16 at load
+   * time): 0 keeps the loop and pre-blocks as packed W4 (the default); 1
+   * stores each block linear as fp16(q * s) tiles (4x the bytes, no scales)
+   * and runs the same GEMM/GEMV kernels without the dequantization. */
+  int32_t fp16_body;
 } tl_config;
 
 /* One INT4 linear layer in the canonical layout (device pointers):

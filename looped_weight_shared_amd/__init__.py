@@ -57,7 +57,7 @@ class TlConfig(ctypes.Structure):
     _fields_ = [("vocab", _i32), ("d_model", _i32), ("n_heads", _i32), ("head_dim", _i32),
                 ("ffn_dim", _i32), ("n_pre", _i32), ("group_size", _i32), ("rope_base", _f32),
                 ("rms_eps", _f32), ("max_seq", _i32), ("max_loops", _i32), ("n_lanes", _i32),
-                ("kv_dtype", _i32), ("max_tokens", _i32), ("cache_window", _i32)]
+                ("kv_dtype", _i32), ("max_tokens", _i32), ("cache_window", _i32), ("fp16_body", _i32)]
 
 
 class TlQLinear(ctypes.Structure):

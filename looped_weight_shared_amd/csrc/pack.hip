@@ -61,6 +61,48 @@ hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, i
   return hipGetLastError();
 }
 
+// FP16 body tiles: one thread per 16-byte slot (8 columns of one row).
+__global__ void pack_f16_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc, int N, int K,
+                                uint32_t* __restrict__ dst, int G, int nb_offset, int nb_stride, int perm_hd) {
+  const int G_src = (K + 127) / 128;
+  const long long total = (long long)(N / 16) * G_src * 256;  // slots
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int l = (int)(i & 63);
+  const int s = (int)((i >> 6) & 3);
+  const long long tile = i >> 8;
+  const int g = (int)(tile % G_src);
+  const int nb = (int)(tile / G_src);
+  const int n = perm_hd ? qkv_natural_col(nb * 16 + (l & 15), perm_hd) : nb * 16 + (l & 15);
+  const int k0 = g * 128 + 32 * s + 8 * (l >> 4);
+  uint32_t out[4] = {0, 0, 0, 0};
+  if (k0 < K) {
+    const uint32_t cw = qw[(size_t)n * (K / 8) + k0 / 8];
+    const float scale = (float)__builtin_bit_cast(_Float16, sc[(size_t)n * G_src + g]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = (int)((cw >> (4 * e)) & 0xFu) - (((cw >> (4 * e)) & 0x8u) ? 16 : 0);  // two's complement nibble
+      const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)((float)q * scale));    // exact product, one rounding
+      out[e >> 1] |= h << (16 * (e & 1));
+    }
+  }
+  const int dnb = nb_offset + nb * nb_stride;
+  uint32_t* d = dst + ((((size_t)dnb * G + g) * 4 + s) * 64 + l) * 4;
+  d[0] = out[0];
+  d[1] = out[1];
+  d[2] = out[2];
+  d[3] = out[3];
+}
+
+hipError_t launch_pack_f16(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles, int dst_G,
+                           int nb_offset, int nb_stride, int perm_hd, hipStream_t s) {
+  if (perm_hd && (perm_hd % 16 || N % perm_hd)) return hipErrorInvalidValue;
+  const long long total = (long long)(N / 16) * ((K + 127) / 128) * 256;
+  launch(pack_f16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, qweight, scales, N, K,
+         reinterpret_cast<uint32_t*>(dst_tiles), dst_G, nb_offset, nb_stride, perm_hd);
+  return hipGetLastError();
+}
+
 // Inverse view: packed -> int8 [N][K] values and fp16 [N][G] scales.
 __global__ void unpack_kernel(const uint32_t* __restrict__ src, const uint16_t* __restrict__ src_sc, int N, int K,
                               int G, int8_t* __restrict__ q, uint16_t* __restrict__ sc) {

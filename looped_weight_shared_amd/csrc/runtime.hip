@@ -63,6 +63,7 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->n_lanes < 1 || c->n_lanes > 8) return *why = "n_lanes must be in 1..8", false;
   if (c->max_seq < 1 || c->max_tokens < 1) return *why = "max_seq and max_tokens must be >= 1", false;
   if (c->cache_window < 0) return *why = "cache_window must be >= 0", false;
+  if (c->fp16_body != 0 && c->fp16_body != 1) return *why = "fp16_body must be 0 or 1", false;
   if (c->kv_dtype == TL_KV_H16 && c->cache_window > 0) {
     *st = TL_E_UNSUPPORTED;
     return *why = "store-h (TL_KV_H16) does not combine with cache_window", false;
@@ -71,8 +72,15 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   return true;
 }
 
+// one linear in the block store: packed W4 (tiles + scales) or the FP16 body
+size_t linear_bytes(const tl_config* c, int N, int K) {
+  return c->fp16_body ? tl::packed_f16_bytes(N, K) : tl::packed_bytes(N, K);
+}
 size_t block_bytes(const tl_config* c) {
   const int d = c->d_model, f = c->ffn_dim;
+  if (c->fp16_body)
+    return al256(linear_bytes(c, 3 * d, d)) + al256(linear_bytes(c, d, d)) + al256(linear_bytes(c, 2 * f, d)) +
+           al256(linear_bytes(c, d, f));
   return al256(tl::packed_bytes(3 * d, d)) + al256(tl::packed_bytes(d, d)) + al256(tl::packed_bytes(2 * f, d)) +
          al256(tl::packed_bytes(d, f));
 }
@@ -268,9 +276,11 @@ tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
     TL_HIP(tl::launch_store_h(c->h, M, d, rm, c->hc_base, c->hc_layer_bytes, c->hc_layers, layer, s));
   }
   const int nbd = d / 16;  // n-blocks per section
-  const tl::Packed qsec{B.qkv.tiles, B.qkv.scales, d, d, B.qkv.G};
-  const tl::Packed kvsec{B.qkv.tiles + (size_t)nbd * B.qkv.G * 1024,  // 1 KiB tiles
-                         B.qkv.scales + (size_t)nbd * B.qkv.G * 16, 2 * d, d, B.qkv.G};
+  const size_t tb = B.qkv.f16 ? 4096 : 1024;  // tile bytes
+  const tl::Packed qsec{B.qkv.tiles, B.qkv.scales, d, d, B.qkv.G, B.qkv.f16};
+  const tl::Packed kvsec{B.qkv.tiles + (size_t)nbd * B.qkv.G * tb,
+                         B.qkv.f16 ? nullptr : B.qkv.scales + (size_t)nbd * B.qkv.G * 16, 2 * d, d, B.qkv.G,
+                         B.qkv.f16};
   tl::Epi er{tl::EPI_QKV_ROPE, nullptr, nullptr, 0};
   er.perm_hd = hd;
   er.rope = c->rope;
@@ -464,14 +474,18 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   auto carve = [&](int N, int K) {
     tl::Packed pk;
     pk.tiles = p;
-    pk.scales = reinterpret_cast<const uint16_t*>(p + tl::packed_tile_bytes(N, K));
+    pk.scales = cfg->fp16_body ? nullptr : reinterpret_cast<const uint16_t*>(p + tl::packed_tile_bytes(N, K));
     pk.N = N;
     pk.K = K;
     pk.G = (K + 127) / 128;
-    p += al256(tl::packed_bytes(N, K));
+    pk.f16 = cfg->fp16_body ? 1 : 0;
+    p += al256(linear_bytes(cfg, N, K));
     return pk;
   };
   auto pack = [&](const tl_qlinear& l, int N, int K, const tl::Packed& dst, int off, int stride, int perm = 0) {
+    if (dst.f16)
+      return tl::launch_pack_f16(l.qweight, l.scales, N, K, const_cast<uint8_t*>(dst.tiles), dst.G, off, stride, perm,
+                                 s);
     return tl::launch_pack(l.qweight, l.scales, N, K, const_cast<uint8_t*>(dst.tiles),
                            const_cast<uint16_t*>(dst.scales), dst.G, off, stride, perm, s);
   };

@@ -22,6 +22,7 @@ namespace tl {
 // of a consecutive pair), stored offset-binary u = q + 8.
 // ---------------------------------------------------------------------------
 constexpr int kTileBytes = 1024;
+constexpr int kTileBytesF16 = 4096;  // dense fp16 body tile
 constexpr int kGroup = 128;
 
 // 8 signed 4-bit values of one packed word -> 8 exact fp16 integers in

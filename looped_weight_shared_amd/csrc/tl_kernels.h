@@ -34,8 +34,9 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
 // scales fp16 [N/16][G][16]. G = ceil(K / 128).
 struct Packed {
   const uint8_t* tiles;
-  const uint16_t* scales;
+  const uint16_t* scales;  // W4 only
   int N, K, G;
+  int f16 = 0;  // 1: dense fp16 tiles (4 KiB per 16 rows x 128 columns), no scales
 };
 
 inline size_t packed_tile_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 1024; }
@@ -54,6 +55,13 @@ hipError_t launch_pack_head(const uint16_t* head, int V, int d, uint8_t* dst, hi
 hipError_t launch_pack(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles,
                        uint16_t* dst_scales, int dst_G, int nb_offset, int nb_stride, int perm_hd, hipStream_t s);
 hipError_t launch_unpack(const Packed& p, int8_t* q, uint16_t* scales, hipStream_t s);
+// FP16 body: the same canonical linear dequantized to fp16(q * s) (one
+// rounding of the exact product) in the MFMA B-operand order of the W4 tile
+// (slot s of lane l = word s of the W4 slot), 4 KiB per 16-row x 128-column
+// tile laid out [s][lane][16 B]; same n-block placement and row order options.
+inline size_t packed_f16_bytes(int N, int K) { return (size_t)(N / 16) * ((K + 127) / 128) * 4096; }
+hipError_t launch_pack_f16(const uint32_t* qweight, const uint16_t* scales, int N, int K, uint8_t* dst_tiles, int dst_G,
+                           int nb_offset, int nb_stride, int perm_hd, hipStream_t s);
 
 struct KvGeom {
   uint8_t* base;        // start of all caches

@@ -73,7 +73,7 @@ __device__ __forceinline__ void lds_barrier() {
 // straight-line and the compiler's waits stay exact.
 enum GemvSrc { SRC_A16 = 0, SRC_NORM = 1, SRC_ATT = 2 };
 
-template <int NBB, int SRC, int MR, int GI, int APT>
+template <int NBB, int SRC, int MR, int GI, int APT, bool F16>
 __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
                                                                const uint16_t* __restrict__ scales, int N, int K,
                                                                int G, ASrc a, int M, Epi e) {
@@ -123,8 +123,9 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
     }
   }
   asm volatile("" ::: "memory");  // activation requests strictly before the weight requests
-  // ---- 2. weight requests
-  u32x4_t wv[GI][NBB];
+  // ---- 2. weight requests (F16: four 16-byte slots per tile and lane, no scales)
+  constexpr int WS = F16 ? 4 : 1;
+  u32x4_t wv[GI][NBB][WS];
   uint32_t sc[GI][NBB];  // raw fp16 bits: converting at load time would force a wait
 #pragma unroll
   for (int it = 0; it < GI; ++it) {
@@ -132,8 +133,14 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
 #pragma unroll
     for (int j = 0; j < NBB; ++j) {
       const size_t tile = (size_t)(nb0 + j) * G + g;
-      wv[it][j] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes) + lane);
-      sc[it][j] = scales[tile * 16 + l16];
+      if constexpr (F16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          wv[it][j][s] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytesF16) + s * 64 + lane);
+      } else {
+        wv[it][j][0] = *(reinterpret_cast<const u32x4_t*>(tiles + tile * kTileBytes) + lane);
+        sc[it][j] = scales[tile * 16 + l16];
+      }
     }
   }
   asm volatile("" ::: "memory");
@@ -237,12 +244,17 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
         af[s] = arow ? *reinterpret_cast<const half8_t*>(As + l16 * lda + g * 128 + 32 * s + 8 * lq) : hz;
 #pragma unroll
       for (int j = 0; j < NBB; ++j) {
-        float4_t t = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (F16) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) t = mfma16(af[s], dequant_word(wv[it][j][s]), t);
-        const float scf = h2f((uint16_t)sc[it][j]);
+          for (int s = 0; s < 4; ++s) acc[j] = mfma16(af[s], __builtin_bit_cast(half8_t, wv[it][j][s]), acc[j]);
+        } else {
+          float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], scf, acc[j][r]);
+          for (int s = 0; s < 4; ++s) t = mfma16(af[s], dequant_word(wv[it][j][0][s]), t);
+          const float scf = h2f((uint16_t)sc[it][j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(t[r], scf, acc[j][r]);
+        }
       }
     }
   }
@@ -284,19 +296,24 @@ bool gemv_supported(int M, int K, const ASrc& a) {
   return G <= kGemvWaves * kGemvIt && M * (K / 8) <= kGemvThreads * kGemvAChunks;
 }
 
-template <int NBB, int SRC, int MR, int GI, int APT>
-static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+template <int NBB, int SRC, int MR, int GI, int APT, bool F16>
+static hipError_t gemv_launch_t(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<NBB, SRC, MR, GI, APT>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemv_kernel<NBB, SRC, MR, GI, APT, F16>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
   const size_t lds = (size_t)M * (w.G * 128 + 8) * 2;
-  launch((w4_gemv_kernel<NBB, SRC, MR, GI, APT>), dim3(w.N / 16 / NBB), dim3(kGemvThreads), lds, s, w.tiles,
+  launch((w4_gemv_kernel<NBB, SRC, MR, GI, APT, F16>), dim3(w.N / 16 / NBB), dim3(kGemvThreads), lds, s, w.tiles,
          w.scales, w.N, w.K, w.G, a, M, e);
   return hipGetLastError();
+}
+template <int NBB, int SRC, int MR, int GI, int APT>
+static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+  return w.f16 ? gemv_launch_t<NBB, SRC, MR, GI, APT, true>(w, a, M, e, s)
+               : gemv_launch_t<NBB, SRC, MR, GI, APT, false>(w, a, M, e, s);
 }
 
 // fused RMSNorm: K <= 2048, so at most 2 groups per wave
@@ -361,7 +378,7 @@ hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, h
 // writes an fp32 partial tile and the consumer sums the S partials in order.
 constexpr int kGemmAhead = 2;  // groups of loads in flight per wave (the loop is unrolled by it)
 
-template <int MB, int NBW>
+template <int MB, int NBW, bool F16>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int N, int K, int G,
                                                       const uint16_t* __restrict__ A, int M, Epi e, GemmPlan pl) {
@@ -392,25 +409,32 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const size_t nb = (size_t)min(nbw0 + j, NB - 1) * G;
-    btile[j] = reinterpret_cast<const u32x4_t*>(tiles + nb * kTileBytes) + lane;
-    bscale[j] = scales + nb * 16 + l16;
+    btile[j] = reinterpret_cast<const u32x4_t*>(tiles + nb * (F16 ? kTileBytesF16 : kTileBytes)) + lane;
+    bscale[j] = F16 ? scales : scales + nb * 16 + l16;
   }
 
   constexpr int D = kGemmAhead;
+  constexpr int WS = F16 ? 4 : 1;  // 16-byte weight slots per tile and lane
   u32x4_t ar[D][MB];
-  u32x4_t br[D][NBW];
-  uint32_t bs[D][NBW];  // raw fp16 bits
+  u32x4_t br[D][NBW][WS];
+  uint32_t bs[D][NBW];  // raw fp16 bits (W4 only)
   auto load_a = [&](u32x4_t (&ra)[MB], int g) {
     const int col = min(min(g, kg1 - 1) * 128 + acol, K - 8);
 #pragma unroll
     for (int i = 0; i < MB; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + col);
   };
-  auto load_b = [&](u32x4_t (&rb)[NBW], uint32_t (&rs)[NBW], int g) {
+  auto load_b = [&](u32x4_t (&rb)[NBW][WS], uint32_t (&rs)[NBW], int g) {
     const int gc = min(g, kg1 - 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      rb[j] = btile[j][(size_t)gc * 64];
-      rs[j] = bscale[j][(size_t)gc * 16];
+      if constexpr (F16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rb[j][s] = btile[j][((size_t)gc * 4 + s) * 64];
+        rs[j] = 0;
+      } else {
+        rb[j][0] = btile[j][(size_t)gc * 64];
+        rs[j] = bscale[j][(size_t)gc * 16];
+      }
     }
   };
   auto store_a = [&](const u32x4_t (&ra)[MB], int buf) {
@@ -424,7 +448,24 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const u32x4_t (&bw)[NBW], const uint32_t (&bsc)[NBW], bool valid) {
+  auto compute = [&](int buf, const u32x4_t (&bw)[NBW][WS], const uint32_t (&bsc)[NBW], bool valid) {
+    if constexpr (F16) {  // dense fp16 weights: straight into the accumulators
+      const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t af[MB], bf[NBW];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          af[i] = *reinterpret_cast<const half8_t*>(&As[buf][(i * 4 + s) * 1024 + lane * 16]);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) bf[j] = valid ? __builtin_bit_cast(half8_t, bw[j][s]) : hz;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
+      }
+      return;
+    }
     float4_t t[MB][NBW];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -436,7 +477,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const half8_t*>(&As[buf][(i * 4 + s) * 1024 + lane * 16]);
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) bf[j] = dequant_word(valid ? bw[j][s] : 0x88888888u);  // 0x8: q = 0
+      for (int j = 0; j < NBW; ++j) bf[j] = dequant_word(valid ? bw[j][0][s] : 0x88888888u);  // 0x8: q = 0
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -627,8 +668,12 @@ hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float*
 template <int MB, int NBW>
 static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const Epi& e, const GemmPlan& pl,
                               hipStream_t s) {
-  launch((w4_gemm_kernel<MB, NBW>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K,
-                     w.G, A, M, e, pl);
+  if (w.f16)
+    launch((w4_gemm_kernel<MB, NBW, true>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G, A, M,
+           e, pl);
+  else
+    launch((w4_gemm_kernel<MB, NBW, false>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G, A,
+           M, e, pl);
   return hipGetLastError();
 }
 

@@ -20,13 +20,14 @@ _LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
 def make_config(shape, max_seq, max_loops, n_lanes=1, kv_dtype=TL_KV_FP16, max_tokens=None,
-                cache_window=0) -> TlConfig:
+                cache_window=0, fp16_body=0) -> TlConfig:
     """TlConfig from a shape object with vocab/d_model/n_heads/... attributes."""
     return TlConfig(vocab=shape.vocab, d_model=shape.d_model, n_heads=shape.n_heads,
                     head_dim=shape.head_dim, ffn_dim=shape.ffn_dim, n_pre=shape.n_pre,
                     group_size=shape.group_size, rope_base=shape.rope_base, rms_eps=shape.rms_eps,
                     max_seq=max_seq, max_loops=max_loops, n_lanes=n_lanes, kv_dtype=kv_dtype,
-                    max_tokens=max_tokens or max_seq, cache_window=cache_window)
+                    max_tokens=max_tokens or max_seq, cache_window=cache_window,
+                    fp16_body=1 if fp16_body else 0)
 
 
 def device_bytes(nbytes: int, device="cuda") -> torch.Tensor:
@@ -50,9 +51,10 @@ class Model:
 
     def __init__(self, weights: dict, max_seq: int, max_loops: int, n_lanes: int = 1,
                  kv_dtype: int = TL_KV_FP16, max_tokens: int | None = None, device="cuda",
-                 cache_window: int = 0):
+                 cache_window: int = 0, fp16_body: bool = False):
         self.shape = weights["shape"]
-        self.cfg = make_config(self.shape, max_seq, max_loops, n_lanes, kv_dtype, max_tokens, cache_window)
+        self.cfg = make_config(self.shape, max_seq, max_loops, n_lanes, kv_dtype, max_tokens, cache_window,
+                               fp16_body)
         self.device = device
         keep = []
 

@@ -64,35 +64,50 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
 }
 
-// Butterfly reductions over a whole wave (fixed order: every lane ends with
-// the same value, computed in the same order whatever the data).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, TL_WAVE);
-  return v;
+// Reductions over the 16 lanes of one row of the wave (lanes 16r..16r+15)
+// and over the whole wave, on DPP lane moves instead of LDS permutes: swap
+// neighbours, swap pairs (quad_perm), then half-row and row mirrors add the
+// other quad and the other half, so every lane of the row ends with the same
+// bits (each step adds two equal-order operands: a + b on one side, b + a on
+// the other). The wave-wide forms read the four row results with readlane
+// and combine them in row order (a uniform value). Callers run them with the
+// whole wave active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, TL_WAVE));
-  return v;
-}
-// Reductions over the 16 lanes of one row of the wave (lanes 16r..16r+15).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15 - i within each 16
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, TL_WAVE);
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
   return v;
 }
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, TL_WAVE));
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppMirror>(v));
   return v;
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Rotary embedding of one pair (x1 = dim i, x2 = dim i + hd/2) by the angle
-// whose cos/sin are c, s; both results are rounded to fp16 (Q and K cast
-// points). Every kernel that rotates uses this one expression.
 // RoPE-pair packing of the QKV rows: within each head of hd rows, packed
 // row 16j + r holds natural row 8j + r (r < 8, first half of rotation pair
 // 8j + r) or hd/2 + 8j + r - 8 (r >= 8, its second half).
@@ -105,6 +120,9 @@ __host__ __device__ __forceinline__ int qkv_natural_col(int n, int hd) {
   return n - p + rope_pair_row(p, hd);
 }
 
+// Rotary embedding of one pair (x1 = dim i, x2 = dim i + hd/2) by the angle
+// whose cos/sin are c, s; both results are rounded to fp16 (Q and K cast
+// points). Every kernel that rotates uses this one expression.
 __device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, _Float16* r1, _Float16* r2) {
   *r1 = (_Float16)(x1 * c - x2 * s);
   *r2 = (_Float16)(x2 * c + x1 * s);

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   constexpr int KPP = 64 / LPK;  // keys per pass
   constexpr int NP = kDecChunk / KPP;
   constexpr int HALF = HD / 2;
-  __shared__ float red_o[kDecWaves][HD];
+  __shared__ float red_o[kDecWaves][64 / (HD / 8)][HD];  // per wave and key row of a pass
   __shared__ float red_m[kDecWaves], red_l[kDecWaves];
   const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
   const int pos = rm.row_pos[m];
@@ -410,11 +410,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
         ka = fmaxf(ka, fabsf((float)kf[j]));
         va = fmaxf(va, fabsf((float)vf[j]));
       }
-#pragma unroll
-      for (int off = LPK / 2; off >= 1; off >>= 1) {
-        ka = fmaxf(ka, __shfl_xor(ka, off, 64));
-        va = fmaxf(va, __shfl_xor(va, off, 64));
-      }
+      ka = lanes_max<LPK>(ka);
+      va = lanes_max<LPK>(va);
       const _Float16 s16k = kv_scale(ka), s16v = kv_scale(va);
       ksn = (float)s16k;
       vsn = (float)s16v;
@@ -477,8 +474,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
 #pragma unroll
     for (int j = 0; j < 8; ++j) tn = fmaf(qv[j], kn[j], tn);
     t = key < pos ? t : (key == pos ? tn : 0.f);
-#pragma unroll
-    for (int off = LPK / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+    t = lanes_sum<LPK>(t);
     float kscale = ksn;
     if constexpr (I8) kscale = key < pos ? h2f((uint16_t)ksr[p]) : ksn;
     sc[p] = key <= pos ? t * scale * kscale : -INFINITY;
@@ -516,12 +512,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   }
   lsum = wave_sum(lsum);
 #pragma unroll
-  for (int off = LPK; off < 64; off <<= 1)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ov[j] += __shfl_xor(ov[j], off, 64);
-  if (kg == 0)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) red_o[wave][d0 + j] = ov[j];
+  for (int j = 0; j < 8; ++j) red_o[wave][kg][d0 + j] = ov[j];
   if (ln == 0) {
     red_m[wave] = mx;
     red_l[wave] = lsum;
@@ -537,7 +528,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
     for (int w = 0; w < kDecWaves; ++w) {
       if (red_m[w] == -INFINITY) continue;  // chunk beyond the context
       const float sw = expf(red_m[w] - bm);
-      num = fmaf(sw, red_o[w][tid], num);
+      float o = red_o[w][0][tid];
+#pragma unroll
+      for (int g = 1; g < KPP; ++g) o += red_o[w][g][tid];  // key rows in order
+      num = fmaf(sw, o, num);
       den = fmaf(sw, red_l[w], den);
     }
     dst[tid] = num;

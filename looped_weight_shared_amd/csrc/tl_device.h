@@ -94,6 +94,24 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_mov<kDppMirror>(v));
   return v;
 }
+// The same over aligned groups of N = 8 or 16 lanes.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  if constexpr (N == 16) return row16_sum(v);
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  return v + dpp_mov<kDppHalfMirror>(v);
+}
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  if constexpr (N == 16) return row16_max(v);
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  return fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+}
+constexpr int kDppRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each 16: the xor-8 partner
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }

@@ -554,7 +554,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
           const int m = m0 + i * 16 + 4 * lq + rr;
           const int pos = e.p0 + min(m, M - 1);
           const float v = acc[i][j][rr];
-          const float other = __shfl_xor(v, 8, 64);
+          const float other = dpp_mov<kDppRor8>(v);  // the pair partner, 8 lanes away
           float y = v;
           if (sec < 2) {
             const float c = e.rope[(size_t)pos * half + t];

@@ -393,15 +393,7 @@ __global__ __launch_bounds__(256) void head_kernel(const float* __restrict__ x, 
         bi = v;
       }
       // max over the 16 vocab rows, ties to the lowest index
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      row16_argmax(bv, bi);
       if (l16 == 0 && m < M) {
         cval[(size_t)m * nblk + nb] = bv;
         cidx[(size_t)m * nblk + nb] = bi;
@@ -442,15 +434,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ c
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > bv || (ov == bv && oi < bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
+  wave_argmax(bv, bi);
   if ((tid & 63) == 0) {
     bv_s[tid >> 6] = bv;
     bi_s[tid >> 6] = bi;

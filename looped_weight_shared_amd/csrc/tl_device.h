@@ -111,6 +111,40 @@ __device__ __forceinline__ float lanes_max(float v) {
   v = fmaxf(v, dpp_mov<kDppXor2>(v));
   return fmaxf(v, dpp_mov<kDppHalfMirror>(v));
 }
+// (value, index) maximum with ties to the lower index (a total order, so both
+// lanes of an exchange keep the same winner) over the 16 lanes of a row, and
+// over the wave (uniform result).
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_mov<CTRL>(v);
+  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, true);
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  argmax_step<kDppXor1>(v, i);
+  argmax_step<kDppXor2>(v, i);
+  argmax_step<kDppHalfMirror>(v, i);
+  argmax_step<kDppMirror>(v, i);
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  row16_argmax(v, i);
+  float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (rv > bv || (rv == bv && ri < bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
+}
 constexpr int kDppRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each 16: the xor-8 partner
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

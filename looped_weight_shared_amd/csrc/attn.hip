@@ -204,11 +204,15 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
       for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, sv[kb][r]);
       mx = row16_max(mx);
       const float mnew = fmaxf(mrow[r], mx);
-      const float alpha = expf(mrow[r] - mnew);  // 0 on the first tile (mrow = -inf)
+      // a row with no visible key so far (a sliding window that starts in a
+      // later tile) keeps mnew = -inf: subtract 0 instead, so its weights
+      // are exp(-inf) = 0 rather than exp(-inf - -inf) = NaN
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = expf(mrow[r] - mref);  // 0 while mrow = -inf
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const float p = expf(sv[kb][r] - mnew);
+        const float p = expf(sv[kb][r] - mref);
         ps += p;
         sv[kb][r] = p;
       }

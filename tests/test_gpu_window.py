@@ -86,6 +86,16 @@ def test_window_matches_oracle_fp16(sharp, W, L):
                  steps=40)
 
 
+@pytest.mark.parametrize("W", [2, 16])
+def test_short_window_within_one_prefill_over_two_key_tiles(sharp, W):
+    """A 150-token prefill in one call: with W = 16, queries 143..149 see no
+    key of the first 128-key tile, so the online softmax must skip that tile
+    for them (regression: their rows came out NaN)."""
+    s, w, om = sharp
+    _window_case(s, w, om, W, 3, kv_int8=False, max_seq=200, max_tokens=150, lens=[160, 150], chunks=[150, 150],
+                 steps=10)
+
+
 # INT8 windows are checked at the 407M shape. At the tiny shape (d = 256) a
 # code decided differently on a one-ulp fp16 difference between two correct
 # evaluations of a K/V row is a large part of a short dot product: a CPU run

@@ -106,7 +106,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
     kernels = {
         # dominant prefill kernel: the gate/up GEMM at M=128, 32x128 tiles: 88 column blocks x 4
         # row tiles = 352 blocks of 256 threads (the 256-token prompt's instance has 704)
-        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2, false>" in n and g == 352 * 256,
+        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2, false, 2>" in n and g == 352 * 256,
                          tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
         # decode gate/up GEMV: the only two-n-block GEMV (fused RMSNorm, one row)
         "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1, false>" in n,

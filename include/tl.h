@@ -319,7 +319,8 @@ tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, i
 tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* d_q,
                             uint16_t* d_scales, void* stream);
 /* C[m][n] = sum_k A[m][k] * W[n][k] over a packed linear, fp32 out [M][N].
- * A is fp16 [M][K] row-major. M >= 1: M <= 8 runs the decode GEMV kernel,
+ * A is fp16 [M][K] row-major; d_A and d_C 16-byte aligned (TL_E_INVAL
+ * otherwise). M >= 1: M <= 8 runs the decode GEMV kernel,
  * larger M the prefill GEMM kernel with the launch plan the forward pass
  * uses for that shape (including its K split); fp32 accumulation.
  * d_ws: scratch of tl_w4_linear_ws_bytes(N, K, M) bytes (may be NULL when

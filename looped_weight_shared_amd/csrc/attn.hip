@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const uint16_t* __res
     const int key0 = kt * KT;
     store_tile(kt);
     attn_lds_barrier();
-    load_tile(min(kt + 1, nkt - 1));  // the next tile is in flight during this tile's math
+    if (kt + 1 < nkt) load_tile(kt + 1);  // the next tile is in flight during this tile's math
     asm volatile("" ::: "memory");
 
     // ---- S = Q K^T for 16 rows x KT keys (lane: rows 4lq+r, key 16kb + l16)

@@ -1045,7 +1045,7 @@ tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_
                        void* d_ws, void* stream) {
   if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
   if (M < 1) return fail(TL_E_RANGE, "M < 1");
-  if (!d_packed || !d_A || !d_C || !aligned(d_A, 16)) return fail(TL_E_INVAL, "bad pointer");
+  if (!d_packed || !d_A || !d_C || !aligned(d_A, 16) || !aligned(d_C, 16)) return fail(TL_E_INVAL, "bad pointer");
   const tl::Packed p = packed_view(d_packed, N, K);
   const tl::Epi e{tl::EPI_STORE, d_C, nullptr, N};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -378,7 +378,12 @@ hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, h
 // writes an fp32 partial tile and the consumer sums the S partials in order.
 constexpr int kGemmAhead = 2;  // groups of loads in flight per wave (the loop is unrolled by it)
 
-template <int MB, int NBW, bool F16>
+// Epilogue kinds, a template parameter so that each kind's kernel is
+// register-allocated for its own epilogue: fp32 out (split-K partials,
+// STORE, RESID), QKV_ROPE, SWIGLU.
+enum GemmEp { GEP_F32 = 0, GEP_QKV = 1, GEP_SWIGLU = 2 };
+
+template <int MB, int NBW, bool F16, int EP>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int N, int K, int G,
                                                       const uint16_t* __restrict__ A, int M, Epi e, GemmPlan pl) {
@@ -517,36 +522,60 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
   // ---- split-K: publish this split's partial tile; the kernel that consumes
   // the result sums the S partials in split order (kernel boundaries make
   // them visible; no in-kernel cross-block traffic).
-  if (pl.S > 1) {
+  // Every epilogue stages each n-block's 16 columns of the wave's 16*MB rows
+  // in the wave's own LDS slot (the activation stages are free once the last
+  // group's barrier has passed), so that each lane then stores one 16-byte
+  // run of consecutive output columns instead of scattered 2- or 4-byte
+  // stores. Lane (lq, l16) holds C[m0 + 16i + 4lq + rr][16(nbw0 + j) + l16].
+  float* stf = reinterpret_cast<float*>(&As[0][0]) + wave * (MB * 16 * 16);
+  uint16_t* stg = reinterpret_cast<uint16_t*>(&As[0][0]) + wave * (MB * 16 * 16);
+  auto stage = [&](int i, int rr, uint16_t v) { stg[(i * 16 + 4 * lq + rr) * 16 + l16] = v; };
+
+  // ---- fp32 out: split-K partial tiles (the consumer sums the S partials in
+  // split order; kernel boundaries make them visible), STORE, RESID
+  if constexpr (EP == GEP_F32) {
+    const bool resid = pl.S == 1 && e.mode == EPI_RESID;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int j = 0; j < NBW; ++j) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = m0 + i * 16 + 4 * lq + rr;
-        if (m >= M) continue;
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int n = (nbw0 + j) * 16 + l16;
-          if (nbw0 + j < NB) pl.part[((size_t)sp * M + m) * N + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)] = acc[i][j][rr];
+        for (int rr = 0; rr < 4; ++rr) stf[(i * 16 + 4 * lq + rr) * 16 + l16] = acc[i][j][rr];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes land before its reads
+      if (nbw0 + j < NB) {
+#pragma unroll
+        for (int c = lane; c < MB * 64; c += 64) {  // 4 runs of 4 columns per row
+          const int r = c >> 2, q4 = c & 3;
+          const int m = m0 + r;
+          float4_t v = *reinterpret_cast<const float4_t*>(stf + r * 16 + q4 * 4);
+          if (m < M) {
+            // 4 consecutive packed columns stay consecutive in natural order
+            const int n = (nbw0 + j) * 16 + q4 * 4;
+            const int nn = e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n;
+            float* dst = pl.S > 1 ? pl.part + ((size_t)sp * M + m) * N + nn : e.out_f32 + (size_t)m * e.ldo + nn;
+            if (resid) v = *reinterpret_cast<const float4_t*>(dst) + v;
+            *reinterpret_cast<float4_t*>(dst) = v;
+          }
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next n-block's writes
+    }
     return;
   }
 
   // ---- QKV with RoPE, fp16 Q and the K/V cache rows (RoPE-pair packing:
   // lane l16 < 8 holds the first half of rotation pair t, lane l16 + 8 the
   // second half; both halves are rotated as rope_pair does)
-  if (e.mode == EPI_QKV_ROPE) {
+  if constexpr (EP == GEP_QKV) {
     const int hd = e.kv.hd, half = hd / 2, d = e.kv.H * hd;
     uint8_t* base = e.kv.base + ((size_t)e.lane * e.kv.n_layers + e.layer) * e.kv.layer_bytes;
     const size_t HS = (size_t)e.kv.H * e.kv.cap;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int n = min(nbw0 + j, NB - 1) * 16 + l16;
-      const int sec = e.sec_base + n / d, hh = (n % d) / hd, p = n % hd;
+      const int sec = e.sec_base + n / d, p = n % hd;
       const bool first = (p & 15) < 8;
       const int t = 8 * (p >> 4) + (p & 7);
-      const int dim = first ? t : half + t;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -563,54 +592,55 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
             rope_pair(first ? v : other, first ? other : v, c, sn, &y1, &y2);
             y = (float)(first ? y1 : y2);
           }
-          const uint16_t hv = f2h(y);
-          if (m < M && nbw0 + j < NB) {
-            if (sec == 0)
-              e.qout[(size_t)m * d + hh * hd + dim] = hv;
-            else
-              reinterpret_cast<uint16_t*>(base)[(sec == 2 ? HS * hd : 0) +
-                                                ((size_t)hh * e.kv.cap + kv_slot(e.kv, pos)) * hd + dim] = hv;
+          stage(i, rr, f2h(y));
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes land before its reads
+      if (nbw0 + j < NB) {
+        // columns 0..7 of the n-block are dims t0..t0+7 of its head, 8..15 are half+t0..
+        const int n0 = (nbw0 + j) * 16;
+        const int sec0 = e.sec_base + n0 / d, hh = (n0 % d) / hd, t0 = 8 * ((n0 % hd) >> 4);
+#pragma unroll
+        for (int c = lane; c < MB * 32; c += 64) {
+          const int r = c >> 1, hl = c & 1;
+          const int m = m0 + r;
+          const u32x4_t v8 = *reinterpret_cast<const u32x4_t*>(stg + r * 16 + hl * 8);
+          if (m < M) {
+            const int dim0 = hl ? half + t0 : t0;
+            uint16_t* dst = sec0 == 0 ? e.qout + (size_t)m * d + hh * hd + dim0
+                                      : reinterpret_cast<uint16_t*>(base) + (sec0 == 2 ? HS * hd : 0) +
+                                            ((size_t)hh * e.kv.cap + kv_slot(e.kv, e.p0 + m)) * hd + dim0;
+            *reinterpret_cast<u32x4_t*>(dst) = v8;
           }
         }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next n-block's writes
     }
     return;
   }
 
-  // ---- epilogue: lane holds C[m0 + 16i + 4lq + r][16*(nbw0 + j) + l16]
-  if (e.mode == EPI_RESID) {
-    // read every residual element first (one round trip), then write
+  if constexpr (EP == GEP_SWIGLU) {
+    if constexpr (NBW % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+      for (int j = 0; j < NBW; j += 2) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int m = min(m0 + i * 16 + 4 * lq + rr, M - 1);
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int n = min(nbw0 + j, NB - 1) * 16 + l16;
-          acc[i][j][rr] += e.out_f32[(size_t)m * e.ldo + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)];
+          for (int rr = 0; rr < 4; ++rr) stage(i, rr, f2h(silu(acc[i][j][rr]) * acc[i][j + 1][rr]));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (nbw0 + j < NB) {
+          const int c0 = ((nbw0 + j) >> 1) * 16;
+#pragma unroll
+          for (int c = lane; c < MB * 32; c += 64) {
+            const int r = c >> 1, hl = c & 1;
+            const int m = m0 + r;
+            const u32x4_t v8 = *reinterpret_cast<const u32x4_t*>(stg + r * 16 + hl * 8);
+            if (m < M) *reinterpret_cast<u32x4_t*>(e.out_f16 + (size_t)m * e.ldo + c0 + hl * 8) = v8;
+          }
         }
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int m = m0 + i * 16 + 4 * lq + rr;
-      if (m >= M) continue;
-      if (e.mode == EPI_SWIGLU) {
-        if constexpr (NBW % 2 == 0) {
-#pragma unroll
-          for (int j = 0; j < NBW; j += 2)
-            if (nbw0 + j < NB) epi_swiglu(e, m, ((nbw0 + j) >> 1) * 16 + l16, acc[i][j][rr], acc[i][j + 1][rr]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int n = (nbw0 + j) * 16 + l16;
-          if (nbw0 + j < NB) e.out_f32[(size_t)m * e.ldo + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n)] = acc[i][j][rr];
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
+    return;
   }
 }
 
@@ -665,16 +695,25 @@ hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float*
   return hipGetLastError();
 }
 
+template <int MB, int NBW, int EP>
+static hipError_t gemm_launch_ep(const Packed& w, const uint16_t* A, int M, const Epi& e, const GemmPlan& pl,
+                                 hipStream_t s) {
+  if (w.f16)
+    launch((w4_gemm_kernel<MB, NBW, true, EP>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G,
+           A, M, e, pl);
+  else
+    launch((w4_gemm_kernel<MB, NBW, false, EP>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G,
+           A, M, e, pl);
+  return hipGetLastError();
+}
 template <int MB, int NBW>
 static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const Epi& e, const GemmPlan& pl,
                               hipStream_t s) {
-  if (w.f16)
-    launch((w4_gemm_kernel<MB, NBW, true>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G, A, M,
-           e, pl);
-  else
-    launch((w4_gemm_kernel<MB, NBW, false>), dim3(pl.blocks), dim3(256), 0, s, w.tiles, w.scales, w.N, w.K, w.G, A,
-           M, e, pl);
-  return hipGetLastError();
+  if (pl.S > 1 || e.mode == EPI_STORE || e.mode == EPI_RESID) return gemm_launch_ep<MB, NBW, GEP_F32>(w, A, M, e, pl, s);
+  if (e.mode == EPI_QKV_ROPE) return gemm_launch_ep<MB, NBW, GEP_QKV>(w, A, M, e, pl, s);
+  if constexpr (NBW % 2 == 0)
+    if (e.mode == EPI_SWIGLU) return gemm_launch_ep<MB, NBW, GEP_SWIGLU>(w, A, M, e, pl, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s) {
@@ -687,20 +726,8 @@ hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& 
       return hipErrorInvalidValue;
   }
   pl.part = part;
-  if (pl.nbw == 2) {
-    switch (pl.mb) {
-      case 8: return gemm_launch<8, 2>(w, A, M, e, pl, s);
-      case 4: return gemm_launch<4, 2>(w, A, M, e, pl, s);
-      case 2: return gemm_launch<2, 2>(w, A, M, e, pl, s);
-      default: return gemm_launch<1, 2>(w, A, M, e, pl, s);
-    }
-  }
-  switch (pl.mb) {
-    case 8: return gemm_launch<8, 1>(w, A, M, e, pl, s);
-    case 4: return gemm_launch<4, 1>(w, A, M, e, pl, s);
-    case 2: return gemm_launch<2, 1>(w, A, M, e, pl, s);
-    default: return gemm_launch<1, 1>(w, A, M, e, pl, s);
-  }
+  if (pl.nbw == 2) return pl.mb == 2 ? gemm_launch<2, 2>(w, A, M, e, pl, s) : gemm_launch<1, 2>(w, A, M, e, pl, s);
+  return pl.mb == 2 ? gemm_launch<2, 1>(w, A, M, e, pl, s) : gemm_launch<1, 1>(w, A, M, e, pl, s);
 }
 
 }  // namespace tl

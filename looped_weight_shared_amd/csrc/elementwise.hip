@@ -109,6 +109,71 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pen
   }
 }
 
+// First layer of a prefill: x[m] = f32(E[tokens[m]]) and h[m] =
+// fp16(RMSNorm(x[m]) * gamma) in one pass (the same arithmetic as the embed
+// kernel followed by rmsnorm_kernel<CH, 0>, so the same bits).
+template <int CH>
+__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const uint16_t* __restrict__ E,
+                                                            const int32_t* __restrict__ tokens, float* __restrict__ x,
+                                                            const uint16_t* __restrict__ g, float eps, int d,
+                                                            uint16_t* __restrict__ h) {
+  __shared__ float part[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int nc = d / 4;
+  int cc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) cc[c] = min(tid + 256 * c, nc - 1);
+  uint2 gr[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) gr[c] = *reinterpret_cast<const uint2*>(g + 4 * cc[c]);
+  const uint2* er = reinterpret_cast<const uint2*>(E + (size_t)tokens[m] * d);
+  float4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint2 e4 = er[cc[c]];
+    v[c] = make_float4(h2f(e4.x & 0xFFFF), h2f(e4.x >> 16), h2f(e4.y & 0xFFFF), h2f(e4.y >> 16));
+  }
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    if (tid + 256 * c < nc) {
+      xr[cc[c]] = v[c];
+      acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+  acc = wave_sum(acc);
+  if ((tid & 63) == 0) part[tid >> 6] = acc;
+  __syncthreads();
+  const float ss = part[0] + part[1] + part[2] + part[3];
+  const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = tid + 256 * c;
+    if (ci >= nc) continue;
+    const int k = ci * 4;
+    const float g0 = h2f(gr[c].x & 0xFFFF), g1 = h2f(gr[c].x >> 16), g2 = h2f(gr[c].y & 0xFFFF), g3 = h2f(gr[c].y >> 16);
+    const uint32_t lo = (uint32_t)f2h((v[c].x * rinv) * g0) | ((uint32_t)f2h((v[c].y * rinv) * g1) << 16);
+    const uint32_t hi = (uint32_t)f2h((v[c].z * rinv) * g2) | ((uint32_t)f2h((v[c].w * rinv) * g3) << 16);
+    *reinterpret_cast<uint2*>(h + (size_t)m * d + k) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int M, int d, float* x,
+                                const uint16_t* gamma, float eps, uint16_t* h, hipStream_t s) {
+  if (M < 1) return hipSuccess;
+  if (d % 4 || d < 4 || d > 8192) return hipErrorInvalidValue;
+  const int ch = (d / 4 + 255) / 256;
+  if (ch <= 1)
+    launch(embed_rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+  else if (ch <= 2)
+    launch(embed_rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+  else if (ch <= 4)
+    launch(embed_rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+  else
+    launch(embed_rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+  return hipGetLastError();
+}
+
 template <int CH>
 static hipError_t rmsnorm_splits(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
                                  hipStream_t s) {

@@ -183,6 +183,7 @@ struct tl_ctx {
   // when a later call has the same shape and pointers (cuts host enqueue
   // time; the GPU time per step is not lower than eager launches)
   bool graphs = false;
+  bool h_ready = false;  // c->h holds the next linear's normalised input (fused embed + RMSNorm)
   hipStream_t cap_stream = nullptr;  // capture only; default priority
   struct PrefillGraph {
     bool valid = false;
@@ -228,6 +229,16 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
   // the GEMV's fused RMSNorm reads x as is: pending split-K residual partials
   // (left by a GEMM) must go through the RMSNorm kernel first
   const bool pending = src.x32 && c->pend.part;
+  if (c->h_ready && src.x32) {  // h = fp16(RMSNorm(x) * gamma) is already in place
+    c->h_ready = false;
+    const bool alt = gemm_epi != nullptr;
+    const int S = alt ? 1 : tl::plan_w4_gemm(w.N, w.K, M, e.mode == tl::EPI_SWIGLU).S;
+    KScope k(c, kind, s);
+    TL_HIP(tl::launch_w4_gemm(w, c->h, M, alt ? *gemm_epi : e, c->gpart, s));
+    *S_out = S;
+    if (used_gemm_epi) *used_gemm_epi = alt;
+    return TL_OK;
+  }
   if (!pending && tl::gemv_supported(M, w.K, src)) {
     KScope k(c, kind, s);
     TL_HIP(tl::launch_w4_gemv(w, src, M, e, s));
@@ -645,11 +656,20 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   rm.p0 = p0;
   const int d = C.d_model;
   const bool safe = ctx->safety_max > 0.f;
+  ctx->h_ready = false;
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
   }
-  {
+  // embedding gather; when the first layer's QKV runs as a GEMM (n > 8 rows,
+  // K/V stored), fused with that layer's RMSNorm
+  const tl::ASrc first{nullptr, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps};
+  if (C.n_pre + L > 0 && !ctx->hmode && !tl::gemv_supported(n, d, first)) {
+    KScope k(ctx, TL_K_EMBED, s);
+    TL_HIP(tl::launch_embed_rmsnorm(ctx->embed, d_tokens, n, d, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps, ctx->h,
+                                    s));
+    ctx->h_ready = true;
+  } else {
     KScope k(ctx, TL_K_EMBED, s);
     TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
   }
@@ -818,6 +838,7 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int d = C.d_model;
   const bool safe = ctx->safety_max > 0.f;
+  ctx->h_ready = false;
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));

@@ -145,6 +145,10 @@ struct Pending {
   const float* part;  // [S][M][d] or null
   int S;
 };
+// First layer of a prefill: x [M][d] = f32(embed[tokens[m]]) and fp16 h =
+// RMSNorm(x) * gamma, bit-identical to launch_embed then launch_rmsnorm.
+hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int M, int d, float* x,
+                                const uint16_t* gamma, float eps, uint16_t* h, hipStream_t s);
 // x += pending (if any), then fp16 h [M][d] = RMSNorm(x) (prefill path).
 hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
                           hipStream_t s);

@@ -184,6 +184,10 @@ struct tl_ctx {
   // time; the GPU time per step is not lower than eager launches)
   bool graphs = false;
   bool h_ready = false;  // c->h holds the next linear's normalised input (fused embed + RMSNorm)
+  // the first layer's rows are still the embedding rows of these tokens (the
+  // first GEMV reads them directly and writes x); emb_rm maps row -> token
+  const int32_t* emb_tokens = nullptr;
+  tl::RowMap emb_rm{};
   hipStream_t cap_stream = nullptr;  // capture only; default priority
   struct PrefillGraph {
     bool valid = false;
@@ -229,6 +233,20 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
   // the GEMV's fused RMSNorm reads x as is: pending split-K residual partials
   // (left by a GEMM) must go through the RMSNorm kernel first
   const bool pending = src.x32 && c->pend.part;
+  if (c->emb_tokens && src.x32) {  // first layer: the GEMV gathers the embedding rows itself
+    tl::ASrc se = src;
+    se.emb = c->embed;
+    se.tok = c->emb_tokens;
+    for (int m = 0; m < M && m < 8; ++m) se.tok_idx[m] = c->emb_rm.per_row ? c->emb_rm.row_lane[m] : m;
+    c->emb_tokens = nullptr;
+    if (!pending && tl::gemv_supported(M, w.K, se)) {
+      KScope k(c, kind, s);
+      TL_HIP(tl::launch_w4_gemv(w, se, M, e, s));
+      return TL_OK;
+    }
+    KScope k(c, TL_K_EMBED, s);
+    TL_HIP(tl::launch_embed(c->embed, se.tok, M, c->emb_rm, w.K, c->x, s));
+  }
   if (c->h_ready && src.x32) {  // h = fp16(RMSNorm(x) * gamma) is already in place
     c->h_ready = false;
     const bool alt = gemm_epi != nullptr;
@@ -657,6 +675,7 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   const int d = C.d_model;
   const bool safe = ctx->safety_max > 0.f;
   ctx->h_ready = false;
+  ctx->emb_tokens = nullptr;
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
@@ -669,6 +688,9 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
     TL_HIP(tl::launch_embed_rmsnorm(ctx->embed, d_tokens, n, d, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps, ctx->h,
                                     s));
     ctx->h_ready = true;
+  } else if (C.n_pre + L > 0 && !ctx->hmode) {
+    ctx->emb_tokens = d_tokens;  // the first layer's QKV GEMV gathers the rows
+    ctx->emb_rm = rm;
   } else {
     KScope k(ctx, TL_K_EMBED, s);
     TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
@@ -839,15 +861,19 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   const int d = C.d_model;
   const bool safe = ctx->safety_max > 0.f;
   ctx->h_ready = false;
+  ctx->emb_tokens = nullptr;
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
   }
-  {
+  const int Lmax = ctx->loops[rows[0]];
+  if (C.n_pre + Lmax > 0 && !ctx->hmode) {
+    ctx->emb_tokens = d_tokens;  // the first layer's QKV GEMV gathers the rows
+    ctx->emb_rm = rm;
+  } else {
     KScope k(ctx, TL_K_EMBED, s);
     TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
   }
-  const int Lmax = ctx->loops[rows[0]];
   for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
     int Ml = 0;
     while (Ml < M && C.n_pre + ctx->loops[rows[Ml]] > layer) ++Ml;

@@ -114,6 +114,11 @@ struct ASrc {
   // decode attention parts to merge into fp16 A rows (K = H * att_hd)
   const float* att = nullptr;
   int att_np = 0, att_np_max = 0, att_hd = 0;
+  // with x32 and emb set (GEMV, first layer): row m is f32(emb[tok[tok_idx[m]]])
+  // instead of x32's row, and the kernel writes it to x32 (the residual)
+  const uint16_t* emb = nullptr;
+  const int32_t* tok = nullptr;
+  int tok_idx[8] = {};
 };
 
 // C = A * W^T for M <= 8 rows (decode GEMV shape); K split across waves.

@@ -71,14 +71,16 @@ __device__ __forceinline__ void lds_barrier() {
 // fp16 activation chunks per thread (fp16 input). All requests are
 // unconditional with clamped addresses, so the code between them is
 // straight-line and the compiler's waits stay exact.
-enum GemvSrc { SRC_A16 = 0, SRC_NORM = 1, SRC_ATT = 2 };
+enum GemvSrc { SRC_A16 = 0, SRC_NORM = 1, SRC_ATT = 2, SRC_EMB = 3 };
 
 template <int NBB, int SRC, int MR, int GI, int APT, bool F16>
 __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __restrict__ tiles,
                                                                const uint16_t* __restrict__ scales, int N, int K,
                                                                int G, ASrc a, int M, Epi e) {
   constexpr int WK = kGemvWaves;
-  constexpr bool NORM = SRC == SRC_NORM, ATT = SRC == SRC_ATT;
+  // SRC_EMB: the rows are the embedding rows of the tokens (first layer),
+  // normalised as SRC_NORM does; block 0 also writes them to x32
+  constexpr bool EMB = SRC == SRC_EMB, NORM = SRC == SRC_NORM || EMB, ATT = SRC == SRC_ATT;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float red[WK * NBB * 256];
   __shared__ float nrm[WK][MR];
@@ -99,7 +101,17 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   const int kc = min(k4, K - 4);
   const int chunks = K / 8, nch = M * chunks;
   const int npairs = M * a.att_np;  // ATT: (row, part) pairs, row-major
-  if constexpr (NORM) {
+  if constexpr (EMB) {
+    int tk[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) tk[m] = a.tok[a.tok_idx[min(m, M - 1)]];
+    gr = *reinterpret_cast<const uint2*>(a.gamma + kc);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint2 e4 = *reinterpret_cast<const uint2*>(a.emb + (size_t)tk[m] * K + kc);
+      xv[m] = (float4_t){h2f(e4.x & 0xFFFF), h2f(e4.x >> 16), h2f(e4.y & 0xFFFF), h2f(e4.y >> 16)};
+    }
+  } else if constexpr (NORM) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) xv[m] = *reinterpret_cast<const float4_t*>(a.x32 + (size_t)min(m, M - 1) * K + kc);
     gr = *reinterpret_cast<const uint2*>(a.gamma + kc);
@@ -156,6 +168,12 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   }
 
   // ---- 3. activations into LDS
+  if constexpr (EMB) {  // the first layer's residual rows
+    if (blockIdx.x == 0 && k4 < K)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (m < M) *reinterpret_cast<float4_t*>(const_cast<float*>(a.x32) + (size_t)m * K + k4) = xv[m];
+  }
   if constexpr (NORM) {
     const bool kin = k4 < K;
 #pragma unroll
@@ -289,7 +307,7 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
 bool gemv_supported(int M, int K, const ASrc& a) {
   const int G = (K + 127) / 128;
   if (M < 1 || M > 8 || K < 8 || K % 8) return false;
-  if (a.x32) return K <= 4 * kGemvThreads;  // one float4 per thread and row
+  if (a.x32) return K <= 4 * kGemvThreads && (!a.emb || a.tok);  // one float4 per thread and row
   if (a.att)
     return K <= 4 * kGemvThreads && a.att_hd >= 4 && a.att_hd % 4 == 0 && K % a.att_hd == 0 && a.att_np >= 1 &&
            M * a.att_np <= 16;
@@ -314,6 +332,15 @@ template <int NBB, int SRC, int MR, int GI, int APT>
 static hipError_t gemv_launch(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
   return w.f16 ? gemv_launch_t<NBB, SRC, MR, GI, APT, true>(w, a, M, e, s)
                : gemv_launch_t<NBB, SRC, MR, GI, APT, false>(w, a, M, e, s);
+}
+
+// the first layer's rows from the embedding (x written by block 0)
+template <int NBB>
+static hipError_t gemv_emb_rows(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
+  if (M == 1) return gemv_launch<NBB, SRC_EMB, 1, 2, 1>(w, a, M, e, s);
+  if (M == 2) return gemv_launch<NBB, SRC_EMB, 2, 2, 1>(w, a, M, e, s);
+  if (M <= 4) return gemv_launch<NBB, SRC_EMB, 4, 2, 1>(w, a, M, e, s);
+  return gemv_launch<NBB, SRC_EMB, 8, 2, 1>(w, a, M, e, s);
 }
 
 // fused RMSNorm: K <= 2048, so at most 2 groups per wave
@@ -347,6 +374,7 @@ static hipError_t gemv_a16(const Packed& w, const ASrc& a, int M, const Epi& e, 
 
 hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, hipStream_t s) {
   if (!gemv_supported(M, w.K, a) || e.mode == EPI_QKV_ROPE) return hipErrorInvalidValue;
+  if (a.emb) return e.mode == EPI_SWIGLU ? hipErrorInvalidValue : gemv_emb_rows<1>(w, a, M, e, s);
   if (a.x32) return e.mode == EPI_SWIGLU ? gemv_norm_rows<2>(w, a, M, e, s) : gemv_norm_rows<1>(w, a, M, e, s);
   if (e.mode == EPI_SWIGLU) return hipErrorInvalidValue;
   if (a.att) return gemv_att(w, a, M, e, s);

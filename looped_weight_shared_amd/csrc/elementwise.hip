@@ -28,11 +28,17 @@ hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, con
 }
 
 // ------------------------------------------------------------------ RMSNorm
-// One block (256 threads) per row: x += the pending split-K partials of the
-// residual GEMM that produced x (split order), then h = fp16(gamma * x /
-// sqrt(mean(x^2) + eps)). Thread t owns the float4 chunks t, t + 256, ...
+// One block (kNormThreads threads) per row: x += the pending split-K partials
+// of the residual GEMM that produced x (split order), then h = fp16(gamma * x
+// / sqrt(mean(x^2) + eps)). Thread t owns the float4 chunks t, t + 512, ...
 // (CH of them); every load is issued before the first store.
 constexpr int kMaxSplits = kMaxSplitK;
+// 512 threads per row (one float4 of a 2048-wide row each) measured 0.3%
+// faster per prefill than 256; the 8 wave sums are added pairwise.
+constexpr int kNormThreads = 512;
+__device__ __forceinline__ float norm_parts(const float* part) {
+  return ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+}
 
 // One block per row. Every load is issued first (clamped addresses, no
 // branches): the row of x, the SP pending split partials (SP = 0: none; a
@@ -40,16 +46,16 @@ constexpr int kMaxSplits = kMaxSplitK;
 // selected out), and the gains. x += the partials summed in split order,
 // then h = fp16(x * rinv * gamma).
 template <int CH, int SP>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pending pend, int M,
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float* __restrict__ x, Pending pend, int M,
                                                       const uint16_t* __restrict__ g, float eps, int d,
                                                       uint16_t* __restrict__ h) {
-  __shared__ float part[4];
+  __shared__ float part[kNormThreads / 64];
   const int m = blockIdx.x, tid = threadIdx.x;
   float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
   const int nc = d / 4;
   int cc[CH];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) cc[c] = min(tid + 256 * c, nc - 1);
+  for (int c = 0; c < CH; ++c) cc[c] = min(tid + kNormThreads * c, nc - 1);
   float4 v[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) v[c] = xr[cc[c]];
@@ -84,22 +90,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pen
       v[c].y += a.y;
       v[c].z += a.z;
       v[c].w += a.w;
-      if (tid + 256 * c < nc) xr[cc[c]] = v[c];
+      if (tid + kNormThreads * c < nc) xr[cc[c]] = v[c];
     }
   }
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c)
-    if (tid + 256 * c < nc) acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    if (tid + kNormThreads * c < nc) acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   acc = wave_sum(acc);
   if ((tid & 63) == 0) part[tid >> 6] = acc;
   __syncthreads();
-  const float ss = part[0] + part[1] + part[2] + part[3];
+  const float ss = norm_parts(part);
   const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
   if (!h) return;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int ci = tid + 256 * c;
+    const int ci = tid + kNormThreads * c;
     if (ci >= nc) continue;
     const int k = ci * 4;
     const float g0 = h2f(gr[c].x & 0xFFFF), g1 = h2f(gr[c].x >> 16), g2 = h2f(gr[c].y & 0xFFFF), g3 = h2f(gr[c].y >> 16);
@@ -113,16 +119,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, Pen
 // fp16(RMSNorm(x[m]) * gamma) in one pass (the same arithmetic as the embed
 // kernel followed by rmsnorm_kernel<CH, 0>, so the same bits).
 template <int CH>
-__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const uint16_t* __restrict__ E,
+__global__ __launch_bounds__(kNormThreads) void embed_rmsnorm_kernel(const uint16_t* __restrict__ E,
                                                             const int32_t* __restrict__ tokens, float* __restrict__ x,
                                                             const uint16_t* __restrict__ g, float eps, int d,
                                                             uint16_t* __restrict__ h) {
-  __shared__ float part[4];
+  __shared__ float part[kNormThreads / 64];
   const int m = blockIdx.x, tid = threadIdx.x;
   const int nc = d / 4;
   int cc[CH];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) cc[c] = min(tid + 256 * c, nc - 1);
+  for (int c = 0; c < CH; ++c) cc[c] = min(tid + kNormThreads * c, nc - 1);
   uint2 gr[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) gr[c] = *reinterpret_cast<const uint2*>(g + 4 * cc[c]);
@@ -137,18 +143,18 @@ __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(const uint16_t* __re
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c)
-    if (tid + 256 * c < nc) {
+    if (tid + kNormThreads * c < nc) {
       xr[cc[c]] = v[c];
       acc += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
     }
   acc = wave_sum(acc);
   if ((tid & 63) == 0) part[tid >> 6] = acc;
   __syncthreads();
-  const float ss = part[0] + part[1] + part[2] + part[3];
+  const float ss = norm_parts(part);
   const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int ci = tid + 256 * c;
+    const int ci = tid + kNormThreads * c;
     if (ci >= nc) continue;
     const int k = ci * 4;
     const float g0 = h2f(gr[c].x & 0xFFFF), g1 = h2f(gr[c].x >> 16), g2 = h2f(gr[c].y & 0xFFFF), g3 = h2f(gr[c].y >> 16);
@@ -162,15 +168,15 @@ hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, in
                                 const uint16_t* gamma, float eps, uint16_t* h, hipStream_t s) {
   if (M < 1) return hipSuccess;
   if (d % 4 || d < 4 || d > 8192) return hipErrorInvalidValue;
-  const int ch = (d / 4 + 255) / 256;
+  const int ch = (d / 4 + kNormThreads - 1) / kNormThreads;
   if (ch <= 1)
-    launch(embed_rmsnorm_kernel<1>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<1>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
   else if (ch <= 2)
-    launch(embed_rmsnorm_kernel<2>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<2>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
   else if (ch <= 4)
-    launch(embed_rmsnorm_kernel<4>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<4>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
   else
-    launch(embed_rmsnorm_kernel<8>, dim3(M), dim3(256), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<8>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
   return hipGetLastError();
 }
 
@@ -179,15 +185,15 @@ static hipError_t rmsnorm_splits(float* x, Pending pend, const uint16_t* gamma, 
                                  hipStream_t s) {
   const int S = pend.part ? pend.S : 0;
   if (S == 0)
-    launch(rmsnorm_kernel<CH, 0>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<CH, 0>, dim3(M), dim3(kNormThreads), 0, s, x, pend, M, gamma, eps, d, h);
   else if (S <= 2)
-    launch(rmsnorm_kernel<CH, 2>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<CH, 2>, dim3(M), dim3(kNormThreads), 0, s, x, pend, M, gamma, eps, d, h);
   else if (S <= 4)
-    launch(rmsnorm_kernel<CH, 4>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<CH, 4>, dim3(M), dim3(kNormThreads), 0, s, x, pend, M, gamma, eps, d, h);
   else if (S <= 8)
-    launch(rmsnorm_kernel<CH, 8>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<CH, 8>, dim3(M), dim3(kNormThreads), 0, s, x, pend, M, gamma, eps, d, h);
   else
-    launch(rmsnorm_kernel<CH, 16>, dim3(M), dim3(256), 0, s, x, pend, M, gamma, eps, d, h);
+    launch(rmsnorm_kernel<CH, 16>, dim3(M), dim3(kNormThreads), 0, s, x, pend, M, gamma, eps, d, h);
   return hipGetLastError();
 }
 
@@ -195,7 +201,7 @@ hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float e
                           hipStream_t s) {
   if (M < 1) return hipSuccess;
   if (d % 4 || d < 4 || d > 8192 || (pend.part && (pend.S < 1 || pend.S > kMaxSplits))) return hipErrorInvalidValue;
-  const int ch = (d / 4 + 255) / 256;
+  const int ch = (d / 4 + kNormThreads - 1) / kNormThreads;
   if (ch <= 1) return rmsnorm_splits<1>(x, pend, gamma, eps, M, d, h, s);
   if (ch <= 2) return rmsnorm_splits<2>(x, pend, gamma, eps, M, d, h, s);
   if (ch <= 4) return rmsnorm_splits<4>(x, pend, gamma, eps, M, d, h, s);

@@ -6,8 +6,9 @@
 // INT8"). Attention always reads what the cache holds, so an INT8 cache is
 // read back as q * s in the prefill too (cached and uncached paths agree).
 //
-// Prefill: a block takes 64 queries of one head (4 waves x 16 rows) and walks
-// 128-key tiles up to its causal limit: K tile and transposed V tile staged in
+// Prefill: a block takes 64 queries of one head (8 waves: 4 groups of 16
+// rows x 2 halves of each key tile) and walks 128-key tiles up to its causal
+// limit: K tile and transposed V tile staged in
 // LDS, S = Q K^T and O += P V on v_mfma_f32_16x16x32_f16, online softmax in
 // fp32 (running max and sum per row). INT8 codes are exact in fp16, so the
 // MFMAs run on the codes and the per-key scales multiply the score columns

@@ -26,8 +26,9 @@
  *    on the host before anything is enqueued and leave all state unchanged;
  *    a failing HIP call returns TL_E_HIP. tl_last_error() gives a message for
  *    the last failure on the calling thread. No C++ exception crosses the ABI.
- *  - Token ids are not range-checked on the device: an id outside
- *    [0, vocab) is the caller's error.
+ *  - Token ids in device buffers are not checked against [0, vocab) by the
+ *    host; the kernels clamp an id outside that range into it (no
+ *    out-of-bounds read), and the result is then that of the clamped id.
  *  - A tl_ctx is not thread-safe. Identical calls give bit-identical results;
  *    a lane's results do not depend on which other lanes run in the same
  *    decode step.

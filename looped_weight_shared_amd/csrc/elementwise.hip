@@ -14,16 +14,16 @@ __device__ __forceinline__ int out_row(const RowMap& rm, int m) { return rm.per_
 // ------------------------------------------------------------------ embed
 // x[m] = f32(E[token]); decode rows read the token of their lane.
 __global__ void embed_kernel(const uint16_t* __restrict__ E, const int32_t* __restrict__ tokens, RowMap rm, int d,
-                             float* __restrict__ x) {
+                             int V, float* __restrict__ x) {
   const int m = blockIdx.x;
-  const int tok = tokens[rm.per_row ? rm.row_lane[m] : m];
+  const int tok = min(max(tokens[rm.per_row ? rm.row_lane[m] : m], 0), V - 1);  // ids outside [0, V) clamped
   const uint16_t* er = E + (size_t)tok * d;
   for (int k = threadIdx.x; k < d; k += blockDim.x) x[(size_t)m * d + k] = h2f(er[k]);
 }
 
-hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d, float* x,
+hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d, int V, float* x,
                         hipStream_t s) {
-  launch(embed_kernel, dim3(M), dim3(256), 0, s, embed, tokens, rm, d, x);
+  launch(embed_kernel, dim3(M), dim3(256), 0, s, embed, tokens, rm, d, V, x);
   return hipGetLastError();
 }
 
@@ -120,9 +120,9 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(float* __restrict
 // kernel followed by rmsnorm_kernel<CH, 0>, so the same bits).
 template <int CH>
 __global__ __launch_bounds__(kNormThreads) void embed_rmsnorm_kernel(const uint16_t* __restrict__ E,
-                                                            const int32_t* __restrict__ tokens, float* __restrict__ x,
-                                                            const uint16_t* __restrict__ g, float eps, int d,
-                                                            uint16_t* __restrict__ h) {
+                                                            const int32_t* __restrict__ tokens, int V,
+                                                            float* __restrict__ x, const uint16_t* __restrict__ g,
+                                                            float eps, int d, uint16_t* __restrict__ h) {
   __shared__ float part[kNormThreads / 64];
   const int m = blockIdx.x, tid = threadIdx.x;
   const int nc = d / 4;
@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kNormThreads) void embed_rmsnorm_kernel(const uint1
   uint2 gr[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) gr[c] = *reinterpret_cast<const uint2*>(g + 4 * cc[c]);
-  const uint2* er = reinterpret_cast<const uint2*>(E + (size_t)tokens[m] * d);
+  const int tok = min(max(tokens[m], 0), V - 1);  // ids outside [0, V) clamped
+  const uint2* er = reinterpret_cast<const uint2*>(E + (size_t)tok * d);
   float4 v[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -164,19 +165,19 @@ __global__ __launch_bounds__(kNormThreads) void embed_rmsnorm_kernel(const uint1
   }
 }
 
-hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int M, int d, float* x,
+hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int V, int M, int d, float* x,
                                 const uint16_t* gamma, float eps, uint16_t* h, hipStream_t s) {
   if (M < 1) return hipSuccess;
   if (d % 4 || d < 4 || d > 8192) return hipErrorInvalidValue;
   const int ch = (d / 4 + kNormThreads - 1) / kNormThreads;
   if (ch <= 1)
-    launch(embed_rmsnorm_kernel<1>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<1>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, V, x, gamma, eps, d, h);
   else if (ch <= 2)
-    launch(embed_rmsnorm_kernel<2>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<2>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, V, x, gamma, eps, d, h);
   else if (ch <= 4)
-    launch(embed_rmsnorm_kernel<4>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<4>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, V, x, gamma, eps, d, h);
   else
-    launch(embed_rmsnorm_kernel<8>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, x, gamma, eps, d, h);
+    launch(embed_rmsnorm_kernel<8>, dim3(M), dim3(kNormThreads), 0, s, embed, tokens, V, x, gamma, eps, d, h);
   return hipGetLastError();
 }
 

@@ -237,6 +237,7 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
     tl::ASrc se = src;
     se.emb = c->embed;
     se.tok = c->emb_tokens;
+    se.vocab = c->cfg.vocab;
     for (int m = 0; m < M && m < 8; ++m) se.tok_idx[m] = c->emb_rm.per_row ? c->emb_rm.row_lane[m] : m;
     c->emb_tokens = nullptr;
     if (!pending && tl::gemv_supported(M, w.K, se)) {
@@ -245,7 +246,7 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
       return TL_OK;
     }
     KScope k(c, TL_K_EMBED, s);
-    TL_HIP(tl::launch_embed(c->embed, se.tok, M, c->emb_rm, w.K, c->x, s));
+    TL_HIP(tl::launch_embed(c->embed, se.tok, M, c->emb_rm, w.K, c->cfg.vocab, c->x, s));
   }
   if (c->h_ready && src.x32) {  // h = fp16(RMSNorm(x) * gamma) is already in place
     c->h_ready = false;
@@ -685,15 +686,15 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   const tl::ASrc first{nullptr, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps};
   if (C.n_pre + L > 0 && !ctx->hmode && !tl::gemv_supported(n, d, first)) {
     KScope k(ctx, TL_K_EMBED, s);
-    TL_HIP(tl::launch_embed_rmsnorm(ctx->embed, d_tokens, n, d, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps, ctx->h,
-                                    s));
+    TL_HIP(tl::launch_embed_rmsnorm(ctx->embed, d_tokens, C.vocab, n, d, ctx->x, ctx->blocks[0].attn_norm, C.rms_eps,
+                                    ctx->h, s));
     ctx->h_ready = true;
   } else if (C.n_pre + L > 0 && !ctx->hmode) {
     ctx->emb_tokens = d_tokens;  // the first layer's QKV GEMV gathers the rows
     ctx->emb_rm = rm;
   } else {
     KScope k(ctx, TL_K_EMBED, s);
-    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, ctx->x, s));
+    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, n, rm, d, C.vocab, ctx->x, s));
   }
   for (int layer = 0; layer < C.n_pre + L; ++layer) {
     const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
@@ -872,7 +873,7 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
     ctx->emb_rm = rm;
   } else {
     KScope k(ctx, TL_K_EMBED, s);
-    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, ctx->x, s));
+    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, C.vocab, ctx->x, s));
   }
   for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
     int Ml = 0;

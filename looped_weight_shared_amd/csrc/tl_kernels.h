@@ -117,8 +117,9 @@ struct ASrc {
   // with x32 and emb set (GEMV, first layer): row m is f32(emb[tok[tok_idx[m]]])
   // instead of x32's row, and the kernel writes it to x32 (the residual)
   const uint16_t* emb = nullptr;
-  const int32_t* tok = nullptr;
+  const int32_t* tok = nullptr;  // ids outside [0, vocab) are clamped
   int tok_idx[8] = {};
+  int vocab = 0;
 };
 
 // C = A * W^T for M <= 8 rows (decode GEMV shape); K split across waves.
@@ -152,7 +153,7 @@ struct Pending {
 };
 // First layer of a prefill: x [M][d] = f32(embed[tokens[m]]) and fp16 h =
 // RMSNorm(x) * gamma, bit-identical to launch_embed then launch_rmsnorm.
-hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int M, int d, float* x,
+hipError_t launch_embed_rmsnorm(const uint16_t* embed, const int32_t* tokens, int V, int M, int d, float* x,
                                 const uint16_t* gamma, float eps, uint16_t* h, hipStream_t s);
 // x += pending (if any), then fp16 h [M][d] = RMSNorm(x) (prefill path).
 hipError_t launch_rmsnorm(float* x, Pending pend, const uint16_t* gamma, float eps, int M, int d, uint16_t* h,
@@ -190,7 +191,8 @@ int attn_decode_np_max(int S);                  // part slots per (row, head)
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s);
 
-hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d,
+// Token ids outside [0, V) are clamped into range (no out-of-bounds read).
+hipError_t launch_embed(const uint16_t* embed, const int32_t* tokens, int M, const RowMap& rm, int d, int V,
                         float* x, hipStream_t s);
 // Final RMSNorm of the residual rows x [M][d] (M <= 8, d <= 2048), logits
 // against the head in tile order (launch_pack_head) written at

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
   if constexpr (EMB) {
     int tk[MR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) tk[m] = a.tok[a.tok_idx[min(m, M - 1)]];
+    for (int m = 0; m < MR; ++m) tk[m] = min(max(a.tok[a.tok_idx[min(m, M - 1)]], 0), a.vocab - 1);
     gr = *reinterpret_cast<const uint2*>(a.gamma + kc);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
 bool gemv_supported(int M, int K, const ASrc& a) {
   const int G = (K + 127) / 128;
   if (M < 1 || M > 8 || K < 8 || K % 8) return false;
-  if (a.x32) return K <= 4 * kGemvThreads && (!a.emb || a.tok);  // one float4 per thread and row
+  if (a.x32) return K <= 4 * kGemvThreads && (!a.emb || (a.tok && a.vocab > 0));  // one float4 per thread and row
   if (a.att)
     return K <= 4 * kGemvThreads && a.att_hd >= 4 && a.att_hd % 4 == 0 && K % a.att_hd == 0 && a.att_np >= 1 &&
            M * a.att_np <= 16;

@@ -337,3 +337,28 @@ def test_no_device_memory_growth(tiny):
         if i == 1:
             base = torch.cuda.memory_allocated()
     assert torch.cuda.memory_allocated() == base
+
+
+def test_out_of_range_token_ids_are_clamped(tiny):
+    """Token ids outside [0, vocab) read the row of the clamped id (the
+    kernels never index the embedding out of bounds): the same bits as ids 0
+    and vocab - 1, through the short-prefill GEMV path (5 rows), the GEMM
+    path (20 rows) and a decode step."""
+    w, _ = tiny
+    V = w["shape"].vocab
+    for n in (5, 20):
+        good = synth.make_tokens(V, n, seed=3)
+        bad, fix = good.copy(), good.copy()
+        bad[0], bad[-1] = -5, V + 7
+        fix[0], fix[-1] = 0, V - 1
+        outs = []
+        for toks, nxt in ((bad, V + 100), (fix, V - 1)):
+            m = _tiny_model(w)
+            m.set_loops(0, 2)
+            g = GpuRun(m)
+            h, lg, _ = g.prefill(toks)
+            h2, lg2, _ = g.step(nxt)
+            outs.append((h, lg, h2, lg2))
+            m.close()
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b)

@@ -141,6 +141,93 @@ def tl_packed_bytes(N, K):
     return (N // 16) * ((K + 127) // 128) * 1056
 
 
+def _layer_flops(s, M):
+    """Algorithmic flop of one effective layer over M prompt rows: the four
+    W4 GEMMs (2*M*N*K) and causal attention (4*H*hd*M(M+1)/2)."""
+    d, f = s.d_model, s.ffn_dim
+    gemm = 2 * M * (3 * d * d + d * d + 2 * f * d + d * f)
+    return gemm + 4 * s.n_heads * s.head_dim * M * (M + 1) // 2
+
+
+def other_configs(s, w, tl, Model, torch, synth, stream):
+    """The 407M workloads besides the headline one: seq-1024 prefill at L=16
+    and 32 (tokens/s against the MFMA roofline), and cached greedy decode at
+    context 2048 with an INT8 KV cache (prompt 1920 + 128 steps), one lane at
+    L=8 and three lanes at L=4/16/32 decoded together (against the HBM
+    roofline of their algorithmic bytes)."""
+    res = {}
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    M = 1024
+    t1024 = torch.from_numpy(synth.make_tokens(s.vocab, M, seed=0)).cuda()
+    for Lx in (16, 32):
+        mx = Model(w, max_seq=2048, max_loops=Lx, n_lanes=1, kv_dtype=tl.TL_KV_FP16, max_tokens=M)
+        mx.set_loops(0, Lx)
+
+        def step():
+            mx.reset(0)
+            mx.prefill(t1024)
+        for _ in range(2):
+            step()
+        ms = timed(step, 5)
+        flop = _layer_flops(s, M) * (s.n_pre + Lx)
+        roof_us = flop / (PEAK_F16_TFLOPS * 1e12) * 1e6
+        res[f"prefill_seq{M}_L{Lx}"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(M / ms * 1e3, 1),
+                                        "gflop": round(flop / 1e9, 1), "mfma_roofline_us": round(roof_us, 1),
+                                        "frac": round(roof_us / (ms * 1e3), 4)}
+        print(f"[bench] prefill seq {M} L={Lx}: {ms:.3f} ms/step, {M / ms * 1e3:,.0f} tok/s "
+              f"({roof_us / (ms * 1e3):.1%} of the MFMA roofline)", file=sys.stderr, flush=True)
+        mx.close()
+
+    P, D = 1920, 128
+    wbytes = (tl.tl_qlinear_packed_bytes(3 * s.d_model, s.d_model) + tl.tl_qlinear_packed_bytes(s.d_model, s.d_model)
+              + tl.tl_qlinear_packed_bytes(2 * s.ffn_dim, s.d_model)
+              + tl.tl_qlinear_packed_bytes(s.d_model, s.ffn_dim))
+    kv_per_tok = 2 * s.n_heads * (s.head_dim + 2)  # INT8 K and V rows plus their fp16 scales, one layer
+    for name, loops in (("decode_int8_ctx2048_L8", [8]), ("decode_int8_ctx2048_3lanes_L4_16_32", [4, 16, 32])):
+        nl = len(loops)
+        mi = Model(w, max_seq=2048, max_loops=max(loops), n_lanes=nl, kv_dtype=tl.TL_KV_INT8, max_tokens=P)
+        bufs = [torch.zeros(nl, dtype=torch.int32, device="cuda") for _ in range(2)]
+
+        def prime():
+            for lane, Lx in enumerate(loops):
+                mi.reset(lane)
+                mi.set_loops(lane, Lx)
+                pt = torch.from_numpy(synth.make_tokens(s.vocab, P, seed=0, lane=lane)).cuda()
+                mi.prefill(pt, lane=lane, next_tok=bufs[0][lane:lane + 1])
+        prime()
+        for t in range(4):
+            mi.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+        prime()
+        it = iter(range(D))
+
+        def dstep():
+            t = next(it)
+            mi.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+        ms = timed(dstep, D)
+        # lanes decoded together share each layer's weight read (the deepest
+        # lane sets the layer count) and the head read; K/V are per lane
+        algo = (wbytes * (s.n_pre + max(loops)) + s.vocab * s.d_model * 2
+                + sum(kv_per_tok * (s.n_pre + Lx) * (P + D // 2) for Lx in loops))
+        roof_us = algo / (PEAK_HBM_GBS * 1e9) * 1e6
+        res[name] = {"ms_per_step": round(ms, 4), "lanes": nl, "loops": loops, "context": P + D,
+                     "algorithmic_bytes_per_step": int(algo), "hbm_roofline_us": round(roof_us, 1),
+                     "frac": round(roof_us / (ms * 1e3), 4)}
+        print(f"[bench] {name}: {ms:.4f} ms/step ({roof_us / (ms * 1e3):.1%} of the HBM roofline)",
+              file=sys.stderr, flush=True)
+        mi.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +241,9 @@ def main():
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
     ap.add_argument("--no-storeh", action="store_true", help="skip the store-h (TL_KV_H16) leg")
     ap.add_argument("--no-fp16body", action="store_true", help="skip the FP16-body leg")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
+                         "context 2048, one lane at L=8 and three lanes at L=4/16/32)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -393,6 +483,10 @@ def main():
             out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
                                   "note": "greedy; acceptance is a property of the weights (synthetic here)",
                                   **spec}
+
+    # ---------------------------------------------------------------- other workloads (opt-in)
+    if args.configs:
+        out["other_configs"] = other_configs(s, w, tl, Model, torch, synth, stream)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:

@@ -334,12 +334,13 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 }
 
 // ------------------------------------------------------------------ decode
-// A block (4 waves) covers 128 keys of the context 0..pos of one row's lane
-// for one head; wave w takes the 32-key chunk 4*blockIdx.x + w (4 waves of
-// 32 keys measured 4.5 us per layer at context 256-384 against 5.4 us for 2
-// waves of 64; smaller parts shorten the attention further but cost the O
-// projection more to merge). Lanes are 16 per key (8 dims each) x 4 keys per
-// pass. Order of work, so that no wait covers the cache reads:
+// A block of BW waves (4 or 8) covers BW * 32 keys of the visible context of
+// one row's lane for one head; wave w takes the 32-key chunk
+// BW*blockIdx.x + w (4 waves of 32 keys measured 4.5 us per layer at context
+// 256-384 against 5.4 us for 2 waves of 64; smaller parts shorten the
+// attention further but cost the O projection more to merge). Lanes are 16
+// per key (8 dims each) x 4 keys per pass (HD 128). Order of work, so that no
+// wait covers the cache reads:
 //   1. the row's q, k, v projections for this lane's 8 dims (and their RoPE
 //      partners) and the cos/sin of position pos;
 //   2. every K and V row of the chunk (positions < pos; addresses clamped,
@@ -347,12 +348,22 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 //   3. Q = fp16(RoPE(q)); the wave whose chunk holds pos also rotates/rounds
 //      (INT8: quantizes) the new K and V, stores them in the cache and scores
 //      that key from registers; scores, softmax, P V.
-// The waves merge in LDS in wave order and the block writes its softmax state (a
-// block beyond the row's context writes max = -inf); the parts are combined
-// in part order either by attn_merge_kernel or inside the O-projection GEMV.
+// The waves of each part merge in LDS in wave order and the block writes each
+// part's softmax state (a part beyond the row's context: max = -inf, sum 0);
+// the parts are combined in part order either by attn_merge_kernel or inside
+// the O-projection GEMV.
 constexpr int kDecChunk = 32;
-constexpr int kDecWaves = 4;
-constexpr int kDecPart = kDecChunk * kDecWaves;  // keys per block
+constexpr int kDecPart = kDecChunk * 4;  // keys of the smallest part (4 waves)
+
+// Waves per part of a row with `ctx` visible keys: parts of 128 keys up to
+// context 1024, 256 beyond, so a row has at most 8 parts to context 2048.
+// The O-projection GEMV merges every part of the call's rows in each of its
+// blocks, so fewer parts make it cheaper, while larger parts leave fewer
+// blocks to the attention (measured at context 1920-2048, INT8 cache, one
+// lane: 16 parts of 128 keys 0.333 ms/token, 8 of 256 keys 0.324, 4 of 512
+// keys (16-wave blocks) 0.376). The split depends on the row's own context
+// only, so a lane's result does not depend on the other rows of the call.
+__host__ __device__ inline int dec_part_waves(int ctx) { return ctx <= 1024 ? 4 : 8; }
 
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S) {
   const int np = (S + kDecPart - 1) / kDecPart;
@@ -362,28 +373,37 @@ size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S) {
 int attn_decode_np_max(int S) { return (S + kDecPart - 1) / kDecPart; }
 
 int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv) {
-  int maxctx = 0;
-  for (int m = 0; m < M; ++m) maxctx = max(maxctx, rm.row_pos[m] + 1 - kv_first(kv, rm.row_pos[m]));
-  return (maxctx + kDecPart - 1) / kDecPart;
+  int np = 0;
+  for (int m = 0; m < M; ++m) {
+    const int ctx = rm.row_pos[m] + 1 - kv_first(kv, rm.row_pos[m]);
+    const int pk = kDecChunk * dec_part_waves(ctx);
+    np = max(np, (ctx + pk - 1) / pk);
+  }
+  return np;
 }
 
-template <int HD, bool I8>
-__global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float* __restrict__ qkv, RowMap rm,
-                                                                     const float* __restrict__ rope_cs, KvGeom kv,
-                                                                     int layer, float* __restrict__ part, int np_max) {
+// BW waves per block (the largest part of the call's rows): a block covers
+// BW * 32 keys and writes BW / W parts of a row whose parts have W waves.
+template <int HD, bool I8, int BW>
+__global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __restrict__ qkv, RowMap rm,
+                                                              const float* __restrict__ rope_cs, KvGeom kv,
+                                                              int layer, float* __restrict__ part, int np_max) {
   constexpr int LPK = HD / 8;    // lanes per key
   constexpr int KPP = 64 / LPK;  // keys per pass
   constexpr int NP = kDecChunk / KPP;
   constexpr int HALF = HD / 2;
-  __shared__ float red_o[kDecWaves][64 / (HD / 8)][HD];  // per wave and key row of a pass
-  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
+  __shared__ float red_o[BW][64 / (HD / 8)][HD];  // per wave and key row of a pass
+  __shared__ float red_m[BW], red_l[BW];
   const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
   const int pos = rm.row_pos[m];
   const int kbeg = kv_first(kv, pos);  // keys kbeg .. pos are visible
-  const int nparts = (pos + 1 - kbeg + kDecPart - 1) / kDecPart;
-  float* dst = part + ((size_t)(m * kv.H + h) * np_max + bp) * (HD + kAttnPartExtra);
-  if (bp >= nparts) {  // beyond this row's context: an empty part
-    if (threadIdx.x == 0) {
+  const int ctx = pos + 1 - kbeg;
+  const int W = BW == 4 ? 4 : dec_part_waves(ctx), ppb = BW / W;  // waves per part, parts per block
+  const int nparts = (ctx + kDecChunk * W - 1) / (kDecChunk * W);
+  const int pb0 = bp * ppb;  // this block's first part
+  if (pb0 >= nparts) {  // beyond this row's context: empty parts
+    if ((int)threadIdx.x < ppb && pb0 + (int)threadIdx.x < np_max) {
+      float* dst = part + ((size_t)(m * kv.H + h) * np_max + pb0 + threadIdx.x) * (HD + kAttnPartExtra);
       dst[HD] = -INFINITY;
       dst[HD + 1] = 0.f;
     }
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
   const int lane_id = rm.row_lane[m];
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const int rowb = I8 ? HD : 2 * HD;
-  const int k0 = kbeg + (bp * kDecWaves + wave) * kDecChunk;
+  const int k0 = kbeg + (bp * BW + wave) * kDecChunk;
   const bool active = k0 <= pos;
 
   // ---- 1. projections of this row (8 dims + their RoPE partners) and cos/sin
@@ -571,26 +591,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_decode_kernel(const float
     red_l[wave] = lsum;
   }
   __syncthreads();
-  // ---- merge the waves in wave order
-  float bm = -INFINITY;
+  // ---- each part merges its W waves in wave order (a part whose waves all
+  // lie beyond the context comes out empty: max -inf, sum 0)
+  for (int j = 0; j < ppb && pb0 + j < np_max; ++j) {
+    float* dst = part + ((size_t)(m * kv.H + h) * np_max + pb0 + j) * (HD + kAttnPartExtra);
+    float bm = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) bm = fmaxf(bm, red_m[w]);
-  if (tid < HD) {
-    float num = 0.f, den = 0.f;
+    for (int w = j * W; w < (j + 1) * W; ++w) bm = fmaxf(bm, red_m[w]);
+    if (tid < HD) {
+      float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      if (red_m[w] == -INFINITY) continue;  // chunk beyond the context
-      const float sw = expf(red_m[w] - bm);
-      float o = red_o[w][0][tid];
+      for (int w = j * W; w < (j + 1) * W; ++w) {
+        if (red_m[w] == -INFINITY) continue;  // chunk beyond the context
+        const float sw = expf(red_m[w] - bm);
+        float o = red_o[w][0][tid];
 #pragma unroll
-      for (int g = 1; g < KPP; ++g) o += red_o[w][g][tid];  // key rows in order
-      num = fmaf(sw, o, num);
-      den = fmaf(sw, red_l[w], den);
-    }
-    dst[tid] = num;
-    if (tid == 0) {
-      dst[HD] = bm;
-      dst[HD + 1] = den;
+        for (int g = 1; g < KPP; ++g) o += red_o[w][g][tid];  // key rows in order
+        num = fmaf(sw, o, num);
+        den = fmaf(sw, red_l[w], den);
+      }
+      dst[tid] = num;
+      if (tid == 0) {
+        dst[HD] = bm;
+        dst[HD + 1] = den;
+      }
     }
   }
 }
@@ -612,25 +636,45 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(const float* __restrict_
   o[(size_t)m * H * HD + h * HD + i] = f2h(num / den);
 }
 
+template <int HD, bool I8, int BW>
+static void decode_launch_bw(int M, const float* qkv, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+                             int layer, float* part, int np_max, int maxctx, int nparts, hipStream_t s) {
+  // Enough blocks for the longest context, and for every row to write its
+  // first `nparts` parts (the merge reads that many of each row; a row with
+  // W = BW writes one part per block).
+  const dim3 grid(max((maxctx + BW * kDecChunk - 1) / (BW * kDecChunk), nparts), kv.H, M);
+  launch((attn_decode_kernel<HD, I8, BW>), grid, dim3(BW * 64), 0, s, qkv, rm, rope_cs, kv, layer, part, np_max);
+}
+
 template <int HD, bool I8>
-static void decode_launch(dim3 grid, const float* qkv, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
+static void decode_launch(int M, const float* qkv, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                           int layer, float* part, int np_max, uint16_t* o, hipStream_t s) {
-  launch((attn_decode_kernel<HD, I8>), grid, dim3(kDecWaves * 64), 0, s, qkv, rm, rope_cs, kv, layer, part, np_max);
-  if (o) launch(attn_merge_kernel<HD>, dim3(kv.H, grid.z), dim3(HD), 0, s, part, kv.H, (int)grid.x, np_max, o);
+  int maxctx = 1, bw = 4;
+  for (int m = 0; m < M; ++m) {
+    const int ctx = rm.row_pos[m] + 1 - kv_first(kv, rm.row_pos[m]);
+    maxctx = max(maxctx, ctx);
+    bw = max(bw, dec_part_waves(ctx));
+  }
+  const int nparts = attn_decode_parts(M, rm, kv);
+  if (bw == 4)
+    decode_launch_bw<HD, I8, 4>(M, qkv, rm, rope_cs, kv, layer, part, np_max, maxctx, nparts, s);
+  else
+    decode_launch_bw<HD, I8, 8>(M, qkv, rm, rope_cs, kv, layer, part, np_max, maxctx, nparts, s);
+  if (o) launch(attn_merge_kernel<HD>, dim3(kv.H, M), dim3(HD), 0, s, part, kv.H, nparts, np_max, o);
 }
 
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s) {
   const int np_max = attn_decode_np_max(kv.S);
-  dim3 grid(attn_decode_parts(M, rm, kv), kv.H, M);
+  if (attn_decode_parts(M, rm, kv) > np_max) return hipErrorInvalidValue;
   if (kv.hd == 128 && kv.int8)
-    decode_launch<128, true>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<128, true>(M, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 128)
-    decode_launch<128, false>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<128, false>(M, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 64 && kv.int8)
-    decode_launch<64, true>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<64, true>(M, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else if (kv.hd == 64)
-    decode_launch<64, false>(grid, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
+    decode_launch<64, false>(M, qkv, rm, rope_cs, kv, layer, part, np_max, o, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

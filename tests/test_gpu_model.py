@@ -8,6 +8,8 @@ legitimately pick different continuations. GPU-vs-GPU properties that the
 model family promises (variable-L results, lanes with their own depth,
 repeated runs) are checked bit for bit.
 """
+import gc
+
 import numpy as np
 import pytest
 
@@ -244,6 +246,57 @@ def test_lanes_with_own_depth_are_batch_invariant(tiny_sharp):
     alone.close()
 
 
+@pytest.mark.parametrize("kv", [0, 1])
+def test_decode_lanes_across_part_size_thresholds(tiny_sharp, kv):
+    """Five lanes whose contexts straddle the decode attention's part sizes
+    (128 keys up to context 1024, 256 beyond), decoded together for 8 steps
+    so that one lane crosses the threshold: each lane equals itself decoded
+    alone, bit for bit (the together call merges 5 x 8 parts in the merge
+    kernel, the lone calls inside the O-projection GEMV), and with FP16
+    caches every row matches the oracle (teacher-forced)."""
+    w, om = tiny_sharp
+    s = w["shape"]
+    torch = _torch()
+    L, steps, max_seq = 2, 8, 1200
+    lens = [100, 506, 700, 1019, 1100]
+    n = len(lens)
+    streams = [synth.make_tokens(s.vocab, P + steps, seed=5, lane=i) for i, P in enumerate(lens)]
+    kvd = tl.TL_KV_INT8 if kv else tl.TL_KV_FP16
+
+    def build():
+        m = _model(w, max_seq=max_seq, max_loops=L, n_lanes=n, kv_dtype=kvd, max_tokens=max(lens))
+        for i in range(n):
+            m.set_loops(i, L)
+            m.prefill(_toks(streams[i][:lens[i]]), lane=i)
+        return m
+
+    together, alone = build(), build()
+    hid = torch.zeros((steps, n, s.d_model), dtype=torch.float32, device="cuda")
+    lg = torch.zeros((steps, n, s.vocab), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        tok = [streams[i][lens[i] + t] for i in range(n)]
+        together.decode_step(_toks(tok), hidden=hid[t], logits=lg[t])
+        for i in range(n):
+            h1 = torch.zeros((n, s.d_model), dtype=torch.float32, device="cuda")
+            l1 = torch.zeros((n, s.vocab), dtype=torch.float32, device="cuda")
+            alone.decode_step(_toks(tok), active=[j == i for j in range(n)], hidden=h1, logits=l1)
+            torch.cuda.synchronize()
+            assert torch.equal(h1[i], hid[t, i]) and torch.equal(l1[i], lg[t, i]), (t, i)
+    torch.cuda.synchronize()
+    together.close()
+    alone.close()
+    if kv:
+        return
+    hid, lg = hid.cpu().numpy(), lg.cpu().numpy()
+    for i in range(n):
+        ro = oracle.forward(om, streams[i], L, logits=None, max_seq=max_seq)
+        ref_h = ro["hidden"][lens[i]:]
+        e_h = rel_rows(hid[:, i], ref_h)
+        e_l = rel_rows(lg[:, i], oracle.head_logits(om, ref_h))
+        print(f"lane {i} ctx {lens[i]}..{lens[i] + steps}: hidden {e_h:.2e} logits {e_l:.2e}")
+        assert e_h < TOL and e_l < TOL
+
+
 def test_lanes_match_oracle(tiny_sharp):
     w, om = tiny_sharp
     loops = [4, 16, 32]
@@ -333,6 +386,7 @@ def test_no_device_memory_growth(tiny):
         m.decode_step(_toks([1]))
         m.close()
         del m
+        gc.collect()   # objects of earlier tests freed by a collection are not growth
         torch.cuda.synchronize()
         if i == 1:
             base = torch.cuda.memory_allocated()

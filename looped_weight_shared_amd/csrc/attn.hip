@@ -8,8 +8,9 @@
 //
 // Prefill: a block takes 64 queries of one head (8 waves: 4 groups of 16
 // rows x 2 halves of each key tile) and walks 128-key tiles up to its causal
-// limit: K tile and transposed V tile staged in
-// LDS, S = Q K^T and O += P V on v_mfma_f32_16x16x32_f16, online softmax in
+// limit: K and V tiles staged row-major in LDS (V's MFMA fragments read back
+// with gfx950's transposing LDS read), S = Q K^T and O += P V on
+// v_mfma_f32_16x16x32_f16, online softmax in
 // fp32 (running max and sum per row). INT8 codes are exact in fp16, so the
 // MFMAs run on the codes and the per-key scales multiply the score columns
 // and the probabilities. P enters the PV MFMA as two fp16 parts (high part and
@@ -49,6 +50,21 @@ __device__ __forceinline__ CachePtrs cache_ptrs(const KvGeom& kv, int lane, int 
 
 
 // ------------------------------------------------------------------ prefill
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), in groups of 16 lanes:
+// lane 16g + 4a + b receives element b of the 4-element (8-byte) chunks
+// addressed by lanes 16g + a, 16g + a + 4, 16g + a + 8 and 16g + a + 12, in
+// that order. Two reads (rows r and r + 4) give a lane 8 values of one column.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half8_t lds_read_tr16x8(const _Float16* p0, const _Float16* p1) {
+  typedef __attribute__((address_space(3))) short4_t lds_short4;
+  const short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+  const short4_t c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1));
+  const short4_t lo = a, hi = c;
+  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+  const half4_t l4 = __builtin_bit_cast(half4_t, lo), h4 = __builtin_bit_cast(half4_t, hi);
+  return (half8_t){l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+}
+
 __device__ __forceinline__ void attn_lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -57,8 +73,8 @@ __device__ __forceinline__ void attn_lds_barrier() {
 
 // K/V tile t (keys KT*t .. KT*t + KT-1) is requested into registers while
 // tile t-1 is computed (raw: fp16 rows, or INT8 codes and scales, converted
-// when written to LDS so the request never waits), then written to LDS: K
-// row-major, V transposed. The block barriers wait on LDS only, so the next
+// when written to LDS so the request never waits), then written to LDS as
+// 16-byte row chunks, K and V alike. The block barriers wait on LDS only, so the next
 // tile's requests stay in flight across them. KT = 128 keys per tile: a
 // 128-token call takes one tile per block.
 //
@@ -83,20 +99,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   constexpr int KS = HD / 32;     // k-steps of S = Q K^T
   constexpr int DB = HD / 16;     // 16-wide d blocks of O
   constexpr int LK = HD + 8;      // LDS row stride of the K tile (halves)
-  constexpr int LV = KT + 8;      // LDS row stride of the transposed V tile
   constexpr int LP = KH + 8;      // LDS row stride of a wave's P
-  // Vt row d holds its 8-key chunks in swizzled order: chunk c at slot
-  // c ^ ((d / 8) % NC). The transposing writes (a wave writes one dim of 16
-  // rows 8 apart) then spread over the banks instead of piling onto two,
-  // and an MFMA fragment (8 consecutive keys of one row) stays contiguous.
-  constexpr int NC = KT / 8;
   constexpr int CPT = KT * HD / 8 / kAttnThreads;  // 8-element chunks of K (and of V) per thread and tile
   static_assert(KB >= 1 && PS >= 1 && CPT >= 1, "tile shape");
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
-  // K tile, then the transposed V tile, in one array (reused by the merge)
-  __shared__ __align__(16) _Float16 KVs[KT * LK + HD * LV];
+  // K tile, then the V tile, both row-major (key rows of HD + 8 halves), in
+  // one array (reused by the merge)
+  __shared__ __align__(16) _Float16 KVs[2 * KT * LK];
   _Float16* const Ks = KVs;
-  _Float16* const Vt = KVs + KT * LK;
+  _Float16* const Vs = KVs + KT * LK;
   __shared__ __align__(16) _Float16 Ps[4 * kAttnKSplit][2][16 * LP];  // P as fp16 high and low parts
   __shared__ float ksc[KT], vsc[KT];
 
@@ -152,9 +163,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
       const bool ok = kt * KT + kr < kend && kt * KT + kr >= kbeg;
       *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
-      const half8_t vh = ok ? to_f16(vreg[i]) : hz;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(d0 + j) * LV + 8 * ((kr >> 3) ^ ((d0 >> 3) & (NC - 1))) + (kr & 7)] = vh[j];
+      *reinterpret_cast<half8_t*>(&Vs[kr * LK + d0]) = ok ? to_f16(vreg[i]) : hz;
     }
     if (tid < KT) {
       const bool ok = kt * KT + tid < kend && kt * KT + tid >= kbeg;
@@ -265,14 +274,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       pa[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][0][l16 * LP + 32 * s + 8 * lq]);
       pl[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][1][l16 * LP + 32 * s + 8 * lq]);
     }
-    // ---- O += P V over this wave's keys (8-key chunks kh*KH/8 + 4s + lq of Vt)
+    // ---- O += P V over this wave's keys: the B fragment of lane (lq, n)
+    // (keys kh*KH + 32s + 8lq .. +7 of dim 16b + n) comes from the row-major
+    // V tile by two transposing reads, lane (lq, n) addressing key row
+    // +8lq + n/4 (and +4) at dims 16b + 4(n%4) .. +3
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int s = 0; s < PS; ++s) {
-        const int vr = b * 16 + l16;
-        const int ch = kh * (KH / 8) + 4 * s + lq;
-        const half8_t bf = *reinterpret_cast<const half8_t*>(&Vt[vr * LV + 8 * (ch ^ ((vr >> 3) & (NC - 1)))]);
+        const _Float16* vp = &Vs[(kh * KH + 32 * s + 8 * lq + (l16 >> 2)) * LK + b * 16 + 4 * (l16 & 3)];
+        const half8_t bf = lds_read_tr16x8(vp, vp + 4 * LK);
         oacc[b] = mfma16(pa[s], bf, oacc[b]);
         oacc[b] = mfma16(pl[s], bf, oacc[b]);
       }

@@ -14,6 +14,8 @@ Also reported (same JSON line):
               Per-launch durations come from HIP event pairs the library
               attaches to every launch's own dispatch (tl_profile_begin/end)
               during a separate pass over the same steps.
+  kernels  -- the W4 GEMV (M = 1, cold and warm weights) and the W4A16 GEMM
+              (M = 1024) alone, at the loop block's four linear shapes.
   cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
               the same prefill step (reported, not a target).
 
@@ -228,6 +230,88 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
     return res
 
 
+def kernel_leg(s, tl, torch, stream):
+    """Single-kernel rates through tl_w4_linear at the loop block's four
+    linear shapes (QKV, O, gate/up, down of the 407M shape): the W4 GEMV at
+    M = 1 against HBM, with the weights cold -- the packed matrix replicated
+    until the copies exceed 320 MB (more than the 256 MB Infinity Cache) and
+    the launches cycling through them -- and warm (one copy re-read, as the
+    loop's later iterations see it); and the W4A16 GEMM at M = 1024 (the
+    seq-1024 prefill's shape) against the fp16 MFMA peak. A run of launches
+    is captured once as a HIP graph (no memset nodes: each call is a single
+    kernel) and replayed, so the host's call overhead does not pace the GPU;
+    the figure is the replay's event time divided by its launches, per-dispatch
+    gap included."""
+    d, f = s.d_model, s.ffn_dim
+    shapes = {"qkv": (3 * d, d), "o": (d, d), "gate_up": (2 * f, d), "down": (d, f)}
+    g = torch.Generator(device="cpu").manual_seed(0)
+    res = {}
+
+    def per_launch_us(calls):
+        tl.lib.tl_w4_linear(*calls[0], None)  # eager first call (one-time kernel attributes)
+        torch.cuda.synchronize()
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for c in calls:
+                if tl.lib.tl_w4_linear(*c, cs) != 0:
+                    raise RuntimeError(tl.tl_last_error())
+        cur = torch.cuda.current_stream()
+        for _ in range(2):
+            gph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4
+        e0.record(cur)
+        for _ in range(reps):
+            gph.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        del gph
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+
+    for name, (N, K) in shapes.items():
+        qw = torch.randint(-2**31, 2**31 - 1, (N, K // 8), generator=g, dtype=torch.int32).cuda()
+        sc = (torch.rand((N, (K + 127) // 128), generator=g) * 0.002 + 0.002).half().cuda()
+        nb = tl.tl_qlinear_packed_bytes(N, K)
+        ncopy = -(-320 * 2**20 // nb)
+        packed = torch.empty((ncopy, -(-nb // 256) * 256), dtype=torch.uint8, device="cuda")
+        tl.tl_qlinear_pack(qw, sc, N, K, packed[0])
+        packed[1:].copy_(packed[0].expand(ncopy - 1, -1))
+        torch.cuda.synchronize()
+        del qw, sc
+        ptrs = [packed[i].data_ptr() for i in range(ncopy)]
+        r = {"N": N, "K": K, "packed_bytes": nb}
+        for M in (1, 1024):
+            A = (torch.randn((M, K), generator=g) * 0.5).half().cuda()
+            C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(tl.tl_w4_linear_ws_bytes(N, K, M), 256), dtype=torch.uint8, device="cuda")
+
+            def calls(n, copies):
+                return [(ptrs[i % copies], N, K, A.data_ptr(), M, C.data_ptr(), ws.data_ptr()) for i in range(n)]
+            if M == 1:
+                algo = nb + K * 2 + N * 4
+                cold = per_launch_us(calls(ncopy, ncopy))
+                warm = per_launch_us(calls(64, 1))
+                r["gemv_m1"] = {"algorithmic_bytes": algo, "cold_us": round(cold, 3), "warm_us": round(warm, 3),
+                                "cold_GBps": round(algo / cold / 1e3, 1), "warm_GBps": round(algo / warm / 1e3, 1),
+                                "cold_frac_hbm": round(algo / cold / 1e3 / PEAK_HBM_GBS, 4), "copies": ncopy}
+            else:
+                flop = 2 * M * N * K
+                t = per_launch_us(calls(16, ncopy))
+                r["gemm_m1024"] = {"gflop": round(flop / 1e9, 2), "us": round(t, 2),
+                                   "TFLOPs": round(flop / t / 1e6, 1),
+                                   "frac_mfma": round(flop / t / 1e6 / PEAK_F16_TFLOPS, 4)}
+            del A, C, ws
+        del packed
+        torch.cuda.empty_cache()
+        res[name] = r
+        print(f"[bench] kernel {name} N={N} K={K}: GEMV cold {r['gemv_m1']['cold_us']} us "
+              f"({r['gemv_m1']['cold_GBps']} GB/s), warm {r['gemv_m1']['warm_us']} us; GEMM M=1024 "
+              f"{r['gemm_m1024']['us']} us ({r['gemm_m1024']['TFLOPs']} TFLOP/s)", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +325,8 @@ def main():
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
     ap.add_argument("--no-storeh", action="store_true", help="skip the store-h (TL_KV_H16) leg")
     ap.add_argument("--no-fp16body", action="store_true", help="skip the FP16-body leg")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the single-kernel leg (cold W4 GEMV and M=1024 GEMM at the loop block's shapes)")
     ap.add_argument("--configs", action="store_true",
                     help="also time the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
                          "context 2048, one lane at L=8 and three lanes at L=4/16/32)")
@@ -483,6 +569,10 @@ def main():
             out["spec_decode"] = {"draft_loops": 2, "verify_loops": L, "prompt": P, "tokens": D,
                                   "note": "greedy; acceptance is a property of the weights (synthetic here)",
                                   **spec}
+
+    # ---------------------------------------------------------------- single kernels
+    if not args.no_kernels:
+        out["kernels"] = kernel_leg(s, tl, torch, stream)
 
     # ---------------------------------------------------------------- other workloads (opt-in)
     if args.configs:

@@ -67,10 +67,11 @@ def test_repack_is_bit_exact(N, K):
 
 
 # 407M shapes at M = 100 and 130: ragged last row tiles, with and without K
-# splits (the consumer sums the partials)
-LIN_CASES = [(6144, 2048, m) for m in (1, 3, 8, 16, 17, 128, 130)] + \
+# splits (the consumer sums the partials); QKV and gate/up shapes at M = 512,
+# 700 (a ragged last row tile) and 1024, the long prefill's sizes
+LIN_CASES = [(6144, 2048, m) for m in (1, 3, 8, 16, 17, 128, 130, 512, 700)] + \
             [(2048, 5632, m) for m in (1, 2, 64, 100, 1024)] + [(2048, 2048, 128)] + \
-            [(256, 704, m) for m in (1, 5, 32, 33)] + [(11264, 2048, m) for m in (1, 100, 256)]
+            [(256, 704, m) for m in (1, 5, 32, 33)] + [(11264, 2048, m) for m in (1, 100, 256, 1024)]
 
 
 @pytest.mark.parametrize("N,K,M", LIN_CASES)

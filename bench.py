@@ -86,7 +86,7 @@ def _pmc_dispatches(d, counter):
 
 def ingest_pmc(fetch_dir, write_dir, copy_mib):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --decode-steps 4 --copy-mib <copy_mib>`, one with
+    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --decode-steps 4 --copy-mib <copy_mib>`, one with
     FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
     for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
@@ -115,7 +115,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
                          tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --decode-steps 4 --copy-mib %d" % copy_mib
+    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --decode-steps 4 --copy-mib %d" % copy_mib
     data = {"commands": [
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
         "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,

@@ -181,10 +181,12 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 // Single-query attention for M decode rows (one per lane) over each lane's
 // rows 0..row_pos[m], from the raw QKV projection qkv fp32 [M][3d]: applies
 // RoPE, writes the new K/V row into cache layer `layer` and attends in
-// parts of 128 keys: part receives, per (row, head, part), the part's softmax
-// state (np_max = ceil(S / 128) parts per (row, head), rows of hd + 4
-// floats). With o non-null the parts are also merged into O fp16 [M][d];
-// otherwise the O projection merges them (ASrc::att).
+// parts of 128 keys (256 for a row with more than 1024 visible keys): part
+// receives, per (row, head, part), the part's softmax state (np_max =
+// ceil(S / 128) slots per (row, head), rows of hd + 4 floats; each row's
+// first attn_decode_parts() slots are written, empty ones with max -inf).
+// With o non-null the parts are also merged into O fp16 [M][d]; otherwise
+// the O projection merges them (ASrc::att).
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
 int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv);  // parts written per (row, head) this call
 int attn_decode_np_max(int S);                  // part slots per (row, head)

@@ -99,13 +99,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   constexpr int KS = HD / 32;     // k-steps of S = Q K^T
   constexpr int DB = HD / 16;     // 16-wide d blocks of O
   constexpr int LK = HD + 8;      // LDS row stride of the K tile (halves)
+  // LDS row stride of the V tile: each 16-lane group of a transposing read
+  // covers 4 rows x 16 dims, conflict-free with rows 8 dwords apart mod 64
+  constexpr int LV = HD + 16;
   constexpr int LP = KH + 8;      // LDS row stride of a wave's P
   constexpr int CPT = KT * HD / 8 / kAttnThreads;  // 8-element chunks of K (and of V) per thread and tile
   static_assert(KB >= 1 && PS >= 1 && CPT >= 1, "tile shape");
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
   // K tile, then the V tile, both row-major (key rows of HD + 8 halves), in
   // one array (reused by the merge)
-  __shared__ __align__(16) _Float16 KVs[2 * KT * LK];
+  __shared__ __align__(16) _Float16 KVs[KT * LK + KT * LV];
   _Float16* const Ks = KVs;
   _Float16* const Vs = KVs + KT * LK;
   __shared__ __align__(16) _Float16 Ps[4 * kAttnKSplit][2][16 * LP];  // P as fp16 high and low parts
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
       const bool ok = kt * KT + kr < kend && kt * KT + kr >= kbeg;
       *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
-      *reinterpret_cast<half8_t*>(&Vs[kr * LK + d0]) = ok ? to_f16(vreg[i]) : hz;
+      *reinterpret_cast<half8_t*>(&Vs[kr * LV + d0]) = ok ? to_f16(vreg[i]) : hz;
     }
     if (tid < KT) {
       const bool ok = kt * KT + tid < kend && kt * KT + tid >= kbeg;
@@ -282,8 +285,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
     for (int b = 0; b < DB; ++b) {
 #pragma unroll
       for (int s = 0; s < PS; ++s) {
-        const _Float16* vp = &Vs[(kh * KH + 32 * s + 8 * lq + (l16 >> 2)) * LK + b * 16 + 4 * (l16 & 3)];
-        const half8_t bf = lds_read_tr16x8(vp, vp + 4 * LK);
+        const _Float16* vp = &Vs[(kh * KH + 32 * s + 8 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
+        const half8_t bf = lds_read_tr16x8(vp, vp + 4 * LV);
         oacc[b] = mfma16(pa[s], bf, oacc[b]);
         oacc[b] = mfma16(pl[s], bf, oacc[b]);
       }
@@ -294,7 +297,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   // ---- merge the key halves: wave (g, 1) -> LDS (the K/V tiles are free
   // after the loop's last barrier) -> wave (g, 0), which scales both by
   // exp(m_half - m) and adds them in half order
-  constexpr int RW = 8 + 4 * DB;  // floats per lane: m[4], l[4], o[DB][4]
+  // floats per lane: m[4], l[4], o[DB][4], 4 of padding (a stride of 4 mod
+  // 8 dwords keeps each 16-lane pass of 16-byte accesses on distinct banks)
+  constexpr int RW = 12 + 4 * DB;
   static_assert((size_t)4 * 64 * RW * 4 <= sizeof(KVs), "merge buffer");
   float* const mb = reinterpret_cast<float*>(KVs);
   if (kh == 1) {

@@ -9,9 +9,10 @@
 // Prefill: a block takes 64 queries of one head (8 waves: 4 groups of 16
 // rows x 2 halves of each key tile) and walks 128-key tiles up to its causal
 // limit: K and V tiles staged row-major in LDS (V's MFMA fragments read back
-// with gfx950's transposing LDS read), S = Q K^T and O += P V on
-// v_mfma_f32_16x16x32_f16, online softmax in
-// fp32 (running max and sum per row). INT8 codes are exact in fp16, so the
+// with gfx950's transposing LDS read), S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_f16 (the transposed score tile is already in the PV
+// MFMA's operand layout, so P stays in registers), online softmax in
+// fp32 (running max and sum per query). INT8 codes are exact in fp16, so the
 // MFMAs run on the codes and the per-key scales multiply the score columns
 // and the probabilities. P enters the PV MFMA as two fp16 parts (high part and
 // the rounded remainder), so the weights keep about 22 significant bits.
@@ -102,7 +103,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   // LDS row stride of the V tile: each 16-lane group of a transposing read
   // covers 4 rows x 16 dims, conflict-free with rows 8 dwords apart mod 64
   constexpr int LV = HD + 16;
-  constexpr int LP = KH + 8;      // LDS row stride of a wave's P
   constexpr int CPT = KT * HD / 8 / kAttnThreads;  // 8-element chunks of K (and of V) per thread and tile
   static_assert(KB >= 1 && PS >= 1 && CPT >= 1, "tile shape");
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   __shared__ __align__(16) _Float16 KVs[KT * LK + KT * LV];
   _Float16* const Ks = KVs;
   _Float16* const Vs = KVs + KT * LK;
-  __shared__ __align__(16) _Float16 Ps[4 * kAttnKSplit][2][16 * LP];  // P as fp16 high and low parts
-  __shared__ float ksc[KT], vsc[KT];
+  __shared__ __align__(16) float ksc[KT];
+  __shared__ __align__(16) float vsc[KT];
 
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int qg = wave & 3, kh = wave >> 2;  // query group, key half
@@ -192,19 +192,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       qf[s] = qr < M ? __builtin_bit_cast(half8_t, v) : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  float mrow[4], lrow[4];
+  // Scores are computed transposed (S^T = K Q^T), so a lane holds 4 keys of
+  // one query: lane (lq, n) has query 16*qg + n and keys 16kb + 4lq + r of
+  // every 16-key block, which is the B-operand layout O^T = V^T P^T needs;
+  // P never leaves registers. Each lane keeps its query's running max and
+  // sum (the 4 lanes of a query hold the same values) and O^T: dims
+  // 16b + 4lq + r of its query.
+  float mrow = -INFINITY, lrow = 0.f;
   float4_t oacc[DB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.f;
-  }
-#pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  const int qpos_base = p0 + q0 + 16 * qg + 4 * lq;  // + r
-  int kfirst[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) kfirst[r] = kv_first(kv, qpos_base + r);
+  const int qpos = p0 + q0 + 16 * qg + l16;
+  const int kfirst = kv_first(kv, qpos);
 
   for (int kt = kt0; kt < nkt; ++kt) {
     const int key0 = kt * KT + kh * KH;  // this wave's keys key0 .. key0 + KH - 1
@@ -213,82 +212,86 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
     if (kt + 1 < nkt) load_tile(kt + 1);  // the next tile is in flight during this tile's math
     asm volatile("" ::: "memory");
 
-    // ---- S = Q K^T for 16 rows x KH keys (lane: rows 4lq+r, key 16kb + l16)
+    // ---- S^T = K Q^T for KH keys x 16 queries (lane: keys 16kb + 4lq + r, query n)
     float sv[KB][4];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const half8_t bf = *reinterpret_cast<const half8_t*>(&Ks[(kh * KH + kb * 16 + l16) * LK + 32 * s + 8 * lq]);
-        t = mfma16(qf[s], bf, t);
+        const half8_t kf = *reinterpret_cast<const half8_t*>(&Ks[(kh * KH + kb * 16 + l16) * LK + 32 * s + 8 * lq]);
+        t = mfma16(kf, qf[s], t);
       }
-      const int key = key0 + kb * 16 + l16;
-      const float ks = ksc[kh * KH + kb * 16 + l16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[kb][r] = (key <= qpos_base + r && key >= kfirst[r]) ? t[r] * ks : -INFINITY;
-    }
-    // ---- online softmax per row
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mx = sv[0][r];
-#pragma unroll
-      for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, sv[kb][r]);
-      mx = row16_max(mx);
-      const float mnew = fmaxf(mrow[r], mx);
-      // a row with no visible key so far (a sliding window that starts in a
-      // later tile, or a key half beyond the row) keeps mnew = -inf: subtract
-      // 0 instead, so its weights are exp(-inf) = 0 rather than NaN
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = expf(mrow[r] - mref);  // 0 while mrow = -inf
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const float p = expf(sv[kb][r] - mref);
-        ps += p;
-        sv[kb][r] = p;
-      }
-      ps = row16_sum(ps);
-      lrow[r] = lrow[r] * alpha + ps;
-      mrow[r] = mnew;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) oacc[b][r] *= alpha;
-    }
-    // ---- P (value scale folded in) through this wave's LDS region into
-    // A-operand order, split into an fp16 high part and the fp16 rounding of
-    // the remainder: the two MFMAs below then apply P with about 22
-    // significant bits instead of 11, so the softmax weights are not rounded
-    // to fp16 before the weighted sum.
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const float vs = vsc[kh * KH + kb * 16 + l16];
+      const float4_t ks = *reinterpret_cast<const float4_t*>(&ksc[kh * KH + kb * 16 + 4 * lq]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = sv[kb][r] * vs;
-        const _Float16 hi = (_Float16)x;
-        Ps[wave][0][(4 * lq + r) * LP + kb * 16 + l16] = hi;
-        Ps[wave][1][(4 * lq + r) * LP + kb * 16 + l16] = (_Float16)(x - (float)hi);
+        const int key = key0 + kb * 16 + 4 * lq + r;
+        sv[kb][r] = (key <= qpos && key >= kfirst) ? t[r] * ks[r] : -INFINITY;
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's P writes land before its reads
-    half8_t pa[PS], pl[PS];
+    // ---- online softmax of the lane's query (its keys are spread over the
+    // lanes n, n+16, n+32, n+48)
+    {
+      float mx = sv[0][0];
 #pragma unroll
-    for (int s = 0; s < PS; ++s) {
-      pa[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][0][l16 * LP + 32 * s + 8 * lq]);
-      pl[s] = *reinterpret_cast<const half8_t*>(&Ps[wave][1][l16 * LP + 32 * s + 8 * lq]);
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow, mx);
+      // a query with no visible key so far (a sliding window that starts in a
+      // later tile, or a key half beyond the query) keeps mnew = -inf:
+      // subtract 0 instead, so its weights are exp(-inf) = 0 rather than NaN
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = expf(mrow - mref);  // 0 while mrow = -inf
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = expf(sv[kb][r] - mref);
+          ps += pr;
+          sv[kb][r] = pr;
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lrow = lrow * alpha + ps;
+      mrow = mnew;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[b][r] *= alpha;
     }
-    // ---- O += P V over this wave's keys: the B fragment of lane (lq, n)
-    // (keys kh*KH + 32s + 8lq .. +7 of dim 16b + n) comes from the row-major
-    // V tile by two transposing reads, lane (lq, n) addressing key row
-    // +8lq + n/4 (and +4) at dims 16b + 4(n%4) .. +3
+    // ---- O^T += V^T P^T over this wave's keys, 32 keys per MFMA. A k-step
+    // pairs key blocks 2j and 2j+1: lane (lq, n) holds P^T for keys
+    // 32j + 4lq + (0..3) and 32j + 16 + 4lq + (0..3) of query n, and reads V^T
+    // for the same 8 keys of dim 16b + n with two transposing reads (lane
+    // (lq, n) addressing key row +4lq + n/4 at dims 16b + 4(n%4) .. +3), so
+    // both operands enumerate k in the same order. P (value scale folded in)
+    // enters as an fp16 high part and the fp16 rounding of the remainder: the
+    // two MFMAs apply it with about 22 significant bits instead of 11.
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
+    for (int j = 0; j < PS; ++j) {
+      half8_t ph, pl;
 #pragma unroll
-      for (int s = 0; s < PS; ++s) {
-        const _Float16* vp = &Vs[(kh * KH + 32 * s + 8 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
-        const half8_t bf = lds_read_tr16x8(vp, vp + 4 * LV);
-        oacc[b] = mfma16(pa[s], bf, oacc[b]);
-        oacc[b] = mfma16(pl[s], bf, oacc[b]);
+      for (int hblk = 0; hblk < 2; ++hblk) {
+        const int kb = 2 * j + hblk;
+        const float4_t vs = *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = sv[kb][r] * vs[r];
+          const _Float16 hi = (_Float16)x;
+          ph[4 * hblk + r] = hi;
+          pl[4 * hblk + r] = (_Float16)(x - (float)hi);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const _Float16* vp = &Vs[(kh * KH + 32 * j + 4 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
+        const half8_t vf = lds_read_tr16x8(vp, vp + 16 * LV);
+        oacc[b] = mfma16(vf, ph, oacc[b]);
+        oacc[b] = mfma16(vf, pl, oacc[b]);
       }
     }
     attn_lds_barrier();  // every wave is done with this K/V tile before the next is written
@@ -297,39 +300,36 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   // ---- merge the key halves: wave (g, 1) -> LDS (the K/V tiles are free
   // after the loop's last barrier) -> wave (g, 0), which scales both by
   // exp(m_half - m) and adds them in half order
-  // floats per lane: m[4], l[4], o[DB][4], 4 of padding (a stride of 4 mod
-  // 8 dwords keeps each 16-lane pass of 16-byte accesses on distinct banks)
-  constexpr int RW = 12 + 4 * DB;
+  // floats per lane: m, l, 2 of padding, o[DB][4] (a stride of 4 mod 8
+  // dwords keeps each 16-lane pass of 16-byte accesses on distinct banks)
+  constexpr int RW = 4 + 4 * DB;
   static_assert((size_t)4 * 64 * RW * 4 <= sizeof(KVs), "merge buffer");
   float* const mb = reinterpret_cast<float*>(KVs);
   if (kh == 1) {
     float* dst = mb + (size_t)(qg * 64 + ln) * RW;
+    dst[0] = mrow;
+    dst[1] = lrow;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dst[r] = mrow[r];
-      dst[4 + r] = lrow[r];
-    }
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[8 + 4 * b + r] = oacc[b][r];
+    for (int b = 0; b < DB; ++b) *reinterpret_cast<float4_t*>(dst + 4 + 4 * b) = oacc[b];
   }
   attn_lds_barrier();
   if (kh == 1) return;
   const float* src = mb + (size_t)(qg * 64 + ln) * RW;
-  // ---- normalise and store rows q0 + 16*qg + 4lq + r
+  // ---- normalise and store query q0 + 16*qg + n, dims 16b + 4lq .. +3
+  const float m2 = src[0], l2 = src[1];
+  const float m = fmaxf(mrow, m2);
+  const float mref = m == -INFINITY ? 0.f : m;
+  const float a1 = expf(mrow - mref), a2 = expf(m2 - mref);
+  const float inv = 1.0f / (lrow * a1 + l2 * a2);
+  const int qr = q0 + 16 * qg + l16;
+  if (qr >= M) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float m2 = src[r], l2 = src[4 + r];
-    const float m = fmaxf(mrow[r], m2);
-    const float mref = m == -INFINITY ? 0.f : m;
-    const float a1 = expf(mrow[r] - mref), a2 = expf(m2 - mref);
-    const float inv = 1.0f / (lrow[r] * a1 + l2 * a2);
-    const int qr = q0 + 16 * qg + 4 * lq + r;
-    if (qr >= M) continue;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-      o[(size_t)qr * d + h * HD + b * 16 + l16] = f2h((oacc[b][r] * a1 + src[8 + 4 * b + r] * a2) * inv);
+  for (int b = 0; b < DB; ++b) {
+    const float4_t o2 = *reinterpret_cast<const float4_t*>(src + 4 + 4 * b);
+    uint2 w;
+    w.x = (uint32_t)f2h((oacc[b][0] * a1 + o2[0] * a2) * inv) | ((uint32_t)f2h((oacc[b][1] * a1 + o2[1] * a2) * inv) << 16);
+    w.y = (uint32_t)f2h((oacc[b][2] * a1 + o2[2] * a2) * inv) | ((uint32_t)f2h((oacc[b][3] * a1 + o2[3] * a2) * inv) << 16);
+    *reinterpret_cast<uint2*>(o + (size_t)qr * d + h * HD + b * 16 + 4 * lq) = w;
   }
 }
 

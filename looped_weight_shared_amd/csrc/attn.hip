@@ -108,7 +108,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
   // K tile, then the V tile, both row-major (key rows of HD + 8 halves), in
   // one array (reused by the merge)
-  __shared__ __align__(16) _Float16 KVs[KT * LK + KT * LV];
+  // floats per lane of the key-half merge: m, l, 2 of padding, o[DB][4] (a
+  // stride of 4 mod 8 dwords keeps each 16-lane pass of 16-byte accesses on
+  // distinct banks); the merge reuses the K/V array
+  constexpr int RW = 4 + 4 * DB;
+  constexpr int KVH = KT * (LK + LV) > 4 * 64 * RW * 2 ? KT * (LK + LV) : 4 * 64 * RW * 2;
+  __shared__ __align__(16) _Float16 KVs[KVH];
   _Float16* const Ks = KVs;
   _Float16* const Vs = KVs + KT * LK;
   __shared__ __align__(16) float ksc[KT];
@@ -300,9 +305,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   // ---- merge the key halves: wave (g, 1) -> LDS (the K/V tiles are free
   // after the loop's last barrier) -> wave (g, 0), which scales both by
   // exp(m_half - m) and adds them in half order
-  // floats per lane: m, l, 2 of padding, o[DB][4] (a stride of 4 mod 8
-  // dwords keeps each 16-lane pass of 16-byte accesses on distinct banks)
-  constexpr int RW = 4 + 4 * DB;
   static_assert((size_t)4 * 64 * RW * 4 <= sizeof(KVs), "merge buffer");
   float* const mb = reinterpret_cast<float*>(KVs);
   if (kh == 1) {

@@ -128,7 +128,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   const int kend = p0 + min(q0 + 64, M);  // keys [kbeg, kend) can be visible to this block
   const int kbeg = kv_first(kv, p0 + q0);  // the window of the block's first query
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
-  const float scale = 1.0f / sqrtf((float)HD);
+  // scores in log2 units (softmax scale times log2 e folded into the key
+  // scales), so every weight is one v_exp_f32: exp(x) = 2^(x log2 e)
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
   const int nkt = (kend + KT - 1) / KT;
   const int kt0 = kbeg / KT;
 
@@ -249,13 +251,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       // later tile, or a key half beyond the query) keeps mnew = -inf:
       // subtract 0 instead, so its weights are exp(-inf) = 0 rather than NaN
       const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = expf(mrow - mref);  // 0 while mrow = -inf
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);  // 0 while mrow = -inf
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pr = expf(sv[kb][r] - mref);
+          const float pr = __builtin_amdgcn_exp2f(sv[kb][r] - mref);
           ps += pr;
           sv[kb][r] = pr;
         }
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   const float m2 = src[0], l2 = src[1];
   const float m = fmaxf(mrow, m2);
   const float mref = m == -INFINITY ? 0.f : m;
-  const float a1 = expf(mrow - mref), a2 = expf(m2 - mref);
+  const float a1 = __builtin_amdgcn_exp2f(mrow - mref), a2 = __builtin_amdgcn_exp2f(m2 - mref);
   const float inv = 1.0f / (lrow * a1 + l2 * a2);
   const int qr = q0 + 16 * qg + l16;
   if (qr >= M) return;

@@ -546,7 +546,7 @@ __global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __res
   }
 
   // ---- scores, chunk max
-  const float scale = 1.0f / sqrtf((float)HD);
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // log2 units: weights are 2^x
   float sc[NP];
   float mx = -INFINITY;
 #pragma unroll
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __res
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int key = k0 + p * KPP + kg;
-      const float pr = key <= pos ? expf(sc[p] - mx) : 0.f;
+      const float pr = key <= pos ? __builtin_amdgcn_exp2f(sc[p] - mx) : 0.f;
       if (sub == 0) lsum += pr;
       float vrow[8];
       if constexpr (I8) {
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __res
 #pragma unroll
       for (int w = j * W; w < (j + 1) * W; ++w) {
         if (red_m[w] == -INFINITY) continue;  // chunk beyond the context
-        const float sw = expf(red_m[w] - bm);
+        const float sw = __builtin_amdgcn_exp2f(red_m[w] - bm);
         float o = red_o[w][0][tid];
 #pragma unroll
         for (int g = 1; g < KPP; ++g) o += red_o[w][g][tid];  // key rows in order

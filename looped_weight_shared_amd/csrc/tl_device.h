@@ -193,13 +193,15 @@ __device__ __forceinline__ int kv_code(float x, float sf) {
 // Decode attention writes, per (row, head, key part), the part's softmax
 // state: weighted value sums [hd], then the running max and the sum of
 // weights, in a row of hd + kAttnPartExtra floats (16-byte aligned rows).
+// Scores and maxima are in log2 units (log2 e folded into the softmax scale),
+// so a weight is 2^(score - max), one v_exp_f32.
 // Parts are combined in part order by attn_merge_step; a part with max -inf
 // (beyond the row's context) is skipped. The merge kernel and the O-projection
 // GEMV both use this, so either path gives the same bits.
 constexpr int kAttnPartExtra = 4;
 __device__ __forceinline__ void attn_merge_step(float gm, float mp, float lp, float nump, float& num, float& den) {
   if (mp != -INFINITY) {
-    const float w = expf(mp - gm);
+    const float w = __builtin_amdgcn_exp2f(mp - gm);
     num = fmaf(w, nump, num);
     den = fmaf(w, lp, den);
   }

@@ -158,7 +158,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// e^-z as 2^(-z log2 e): one v_exp_f32 (saturates to +inf for very negative z,
+// where the quotient is -0, as with expf)
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z)); }
 
 // RoPE-pair packing of the QKV rows: within each head of hd rows, packed
 // row 16j + r holds natural row 8j + r (r < 8, first half of rotation pair

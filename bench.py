@@ -40,13 +40,12 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
 def _ensure_built():
-    lib = os.path.join(ROOT, "looped_weight_shared_amd", "libtl.so")
-    if not os.path.exists(lib):
-        spec = importlib.util.spec_from_file_location(
-            "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
-        mod = importlib.util.module_from_spec(spec)
-        spec.loader.exec_module(mod)
-        mod.build()
+    """Builds libtl.so when it is missing or older than its sources."""
+    spec = importlib.util.spec_from_file_location(
+        "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.ensure_current()
 
 
 def _src_hash(*names):
@@ -230,6 +229,83 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
     return res
 
 
+def host_info():
+    """CPU model name (from /proc/cpuinfo) and the BLAS NumPy calls."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "logical_cpus": os.cpu_count()}
+
+
+def cpu_configs(s, w, synth):
+    """The float64 oracle on the other workloads, each on a bounded sample:
+    cfg2 decode (8 cached steps after the 256-token prompt, L=8), seq-1024
+    prefill at L=16 and L=32 (one run each), INT8-KV decode at context
+    1920 + (one prefill of 1920 tokens, then 4 cached steps; L=8), and the
+    three-lane step (the L=4/16/32 lanes' decode steps at context 1920 after
+    each lane's prefill, 2 steps). Prefill time is reported beside the
+    per-step figures."""
+    import numpy as np
+    import oracle
+    om = oracle.OracleModel(w)
+    res = {}
+    tic = time.perf_counter
+
+    def greedy_steps(prompt, L, steps, kv_int8):
+        c = oracle.Cache(s, len(prompt) + steps + 1, kv_int8=kv_int8)
+        t0 = tic()
+        r = oracle.forward(om, prompt, L, cache=c)
+        tp = tic() - t0
+        tok = int(np.argmax(r["logits"]))
+        t0 = tic()
+        for _ in range(steps):
+            lg, _ = oracle.decode_step(om, c, tok, L)
+            tok = int(np.argmax(lg))
+        return tp, (tic() - t0) / steps
+
+    tp, td = greedy_steps(synth.make_tokens(s.vocab, 256, seed=0), 8, 8, False)
+    res["decode_prompt256_L8_fp16kv"] = {"ms_per_token": round(td * 1e3, 1), "prefill_s": round(tp, 2),
+                                         "sample": "8 cached greedy steps after the 256-token prompt"}
+    print(f"[bench] oracle decode prompt 256 L=8: {td * 1e3:.1f} ms/token", file=sys.stderr, flush=True)
+    t1024 = synth.make_tokens(s.vocab, 1024, seed=0)
+    for Lx in (16, 32):
+        t0 = tic()
+        oracle.forward(om, t1024, Lx, logits=None)
+        dt = tic() - t0
+        res[f"prefill_seq1024_L{Lx}"] = {"tokens_per_s": round(1024 / dt, 1), "seconds": round(dt, 2)}
+        print(f"[bench] oracle prefill seq 1024 L={Lx}: {1024 / dt:.1f} tok/s", file=sys.stderr, flush=True)
+    p1920 = synth.make_tokens(s.vocab, 1920, seed=0)
+    tp, td = greedy_steps(p1920, 8, 4, True)
+    res["decode_int8_ctx1920_L8"] = {"ms_per_token": round(td * 1e3, 1), "prefill_s": round(tp, 2),
+                                     "sample": "4 cached greedy steps after the 1920-token prompt"}
+    print(f"[bench] oracle INT8 decode ctx 1920 L=8: {td * 1e3:.1f} ms/token", file=sys.stderr, flush=True)
+    step = pre = 0.0
+    for lane, Lx in enumerate((4, 16, 32)):
+        tp, td = greedy_steps(synth.make_tokens(s.vocab, 1920, seed=0, lane=lane), Lx, 2, True)
+        step += td
+        pre += tp
+    res["decode_int8_ctx1920_3lanes_L4_16_32"] = {"ms_per_step": round(step * 1e3, 1), "prefill_s": round(pre, 2),
+                                                  "sample": "2 cached greedy steps per lane after its 1920-token "
+                                                            "prompt; a step is one token on each lane"}
+    print(f"[bench] oracle INT8 3-lane step: {step * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    res.update(host_info())
+    return res
+
+
 def kernel_leg(s, tl, torch, stream):
     """Single-kernel rates through tl_w4_linear at the loop block's four
     linear shapes (QKV, O, gate/up, down of the 407M shape): the W4 GEMV at
@@ -327,9 +403,11 @@ def main():
     ap.add_argument("--no-fp16body", action="store_true", help="skip the FP16-body leg")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the single-kernel leg (cold W4 GEMV and M=1024 GEMM at the loop block's shapes)")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
                          "context 2048, one lane at L=8 and three lanes at L=4/16/32)")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="also time the CPU oracle on those workloads (bounded samples; about two minutes)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -574,9 +652,33 @@ def main():
     if not args.no_kernels:
         out["kernels"] = kernel_leg(s, tl, torch, stream)
 
-    # ---------------------------------------------------------------- other workloads (opt-in)
-    if args.configs:
+    # ---------------------------------------------------------------- other workloads
+    if not args.no_configs:
         out["other_configs"] = other_configs(s, w, tl, Model, torch, synth, stream)
+
+    # ---------------------------------------------------------------- decode roofline
+    # headline: the four loop-block GEMVs with cold weights (kernel leg), their
+    # algorithmic bytes summed over their summed launch times; the in-situ
+    # gate/up rate (weights possibly served by the Infinity Cache) is context
+    if "decode" in out:
+        rd = out["roofline_decode"]
+        if "kernels" in out:
+            kl = out["kernels"]
+            byts = sum(kl[k]["gemv_m1"]["algorithmic_bytes"] for k in kl)
+            us = sum(kl[k]["gemv_m1"]["cold_us"] for k in kl)
+            agg = byts / us / 1e3
+            out["roofline_decode"] = {
+                "bound": "hbm", "achieved": round(agg, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(agg / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "w4_gemv_kernel, M=1, cold weights: QKV + O + gate/up + down of the loop block "
+                          "(bytes summed over summed launch times)",
+                "bytes_per_launch": {k: kl[k]["gemv_m1"]["algorithmic_bytes"] for k in kl},
+                "avg_launch_us": {k: kl[k]["gemv_m1"]["cold_us"] for k in kl},
+                "in_situ": rd}
+
+    # ---------------------------------------------------------------- CPU oracle on the other workloads
+    if args.cpu_configs:
+        out["cpu_configs"] = cpu_configs(s, w, synth)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:
@@ -598,7 +700,8 @@ def main():
         out["cpu_baseline"] = {"value": round(SEQ * n / el, 2), "unit": "tokens/s", "cores": cores,
                                "kind": "oracle",
                                "sample": f"{n} x float64 oracle prefill of the same 128-token L=8 step "
-                                         f"({el:.1f} s; weight dequantization not timed)"}
+                                         f"({el:.1f} s; weight dequantization not timed)",
+                               **host_info()}
     if args.copy_mib:
         src = torch.ones(args.copy_mib * 2**18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

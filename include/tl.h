@@ -131,11 +131,15 @@ size_t tl_weights_ws_bytes(const tl_config* cfg);
 /* K and V of one lane for one effective layer, with R = max_seq rows (or,
  * with cache_window W > 0, R = min(max_seq, W + max_tokens) ring rows):
  *   FP16: 2 * R * n_heads * head_dim * 2
- *   INT8: 2 * R * n_heads * (head_dim + 2)   (codes + one fp16 scale
- *         per token and head, "Performance and Memory" page, INT8-KV).
+ *   INT8: 2 * (A(R * n_heads * head_dim) + A(R * n_heads * 2)), A(x) = x
+ *         rounded up to a multiple of 256 (codes + one fp16 scale per token
+ *         and head, "Performance and Memory" page, INT8-KV; equal to
+ *         2 * R * n_heads * (head_dim + 2) when R * n_heads % 128 == 0).
  *   H16:  max_seq * d_model * 2               (h rows [max_seq][d_model]).
- * Layout per layer: K then V planes [n_heads][R][head_dim] (INT8: codes, then
- * fp16 scales [n_heads][R]); position p lives in row p (p mod R with a
+ * Layout per layer: K then V planes [n_heads][R][head_dim]; INT8: K codes
+ * int8 [n_heads][R][head_dim] at offset 0, K scales fp16 [n_heads][R] at
+ * A(codes), V codes at A(codes) + A(scales), V scales after them, every
+ * plane 256-byte aligned. Position p lives in row p (p mod R with a
  * window). 0 for an invalid config. */
 size_t tl_kv_layer_bytes(const tl_config* cfg);
 /* n_lanes * (n_pre + max_loops) * tl_kv_layer_bytes. */
@@ -314,6 +318,19 @@ size_t tl_qlinear_packed_bytes(int32_t N, int32_t K);
 /* Repacks a canonical linear (N % 16 == 0, K % 8 == 0) into d_packed. */
 tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, int32_t N, int32_t K,
                           void* d_packed, void* stream);
+/* FP16 body layout of one linear ("Performance and Memory" page, "FP16 body
+ * cache": body weights dequantized to persistent FP16 at load time), the
+ * form tl_create builds when cfg->fp16_body is 1: per 16-row n-block nb and
+ * 128-column group g a 4 KiB tile of fp16 [4][64 lanes][8], where element j
+ * of lane l in slot s is W[16 nb + l%16][128 g + 32 s + 8 (l/16) + j] =
+ * fp16(q * scale), the exact product rounded once to nearest even (columns at
+ * or beyond K are +0). Tiles are ordered [nb][g]. Bytes: N/16 * ceil(K/128) *
+ * 4096, or 0 unless N % 16 == 0 and K % 8 == 0. */
+size_t tl_qlinear_packed_f16_bytes(int32_t N, int32_t K);
+/* Builds that layout from a canonical linear into d_packed (256-byte
+ * aligned). Errors: TL_E_INVAL (shape or pointer), TL_E_HIP. */
+tl_status tl_qlinear_pack_f16(const uint32_t* d_qweight, const uint16_t* d_scales, int32_t N, int32_t K,
+                              void* d_packed, void* stream);
 /* Exact inverse view of the packed layout: d_q int8 [N][K] receives the
  * signed 4-bit values, d_scales fp16 [N][ceil(K/128)] the scales. Used to
  * check the repack bit for bit. */

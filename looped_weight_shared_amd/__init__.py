@@ -25,6 +25,7 @@ __all__ = [
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs", "tl_spec_decode", "TlSpecStats",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
+    "tl_qlinear_packed_f16_bytes", "tl_qlinear_pack_f16",
     "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
     "KERNEL_KINDS", "EXPORTED",
 ]
@@ -101,6 +102,8 @@ _SIGS = {
     "tl_last_error": (ctypes.c_char_p, []),
     "tl_qlinear_packed_bytes": (_sz, [_i32, _i32]),
     "tl_qlinear_pack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "tl_qlinear_packed_f16_bytes": (_sz, [_i32, _i32]),
+    "tl_qlinear_pack_f16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "tl_qlinear_unpack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_w4_linear_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "tl_w4_linear": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
@@ -244,6 +247,14 @@ def tl_qlinear_packed_bytes(N: int, K: int) -> int:
 
 def tl_qlinear_pack(qweight, scales, N: int, K: int, packed, stream=None) -> None:
     _check(lib.tl_qlinear_pack(_ptr(qweight), _ptr(scales), N, K, _ptr(packed), _stream(stream)))
+
+
+def tl_qlinear_packed_f16_bytes(N: int, K: int) -> int:
+    return lib.tl_qlinear_packed_f16_bytes(N, K)
+
+
+def tl_qlinear_pack_f16(qweight, scales, N: int, K: int, packed, stream=None) -> None:
+    _check(lib.tl_qlinear_pack_f16(_ptr(qweight), _ptr(scales), N, K, _ptr(packed), _stream(stream)))
 
 
 def tl_qlinear_unpack(packed, N: int, K: int, q, scales, stream=None) -> None:

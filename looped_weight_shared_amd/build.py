@@ -1,10 +1,14 @@
 """Build libtl.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Every call compiles from source; the library is written next to this file.
+Every call compiles from source; the library is written next to this file,
+together with libtl.so.stamp, a hash of the sources, the public header and the
+compiler flags it was built from. is_current() compares that stamp with the
+sources on disk, so a library older than its sources is rebuilt, not loaded.
 Run directly (this file does not import the package): python looped_weight_shared_amd/build.py
 """
 import concurrent.futures
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -14,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtl.so")
+STAMP = LIB + ".stamp"
 OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,6 +36,35 @@ def _run(cmd):
 
 
 
+def source_hash() -> str:
+    """sha256 over the HIP sources, the kernel headers, include/tl.h and the flags."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                   + glob.glob(os.path.join(INCLUDE, "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join([ARCH] + FLAGS).encode())
+    return h.hexdigest()
+
+
+def is_current() -> bool:
+    """libtl.so exists and was built from the sources now on disk."""
+    if not (os.path.exists(LIB) and os.path.exists(STAMP)):
+        return False
+    with open(STAMP) as f:
+        return f.read().strip() == source_hash()
+
+
+def ensure_current(verbose: bool = False) -> str:
+    """Builds libtl.so unless the one on disk matches the sources."""
+    if not is_current():
+        print(f"[build] {LIB} is missing or older than its sources: building", file=sys.stderr, flush=True)
+        build(verbose)
+    return LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -43,11 +77,15 @@ def build(verbose: bool = False) -> str:
             print(out)
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{out}")
+    digest = source_hash()  # taken before compiling: an edit during the build leaves the stamp stale
     tmp = LIB + ".tmp"
     rc, out = _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
     os.replace(tmp, LIB)
+    with open(STAMP + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(STAMP + ".tmp", STAMP)
     return LIB
 
 

@@ -3,7 +3,7 @@
 // Cache layout of one (lane, effective layer): K then V, each [H][S][hd]
 // fp16; or, in INT8 mode, Kq int8 [H][S][hd], Ks fp16 [H][S], Vq, Vs (one
 // FP16 scale per token and head: "Performance and Memory" page, "KV cache
-// INT8"). Attention always reads what the cache holds, so an INT8 cache is
+// INT8"), each plane 256-byte aligned (int8_planes). Attention always reads what the cache holds, so an INT8 cache is
 // read back as q * s in the prefill too (cached and uncached paths agree).
 //
 // Prefill: a block takes 64 queries of one head (8 waves: 4 groups of 16
@@ -37,10 +37,11 @@ __device__ __forceinline__ CachePtrs cache_ptrs(const KvGeom& kv, int lane, int 
   const size_t HS = (size_t)kv.H * kv.cap;
   CachePtrs c;
   if (kv.int8) {
-    c.k = base + (size_t)h * kv.cap * kv.hd;
-    c.ks = reinterpret_cast<const uint16_t*>(base + HS * kv.hd) + (size_t)h * kv.cap;
-    c.v = base + HS * kv.hd + HS * 2 + (size_t)h * kv.cap * kv.hd;
-    c.vs = reinterpret_cast<const uint16_t*>(base + 2 * HS * kv.hd + HS * 2) + (size_t)h * kv.cap;
+    const Int8Planes pl = int8_planes(kv.H, kv.cap, kv.hd);
+    c.k = base + pl.kq + (size_t)h * kv.cap * kv.hd;
+    c.ks = reinterpret_cast<const uint16_t*>(base + pl.ks) + (size_t)h * kv.cap;
+    c.v = base + pl.vq + (size_t)h * kv.cap * kv.hd;
+    c.vs = reinterpret_cast<const uint16_t*>(base + pl.vs) + (size_t)h * kv.cap;
   } else {
     c.k = base + (size_t)h * kv.cap * kv.hd * 2;
     c.v = base + HS * kv.hd * 2 + (size_t)h * kv.cap * kv.hd * 2;

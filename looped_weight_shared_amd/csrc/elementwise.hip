@@ -307,10 +307,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
       V[ln + half] = __builtin_bit_cast(uint16_t, V2);
     }
   } else {
-    int8_t* Kq = reinterpret_cast<int8_t*>(base) + rowi * hd;
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(base + HS * hd) + rowi;
-    int8_t* Vq = reinterpret_cast<int8_t*>(base + HS * hd + HS * 2) + rowi * hd;
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(base + 2 * HS * hd + HS * 2) + rowi;
+    const Int8Planes pl = int8_planes(kv.H, kv.cap, hd);
+    int8_t* Kq = reinterpret_cast<int8_t*>(base + pl.kq) + rowi * hd;
+    uint16_t* Ks = reinterpret_cast<uint16_t*>(base + pl.ks) + rowi;
+    int8_t* Vq = reinterpret_cast<int8_t*>(base + pl.vq) + rowi * hd;
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(base + pl.vs) + rowi;
     int8_t a, b;
     uint16_t s;
     quant_pair((float)K1, (float)K2, valid, &a, &b, &s);

@@ -345,6 +345,24 @@ tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   return TL_OK;
 }
 
+// Split-K partials [S][M][d] of a residual GEMM (O or down projection). A
+// prefill keeps them pending: the next RMSNorm (or resolve()) adds them to x
+// in split order, saving a pass over x. A decode step adds them right away:
+// its row count shrinks from layer to layer as lanes reach their L, and the
+// head reads x directly, so partials left for later would be summed with the
+// wrong row stride or not at all. (Decode reaches the GEMM only when the
+// GEMV cannot take the shape, e.g. ffn_dim above 8192 for the down projection.)
+tl_status keep_partials(tl_ctx* c, int kind, int S, int M, bool decode, hipStream_t s) {
+  if (S <= 1) return TL_OK;
+  if (!decode) {
+    c->pend = tl::Pending{c->gpart, S};
+    return TL_OK;
+  }
+  KScope k(c, kind, s);
+  TL_HIP(tl::launch_reduce_partials(c->gpart, S, M, c->cfg.d_model, c->x, 1, s));
+  return TL_OK;
+}
+
 tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowMap& rm, bool decode,
                     hipStream_t s) {
   const int d = c->cfg.d_model, f = c->cfg.ffn_dim;
@@ -405,7 +423,8 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   // x += O W_o^T (deferred to the next RMSNorm when K is split)
   st = linear(c, TL_K_O, B.o, osrc, M, tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, &S, s);
   if (st != TL_OK) return st;
-  if (S > 1) c->pend = tl::Pending{c->gpart, S};
+  st = keep_partials(c, TL_K_O, S, M, decode, s);
+  if (st != TL_OK) return st;
   // a = fp16(silu(h2 W_gate^T) * h2 W_up^T), h2 = fp16(RMSNorm(x))
   st = linear(c, TL_K_GATE_UP, B.gu, tl::ASrc{nullptr, c->x, B.mlp_norm, eps}, M,
               tl::Epi{tl::EPI_SWIGLU, nullptr, c->a, f}, &S, s);
@@ -414,8 +433,7 @@ tl_status run_layer(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   st = linear(c, TL_K_DOWN, B.down, tl::ASrc{c->a, nullptr, nullptr, 0.f}, M,
               tl::Epi{tl::EPI_RESID, c->x, nullptr, d}, &S, s);
   if (st != TL_OK) return st;
-  if (S > 1) c->pend = tl::Pending{c->gpart, S};
-  return TL_OK;
+  return keep_partials(c, TL_K_DOWN, S, M, decode, s);
 }
 
 // Apply any pending residual partials to x (after the last layer).
@@ -452,7 +470,7 @@ size_t tl_kv_layer_bytes(const tl_config* cfg) {
   std::string why;
   if (!check_cfg(cfg, &st, &why)) return 0;
   const size_t rows = (size_t)kv_rows(cfg) * cfg->n_heads;
-  if (cfg->kv_dtype == TL_KV_INT8) return 2 * rows * (cfg->head_dim + 2);
+  if (cfg->kv_dtype == TL_KV_INT8) return tl::int8_planes(cfg->n_heads, kv_rows(cfg), cfg->head_dim).bytes;
   if (cfg->kv_dtype == TL_KV_H16) return (size_t)cfg->max_seq * cfg->d_model * 2;
   return 2 * rows * cfg->head_dim * 2;
 }
@@ -677,6 +695,7 @@ tl_status enqueue_prefill(tl_ctx* ctx, int lane, const int32_t* d_tokens, int n,
   const bool safe = ctx->safety_max > 0.f;
   ctx->h_ready = false;
   ctx->emb_tokens = nullptr;
+  ctx->pend = tl::Pending{nullptr, 1};  // nothing carries over from an earlier call
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
@@ -863,6 +882,7 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
   const bool safe = ctx->safety_max > 0.f;
   ctx->h_ready = false;
   ctx->emb_tokens = nullptr;
+  ctx->pend = tl::Pending{nullptr, 1};  // nothing carries over from an earlier call
   if (safe) {
     KScope k(ctx, TL_K_SAFETY, s);
     TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
@@ -1063,6 +1083,20 @@ tl_status tl_qlinear_pack(const uint32_t* d_qweight, const uint16_t* d_scales, i
   uint8_t* t = static_cast<uint8_t*>(d_packed);
   TL_HIP(tl::launch_pack(d_qweight, d_scales, N, K, t, reinterpret_cast<uint16_t*>(t + tl::packed_tile_bytes(N, K)),
                          (K + 127) / 128, 0, 1, 0, reinterpret_cast<hipStream_t>(stream)));
+  return TL_OK;
+}
+
+size_t tl_qlinear_packed_f16_bytes(int32_t N, int32_t K) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return 0;
+  return tl::packed_f16_bytes(N, K);
+}
+
+tl_status tl_qlinear_pack_f16(const uint32_t* d_qweight, const uint16_t* d_scales, int32_t N, int32_t K,
+                              void* d_packed, void* stream) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
+  if (!d_qweight || !d_scales || !d_packed || !aligned(d_packed, 256)) return fail(TL_E_INVAL, "bad pointer");
+  TL_HIP(tl::launch_pack_f16(d_qweight, d_scales, N, K, static_cast<uint8_t*>(d_packed), (K + 127) / 128, 0, 1, 0,
+                             reinterpret_cast<hipStream_t>(stream)));
   return TL_OK;
 }
 

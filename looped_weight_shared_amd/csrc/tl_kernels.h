@@ -72,6 +72,25 @@ struct KvGeom {
   int cap;              // cache rows per (lane, layer, head): S, or the window's ring
   int window;           // 0: full cache; W: queries see the last W positions
 };
+// INT8 cache of one (lane, layer): K codes int8 [H][cap][hd], K scales fp16
+// [H][cap], V codes, V scales, each plane starting on a 256-byte boundary so
+// that every 8- and 16-byte access to a code row stays aligned whatever
+// H * cap is. (At H * cap a multiple of 128 there is no padding.)
+struct Int8Planes {
+  size_t kq, ks, vq, vs, bytes;
+};
+__host__ __device__ inline size_t kv_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline Int8Planes int8_planes(int H, int cap, int hd) {
+  const size_t codes = kv_al256((size_t)H * cap * hd), scales = kv_al256((size_t)H * cap * 2);
+  Int8Planes p;
+  p.kq = 0;
+  p.ks = codes;
+  p.vq = codes + scales;
+  p.vs = 2 * codes + scales;
+  p.bytes = 2 * (codes + scales);
+  return p;
+}
+
 // Cache row of position pos (a ring when windowed) and the first position
 // a query at pos sees.
 __host__ __device__ inline int kv_slot(const KvGeom& kv, int pos) { return kv.window ? pos % kv.cap : pos; }

@@ -186,8 +186,13 @@ class Cache:
         self.h[layer][pos] = h
 
 
-def _block_forward(x, B, cache, layer, positions, s, casts):
-    """One pre-norm block on residual rows x [n][d] at absolute positions."""
+def _block_forward(x, B, cache, layer, positions, s, casts, rec=None):
+    """One pre-norm block on residual rows x [n][d] at absolute positions.
+
+    rec (a dict, optional) receives the tensors at the block's cast sites as
+    they flow on: h, Q, K, V (after RoPE and the cast), O, h2, a, the
+    residual after attention x_attn and after the MLP x_out, and in INT8 mode
+    the K, V values attention reads (Khat, Vhat)."""
     c = fp16 if casts else _identity
     n = x.shape[0]
     H, hd = s.n_heads, s.head_dim
@@ -209,10 +214,13 @@ def _block_forward(x, B, cache, layer, positions, s, casts):
         ca, sa = rope_cos_sin(np.arange(upto), hd, s.rope_base)
         Kall, Vall = c(apply_rope(ka, ca, sa)), c(va)
         O = c(attention(Q, Kall, Vall, positions, cache.window)).reshape(n, H * hd)
-        x = x + O @ B["wo"].T
-        h2 = c(rmsnorm(x, B["mlp_norm"], s.rms_eps))
+        x1 = x + O @ B["wo"].T
+        h2 = c(rmsnorm(x1, B["mlp_norm"], s.rms_eps))
         a = c(silu(h2 @ B["w_gate"].T) * (h2 @ B["w_up"].T))
-        return x + a @ B["w_down"].T
+        x2 = x1 + a @ B["w_down"].T
+        if rec is not None:
+            rec.update(h=h, Q=Q, K=K, V=V, O=O, x_attn=x1, h2=h2, a=a, x_out=x2)
+        return x2
     if cache.kv_int8:
         if not casts:
             raise ValueError("INT8 KV quantizes FP16 rows; it needs the FP16 cast points")
@@ -224,26 +232,37 @@ def _block_forward(x, B, cache, layer, positions, s, casts):
         cache.write(layer, positions, K, V)
     Kall, Vall = cache.read(layer, int(positions[-1]) + 1)
     O = c(attention(Q, Kall, Vall, positions, cache.window)).reshape(n, H * hd)
-    x = x + O @ B["wo"].T
-    h2 = c(rmsnorm(x, B["mlp_norm"], s.rms_eps))
+    x1 = x + O @ B["wo"].T
+    h2 = c(rmsnorm(x1, B["mlp_norm"], s.rms_eps))
     a = c(silu(h2 @ B["w_gate"].T) * (h2 @ B["w_up"].T))
-    return x + a @ B["w_down"].T
+    x2 = x1 + a @ B["w_down"].T
+    if rec is not None:
+        rec.update(h=h, Q=Q, K=K, V=V, O=O, x_attn=x1, h2=h2, a=a, x_out=x2)
+        if cache.kv_int8:
+            rec.update(Khat=Kall[positions], Vhat=Vall[positions])
+    return x2
 
 
-def head_logits(model, x_rows, casts=True):
-    """Final RMSNorm, cast, and the head projection: [m][d] -> [m][V] float64."""
+def head_logits(model, x_rows, casts=True, rec=None):
+    """Final RMSNorm, cast, and the head projection: [m][d] -> [m][V] float64.
+    rec (a dict, optional) receives the normed, cast head input as 'z'."""
     c = fp16 if casts else _identity
     z = c(rmsnorm(np.atleast_2d(x_rows), model.final_norm, model.shape.rms_eps))
+    if rec is not None:
+        rec["z"] = z
     return z @ model.head64.T
 
 
 def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False,
-            max_seq=None, kv_int8=False, window=0, store_h=False):
+            max_seq=None, kv_int8=False, window=0, store_h=False, sites=None):
     """Append `tokens` to a lane at its current length and run all n_pre + L layers.
 
     Returns a dict with the final residual rows 'hidden' [n][d] (before the
     final norm), 'logits' (last position [V], all positions [n][V], or None),
     the 'cache' and, if trace, 'trace': the residual after every effective layer.
+    sites (a list, optional) receives one dict per effective layer with the
+    tensors at that layer's cast sites (see _block_forward), then one dict
+    with the head input 'z' when logits are computed.
     """
     s = model.shape
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -260,19 +279,25 @@ def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False
     positions = p0 + np.arange(n)
     x = model.embed[tokens].astype(np.float64)
     states = []
+    def rec():
+        if sites is None:
+            return None
+        sites.append({})
+        return sites[-1]
+
     for b in range(s.n_pre):
-        x = _block_forward(x, model.pre[b], cache, b, positions, s, casts)
+        x = _block_forward(x, model.pre[b], cache, b, positions, s, casts, rec())
         states.append(x)
     for i in range(L):  # the same loop-block weights on every iteration
-        x = _block_forward(x, model.loop, cache, s.n_pre + i, positions, s, casts)
+        x = _block_forward(x, model.loop, cache, s.n_pre + i, positions, s, casts, rec())
         states.append(x)
     cache.length = p0 + n
     cache.depth[positions] = s.n_pre + L
     out = {"hidden": x, "cache": cache, "logits": None}
     if logits == "last":
-        out["logits"] = head_logits(model, x[-1:], casts)[0]
+        out["logits"] = head_logits(model, x[-1:], casts, rec())[0]
     elif logits == "all":
-        out["logits"] = head_logits(model, x, casts)
+        out["logits"] = head_logits(model, x, casts, rec())
     if trace:
         out["trace"] = states
     return out

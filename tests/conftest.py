@@ -17,15 +17,15 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
 def ensure_library():
-    """Build libtl.so from source if it is not there yet, then import the binding."""
-    lib = os.path.join(ROOT, "looped_weight_shared_amd", "libtl.so")
-    if not os.path.exists(lib):
-        import importlib.util
-        spec = importlib.util.spec_from_file_location(
-            "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
-        mod = importlib.util.module_from_spec(spec)
-        spec.loader.exec_module(mod)
-        mod.build()
+    """Build libtl.so from source if it is missing or older than its sources
+    (its stamp differs from the hash of the sources on disk), then import the
+    binding."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.ensure_current()
     import looped_weight_shared_amd
     return looped_weight_shared_amd
 

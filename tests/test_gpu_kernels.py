@@ -161,3 +161,56 @@ def test_kv_quantizer_worked_rows():
     for i, c in enumerate(cases):
         assert float(s[i]) == c["scale"]
         assert q[i].tolist() == c["q"]
+
+
+def _f16_tiles_to_matrix(raw, N, K):
+    """FP16-body tiles ([nb][g][slot s][lane l][8], see tl_qlinear_pack_f16)
+    -> fp16 [N][K]: element j of lane l in slot s is row 16nb + l%16, column
+    128g + 32s + 8(l//16) + j."""
+    G = -(-K // 128)
+    t = raw.view(np.float16).reshape(N // 16, G, 4, 4, 16, 8)    # nb, g, s, l//16, l%16, j
+    w = t.transpose(0, 4, 1, 2, 3, 5).reshape(N, G * 128)       # nb, l%16 | g, s, l//16, j
+    return w[:, :K], w[:, K:]
+
+
+def test_fp16_body_dequant_bit_exact_all_nibbles_all_finite_scales():
+    """Each FP16-body weight is the exact product q * s rounded once to
+    nearest even ("Performance and Memory" page, "FP16 body cache": weights
+    dequantized to persistent FP16 at load time): every one of the 63,488
+    finite fp16 scales (both signs, subnormals, the largest, where q * s
+    overflows to inf) meets all 16 nibble values."""
+    torch = _torch()
+    from looped_weight_shared_amd.model import device_bytes
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    sc16 = bits[(bits & 0x7C00) != 0x7C00].view(np.float16)     # all finite fp16 values
+    N, K = sc16.size, 128                                       # 63,488 rows = 3,968 n-blocks
+    assert N % 16 == 0
+    nib = (np.arange(K)[None, :] + np.arange(N)[:, None]) % 16  # every value 8x per row, shifted per row
+    qw = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        qw |= nib[:, j::8].astype(np.uint32) << np.uint32(4 * j)
+    sc = sc16.reshape(N, 1)
+    p = device_bytes(tl.tl_qlinear_packed_f16_bytes(N, K))
+    tl.tl_qlinear_pack_f16(dev(qw), dev(sc), N, K, p)
+    torch.cuda.synchronize()
+    got, pad = _f16_tiles_to_matrix(host(p), N, K)
+    with np.errstate(over="ignore"):
+        want = oracle.dequantize(qw, sc).astype(np.float16)     # exact product, one RNE rounding
+    assert pad.size == 0
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K", [(32, 40), (48, 704)])
+def test_fp16_body_tiles_ragged_k(N, K):
+    """Columns past K are +0 in the FP16-body tiles; the rest is RNE(q * s)."""
+    torch = _torch()
+    from looped_weight_shared_amd.model import device_bytes
+    rng = np.random.default_rng(N * K)
+    qw, sc = _linear(rng, N, K)
+    p = device_bytes(tl.tl_qlinear_packed_f16_bytes(N, K))
+    tl.tl_qlinear_pack_f16(dev(qw), dev(sc), N, K, p)
+    torch.cuda.synchronize()
+    got, pad = _f16_tiles_to_matrix(host(p), N, K)
+    want = oracle.dequantize(qw, sc).astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    assert not pad.view(np.uint16).any()

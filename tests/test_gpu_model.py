@@ -325,6 +325,50 @@ def test_lanes_match_oracle(tiny_sharp):
     m.close()
 
 
+def test_wide_ffn_decode_with_split_down_projection():
+    """ffn_dim 8320 is past the decode GEMV's limit for the down projection
+    (more than 64 groups along K), so decode runs it on the prefill GEMM with
+    K split over 8 blocks. Two lanes at L = 3 and 1 make the step's row count
+    shrink from 2 to 1 after the first loop iteration; the split partials must
+    reach x before that and before the head (a prefill keeps them pending for
+    the next RMSNorm instead)."""
+    import dataclasses
+    s = dataclasses.replace(synth.SHAPES["tiny"], ffn_dim=8320)
+    w = synth.make_weights(s, seed=3, gains="random")
+    om = oracle.OracleModel(w)
+    loops = [3, 1]
+    m = _model(w, max_seq=64, max_loops=3, n_lanes=2, kv_dtype=tl.TL_KV_FP16, max_tokens=20)
+    caches = []
+    for i in range(2):
+        m.set_loops(i, loops[i])
+        prompt = synth.make_tokens(s.vocab, 12 + 5 * i, seed=3, lane=i)
+        hid, lg, _ = GpuRun(m, lane=i).prefill(prompt)
+        c = oracle.Cache(s, 64)
+        ro = oracle.forward(om, prompt, loops[i], cache=c)
+        assert rel_rows(hid, ro["hidden"]) < TOL and rel_rows(lg, ro["logits"]) < TOL
+        caches.append(c)
+    torch = _torch()
+    tok = [5, 900]
+    for step in range(4):
+        hid = torch.zeros((2, s.d_model), dtype=torch.float32, device="cuda")
+        lg = torch.zeros((2, s.vocab), dtype=torch.float32, device="cuda")
+        m.decode_step(_toks(tok), hidden=hid, logits=lg)
+        torch.cuda.synchronize()
+        for i in range(2):
+            lo, ho = oracle.decode_step(om, caches[i], tok[i], loops[i])
+            e_h, e_l = rel_rows(hid[i].cpu().numpy(), ho), rel_rows(lg[i].cpu().numpy(), lo)
+            print(f"ffn 8320 lane {i} L={loops[i]} step {step}: hidden {e_h:.2e} logits {e_l:.2e}")
+            assert e_h < TOL and e_l < TOL
+            tok[i] = int(np.argmax(lo))
+    # a prefill after the decode steps starts clean (nothing pending carries over)
+    m.reset(1)
+    prompt = synth.make_tokens(s.vocab, 9, seed=4)
+    hid, lg, _ = GpuRun(m, lane=1).prefill(prompt)
+    ro = oracle.forward(om, prompt, loops[1], max_seq=64)
+    assert rel_rows(hid, ro["hidden"]) < TOL and rel_rows(lg, ro["logits"]) < TOL
+    m.close()
+
+
 def test_repeated_runs_are_bit_identical(tiny_sharp):
     w, _ = tiny_sharp
     prompt = synth.make_tokens(w["shape"].vocab, 50, seed=9)

@@ -96,13 +96,72 @@ def test_short_window_within_one_prefill_over_two_key_tiles(sharp, W):
                  steps=10)
 
 
-# INT8 windows are checked at the 407M shape. At the tiny shape (d = 256) a
-# code decided differently on a one-ulp fp16 difference between two correct
-# evaluations of a K/V row is a large part of a short dot product: a CPU run
-# of the oracle with fp32 group-wise projections (the GPU's accumulation)
-# already differs from the float64 oracle by 1.4e-3 at INT8, window or not,
-# and the GPU measured 2.3e-3 with W = 16. At d = 2048 the same flips average
-# out (the 2048-context INT8 tests stay below 1e-3).
+def _int8_planes(H, R, hd):
+    """Offsets of the INT8 planes in one (lane, layer) region, as include/tl.h
+    documents them: K codes, K scales, V codes, V scales, each 256-byte aligned."""
+    a = lambda x: (x + 255) // 256 * 256
+    codes, scales = a(H * R * hd), a(H * R * 2)
+    return {"kq": 0, "ks": codes, "vq": codes + scales, "vs": 2 * codes + scales, "bytes": 2 * (codes + scales)}
+
+
+def _check_int8_ring(kv_host, layer_bytes, n_layers, s, R, lane, length, n_used, cache, sites):
+    """The GPU ring of one lane against the oracle, layer by layer: ring row r
+    must hold the latest position p < length with p mod R == r, coded as the
+    oracle codes that position's K and V rows. The two sides compute the fp16
+    K/V rows with different (correct) accumulation orders, so a row may differ
+    in the last fp16 bit, and a code decided on it may then move by one step
+    where the quotient x / s lies near a half-integer. So: scales equal or one
+    fp16 ulp apart, codes equal or one step apart, every step at a quotient
+    within 0.15 of a half-integer (an fp16 ulp of x moves x / s by at most
+    127 * 2^-10 = 0.124) and few of them. A ring or position mistake puts
+    unrelated rows side by side and fails all of these. Returns (flips, codes)."""
+    H, hd = s.n_heads, s.head_dim
+    pl = _int8_planes(H, R, hd)
+    assert pl["bytes"] == layer_bytes
+    flips = total = 0
+    for layer in range(n_used):
+        base = (lane * n_layers + layer) * layer_bytes
+        reg = kv_host[base:base + layer_bytes]
+        for kind in ("k", "v"):
+            codes = reg[pl[kind + "q"]:pl[kind + "q"] + H * R * hd].view(np.int8).reshape(H, R, hd)
+            scal = reg[pl[kind + "s"]:pl[kind + "s"] + H * R * 2].view(np.float16).reshape(H, R)
+            oq = getattr(cache, kind + "q")[layer]                 # codes [pos][H][hd]
+            osc = getattr(cache, kind + "s")[layer]                # scales [pos][H]
+            ox = sites[layer][kind.upper()]                        # fp16 rows [pos][H][hd]
+            for r in range(min(R, length)):
+                p = r + (length - 1 - r) // R * R                  # latest position with p mod R == r
+                gq, gs = codes[:, r, :].astype(np.int64), scal[:, r]
+                qo, so = oq[p].astype(np.int64), osc[p]
+                ulps = np.abs(gs.view(np.uint16).astype(np.int64) - so.view(np.uint16).astype(np.int64))
+                assert (ulps <= 1).all(), (layer, kind, r, p)
+                d = np.abs(gq - qo)
+                assert d.max() <= 1, (layer, kind, r, p, int(d.max()))
+                if d.any():
+                    ratio = ox[p].astype(np.float32) / so.astype(np.float32)[:, None]
+                    tie = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5)
+                    assert (tie[d > 0] < 0.15).all(), (layer, kind, r, p, float(tie[d > 0].max()))
+                total += d.size
+                flips += int((d > 0).sum())
+    assert flips <= 0.02 * total, (flips, total)
+    return flips, total
+
+
+@pytest.mark.parametrize("W,L", [(16, 3), (1, 2), (40, 4)])
+def test_window_matches_oracle_int8(sharp, W, L):
+    """INT8 cache with a window at the tiny shape: the ring's codes and scales
+    read back from the caller's KV buffer against the oracle's, then hidden
+    states and logits at the 2e-3 bound."""
+    s, w, om = sharp
+    _window_case(s, w, om, W, L, kv_int8=True, max_seq=160, max_tokens=24, lens=[110, 73], chunks=[24, 11],
+                 steps=40, check_ring=True)
+
+
+def test_window_int8_ring_plain_weights(plain):
+    s, w, om = plain
+    _window_case(s, w, om, 16, 3, kv_int8=True, max_seq=160, max_tokens=24, lens=[110, 73], chunks=[24, 11],
+                 steps=40, check_ring=True)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("kv_int8", [True, False])
 def test_window_407m(kv_int8):
@@ -113,7 +172,7 @@ def test_window_407m(kv_int8):
                  chunks=[96, 70], steps=64)
 
 
-def _window_case(s, w, om, W, L, kv_int8, max_seq, max_tokens, lens, chunks, steps):
+def _window_case(s, w, om, W, L, kv_int8, max_seq, max_tokens, lens, chunks, steps, check_ring=False):
     kv = tl.TL_KV_INT8 if kv_int8 else tl.TL_KV_FP16
     m = _model(w, max_seq=max_seq, max_loops=L, n_lanes=2, kv_dtype=kv, max_tokens=max_tokens,
                cache_window=W)
@@ -121,13 +180,23 @@ def _window_case(s, w, om, W, L, kv_int8, max_seq, max_tokens, lens, chunks, ste
         m.set_loops(lane, L)
     toks = [synth.make_tokens(s.vocab, n, seed=3, lane=i) for i, n in enumerate(lens)]
     hid, lgs = _run(m, s, toks, chunks=chunks, steps=steps)
+    kv_host = m.kv.cpu().numpy() if check_ring else None
+    layer_bytes, n_layers = tl.tl_kv_layer_bytes(m.cfg), s.n_pre + L
     m.close()
+    R = min(max_seq, W + max_tokens)
     for lane in range(2):
-        ro = oracle.forward(om, toks[lane], L, logits=None, max_seq=max_seq, kv_int8=kv_int8, window=W)
+        sites = [] if check_ring else None
+        ro = oracle.forward(om, toks[lane], L, logits=None, max_seq=max_seq, kv_int8=kv_int8, window=W,
+                            sites=sites)
         ref_l = oracle.head_logits(om, ro["hidden"][-steps:])
         e_h = rel_rows(hid[lane], ro["hidden"])
         e_l = rel_rows(lgs[lane], ref_l)
-        print(f"W={W} L={L} int8={kv_int8} lane {lane}: hidden {e_h:.2e} logits {e_l:.2e}")
+        msg = f"W={W} L={L} int8={kv_int8} lane {lane}: hidden {e_h:.2e} logits {e_l:.2e}"
+        if check_ring:
+            fl, tot = _check_int8_ring(kv_host, layer_bytes, n_layers, s, R, lane, len(toks[lane]),
+                                       s.n_pre + L, ro["cache"], sites)
+            msg += f"; ring rows match the oracle's codes except {fl} one-step flips at ties of {tot}"
+        print(msg)
         assert e_h < TOL and e_l < TOL
 
 

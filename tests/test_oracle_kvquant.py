@@ -20,6 +20,10 @@ def test_worked_rows(case):
     q, s = oracle.kv_quantize(x[None])
     assert float(s[0]) == case["scale"]
     assert q[0].tolist() == case["q"]
+    # the value attention reads back, worked by hand as q times the scale
+    assert oracle.kv_dequantize(q, s)[0].tolist() == case["xhat"]
+    # the per-element bound |x - xhat| <= s/2 holds on the worked rows too
+    assert (np.abs(x.astype(np.float64) - np.array(case["xhat"])) <= case["scale"] / 2).all()
 
 
 def _rows(rng, n, hd=128, spread=1.0):

@@ -193,6 +193,51 @@ def test_cast_points_stay_close_to_uncast():
     assert np.array_equal(k, k.astype(np.float16).astype(np.float64))
 
 
+def _is_fp16(a):
+    a = np.asarray(a, dtype=np.float64)
+    return bool(np.array_equal(a, a.astype(np.float16).astype(np.float64)))
+
+
+_CAST_SITES = ("h", "Q", "K", "V", "O", "h2", "a")
+
+
+@pytest.mark.parametrize("kv_int8", [False, True])
+def test_cast_sites_are_fp16_and_the_residual_is_not(kv_int8):
+    """The definition rounds to fp16 exactly at the normed block inputs h and
+    h2, Q/K/V after RoPE, the attention output O, the gated-MLP product a and
+    the head input z, and keeps the residual stream in high precision (FP32
+    residual: "Current Status" page, core-inference table). Every tensor at a
+    cast site, as it flows on, must therefore be an fp16 number, and the
+    residual after attention and after the MLP must not be (a missing cast or
+    a rounded residual fails here)."""
+    s = synth.SHAPES["tiny"]
+    w = synth.make_weights(s, seed=5, gains="random")
+    om = oracle.OracleModel(w)
+    toks = synth.make_tokens(s.vocab, 24, seed=5)
+    sites = []
+    r = oracle.forward(om, toks, 3, logits="all", sites=sites, kv_int8=kv_int8, max_seq=32)
+    assert len(sites) == s.n_pre + 3 + 1
+    for layer, rec in enumerate(sites[:-1]):
+        for name in _CAST_SITES:
+            assert _is_fp16(rec[name]), (layer, name)
+            assert np.abs(rec[name]).max() > 0, (layer, name)
+        for name in ("x_attn", "x_out"):
+            assert not _is_fp16(rec[name]), (layer, name)
+        if kv_int8:   # attention reads f32(q) * f32(s), not the fp16 rows themselves
+            kq, ks = r["cache"].kq[layer][:24], r["cache"].ks[layer][:24]
+            assert np.array_equal(rec["Khat"], oracle.kv_dequantize(kq, ks))
+            assert not np.array_equal(rec["Khat"], rec["K"])
+    assert _is_fp16(sites[-1]["z"])
+    assert np.array_equal(sites[-2]["x_out"], r["hidden"])
+    # without the casts none of the sites is an fp16 number (the check has teeth)
+    raw = []
+    oracle.forward(om, toks, 3, logits="all", sites=raw, casts=False)
+    for rec in raw[:-1]:
+        for name in _CAST_SITES:
+            assert not _is_fp16(rec[name]), name
+    assert not _is_fp16(raw[-1]["z"])
+
+
 # ---------------------------------------------------------------- loop structure invariants
 @pytest.fixture(scope="module")
 def tiny():

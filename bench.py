@@ -514,8 +514,17 @@ def main():
         decode_run(8, False)                       # warm-up
         ms = decode_run(D, True)
         ms_tok = ms / D
-        print(f"[bench] decode L={L} prompt {P} + {D} steps: {ms_tok:.4f} ms/token",
-              file=sys.stderr, flush=True)
+        # host time to enqueue one step (the calls return before the GPU is done)
+        m.reset(0)
+        m.prefill(ptoks, next_tok=bufs[0])
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for t in range(D):
+            m.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+        host_ms = (time.perf_counter() - h0) * 1e3 / D
+        torch.cuda.synchronize()
+        print(f"[bench] decode L={L} prompt {P} + {D} steps: {ms_tok:.4f} ms/token "
+              f"(host enqueue {host_ms:.4f} ms/step)", file=sys.stderr, flush=True)
         # profiled pass
         m.reset(0)
         m.prefill(ptoks, next_tok=bufs[0])
@@ -538,7 +547,7 @@ def main():
         algo = (sum(wbytes.values()) * (s.n_pre + L) + s.vocab * d * 2
                 + 2 * 2 * s.n_heads * s.head_dim * (s.n_pre + L) * (P + D / 2))
         out["decode"] = {"ms_per_token": round(ms_tok, 4), "prompt": P, "steps": D, "loops": L,
-                         "kv": "fp16", "graph_replayed": False,
+                         "kv": "fp16", "graph_replayed": False, "host_enqueue_ms_per_step": round(host_ms, 4),
                          "algorithmic_bytes_per_token": int(algo),
                          "hbm_roofline_ms_per_token": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
                          "frac_of_hbm_roofline": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3 / ms_tok, 4),

@@ -411,10 +411,17 @@ constexpr int kGemmAhead = 2;  // groups of loads in flight per wave (the loop i
 // STORE, RESID), QKV_ROPE, SWIGLU.
 enum GemmEp { GEP_F32 = 0, GEP_QKV = 1, GEP_SWIGLU = 2 };
 
+// MB m-blocks x NBW n-blocks per wave, the block's 4 waves side by side along
+// N: a block tile is 16*MB rows x 64*NBW columns. The small tiles (MB <= 2)
+// request activations two groups ahead; the large-M tile (MB = 8, NBW = 2:
+// 128 x 128 per block, 128 x 32 per wave) feeds each dequantized weight word
+// to 8 MFMAs instead of 2, requests its 32 KiB activation stage one group
+// ahead and runs 2 waves per SIMD (2 blocks per CU).
 template <int MB, int NBW, bool F16, int EP>
-__global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
-                                                      const uint16_t* __restrict__ scales, int N, int K, int G,
-                                                      const uint16_t* __restrict__ A, int M, Epi e, GemmPlan pl) {
+__global__ __launch_bounds__(256, MB > 2 ? 2 : 1) void w4_gemm_kernel(const uint8_t* __restrict__ tiles,
+                                                                      const uint16_t* __restrict__ scales, int N,
+                                                                      int K, int G, const uint16_t* __restrict__ A,
+                                                                      int M, Epi e, GemmPlan pl) {
   constexpr int kA = MB * 4 * 1024;  // one group's activation stage
   __shared__ __align__(16) uint8_t As[2][kA];
   const int L = blockIdx.x;
@@ -426,35 +433,55 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
   const int my = u / pl.S, sp = u - my * pl.S;
   const int kg0 = sp * pl.gps, kg1 = min(G, kg0 + pl.gps);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The large-M tile (MB > 2) keeps its addresses in scalar registers where it
+  // can (the wave index is uniform) and its rows as 32-bit offsets: eight
+  // 64-bit row pointers per lane would not fit its register budget. The small
+  // tiles keep per-lane pointers (measured ~1% faster in the forward pass).
+  constexpr bool kBig = MB > 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = kBig ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int NB = N / 16;
   const int nbw0 = (cb * 4 + wave) * NBW;
   const int m0 = my * 16 * MB;
 
-  // this thread copies k-step s = wave of every m-block of a stage
-  const uint16_t* arow[MB];
+  // this thread copies k-step s = wave of every m-block of a stage (rows past
+  // M read row M-1; they are never stored)
+  const uint16_t* arow[kBig ? 1 : MB];
+  if constexpr (!kBig) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i) arow[i] = A + (size_t)min(m0 + i * 16 + l16, M - 1) * K;
+    for (int i = 0; i < MB; ++i) arow[i] = A + (size_t)min(m0 + i * 16 + l16, M - 1) * K;
+  }
+  const int arow0 = (m0 + l16) * K, arow_last = (M - 1) * K;  // large tile: element offsets
   const int acol = 32 * wave + 8 * lq;
-  const u32x4_t* btile[NBW];
+  const uint8_t* btile[NBW];  // large tile: per-wave (uniform) bases; small: this lane's slot
   const uint16_t* bscale[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const size_t nb = (size_t)min(nbw0 + j, NB - 1) * G;
-    btile[j] = reinterpret_cast<const u32x4_t*>(tiles + nb * (F16 ? kTileBytesF16 : kTileBytes)) + lane;
-    bscale[j] = F16 ? scales : scales + nb * 16 + l16;
+    btile[j] = tiles + nb * (F16 ? kTileBytesF16 : kTileBytes) + (kBig ? 0 : lane * 16);
+    bscale[j] = F16 ? scales : scales + nb * 16 + (kBig ? 0 : l16);
   }
+  const int bl16 = kBig ? lane * 16 : 0, sl16 = kBig ? l16 : 0;
 
   constexpr int D = kGemmAhead;
+  // activation groups held in registers ahead of their LDS stage: 2 for the
+  // small tiles, 1 for the large-M tile (its stage is 4x larger, and one
+  // group's 64 MFMAs per wave cover the loads of the next)
+  constexpr int DA = MB <= 2 ? D : 1;
   constexpr int WS = F16 ? 4 : 1;  // 16-byte weight slots per tile and lane
-  u32x4_t ar[D][MB];
+  u32x4_t ar[DA][MB];
   u32x4_t br[D][NBW][WS];
   uint32_t bs[D][NBW];  // raw fp16 bits (W4 only)
   auto load_a = [&](u32x4_t (&ra)[MB], int g) {
     const int col = min(min(g, kg1 - 1) * 128 + acol, K - 8);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + col);
+    for (int i = 0; i < MB; ++i) {
+      if constexpr (kBig)
+        ra[i] = *reinterpret_cast<const u32x4_t*>(A + (min(arow0 + i * 16 * K, arow_last) + col));
+      else
+        ra[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + col);
+    }
   };
   auto load_b = [&](u32x4_t (&rb)[NBW][WS], uint32_t (&rs)[NBW], int g) {
     const int gc = min(g, kg1 - 1);
@@ -462,11 +489,12 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
     for (int j = 0; j < NBW; ++j) {
       if constexpr (F16) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) rb[j][s] = btile[j][((size_t)gc * 4 + s) * 64];
+        for (int s = 0; s < 4; ++s)
+          rb[j][s] = *reinterpret_cast<const u32x4_t*>(btile[j] + ((size_t)gc * 4 + s) * 1024 + bl16);
         rs[j] = 0;
       } else {
-        rb[j][0] = btile[j][(size_t)gc * 64];
-        rs[j] = bscale[j][(size_t)gc * 16];
+        rb[j][0] = *reinterpret_cast<const u32x4_t*>(btile[j] + (size_t)gc * kTileBytes + bl16);
+        rs[j] = bscale[j][(size_t)gc * 16 + sl16];
       }
     }
   };
@@ -474,6 +502,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < MB; ++i) *reinterpret_cast<u32x4_t*>(&As[buf][(i * 4 + wave) * 1024 + lane * 16]) = ra[i];
   };
+
 
   float4_t acc[MB][NBW];
 #pragma unroll
@@ -526,24 +555,46 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
     }
   };
 
-  // prologue: groups kg0 .. kg0+D-1 requested; group kg0's activations staged
-#pragma unroll
-  for (int k = 0; k < D; ++k) {
-    load_a(ar[k], kg0 + k);
-    load_b(br[k], bs[k], kg0 + k);
-  }
-  store_a(ar[0], 0);
-  lds_barrier();
-  // D groups per trip (D even), so every ring slot and LDS stage is static
-#pragma unroll 1
-  for (int g = kg0; g < kg1; g += D) {
+  if constexpr (DA == D) {
+    // prologue: groups kg0 .. kg0+D-1 requested; group kg0's activations staged
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      load_a(ar[k], g + k + D);                          // group g+k+D -> slot k (staged one step ago)
-      store_a(ar[(k + 1) % D], (k + 1) & 1);            // group g+k+1 -> LDS
-      compute(k & 1, br[k], bs[k], g + k < kg1);         // group g+k
-      load_b(br[k], bs[k], g + k + D);
-      lds_barrier();
+      load_a(ar[k], kg0 + k);
+      load_b(br[k], bs[k], kg0 + k);
+    }
+    store_a(ar[0], 0);
+    lds_barrier();
+    // D groups per trip (D even), so every ring slot and LDS stage is static
+#pragma unroll 1
+    for (int g = kg0; g < kg1; g += D) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        load_a(ar[k], g + k + D);                          // group g+k+D -> slot k (staged one step ago)
+        store_a(ar[(k + 1) % D], (k + 1) & 1);            // group g+k+1 -> LDS
+        compute(k & 1, br[k], bs[k], g + k < kg1);         // group g+k
+        load_b(br[k], bs[k], g + k + D);
+        lds_barrier();
+      }
+    }
+  } else {
+    // one activation group in registers: group g+1 is requested before group
+    // g is computed and written to the other LDS stage right after it
+    load_a(ar[0], kg0);
+#pragma unroll
+    for (int k = 0; k < D; ++k) load_b(br[k], bs[k], kg0 + k);
+    store_a(ar[0], 0);
+    load_a(ar[0], kg0 + 1);
+    lds_barrier();
+#pragma unroll 1
+    for (int g = kg0; g < kg1; g += D) {
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        compute(k & 1, br[k], bs[k], g + k < kg1);         // group g+k from stage k
+        store_a(ar[0], (k + 1) & 1);                      // group g+k+1 -> the other stage
+        load_a(ar[0], g + k + 2);
+        load_b(br[k], bs[k], g + k + D);
+        lds_barrier();
+      }
     }
   }
 
@@ -681,9 +732,28 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint8_t* __restrict_
 // narrow to 64 only when even the split grid stays below 256 blocks (at
 // M = 128 the down projection then runs 8 splits of 32 x 128 tiles instead
 // of 4 splits of 32 x 64: 10.5 -> 9.8 us, partials included).
+//
+// Large M: when even 128 x 128 blocks make at least 512 of them (gate/up from
+// M = 641; at M = 1024 704 blocks), 128 x 32 wave tiles (kernel <8, 2>) are
+// used: each dequantized weight word then feeds 8 MFMAs and each weight tile
+// is read by M/128 row tiles instead of M/32 (gate/up at M = 1024: 73.7 ->
+// 68.5 us in the seq-1024 forward pass). With fewer blocks the 2-blocks-per-CU
+// tile leaves CUs unevenly loaded: QKV at M = 1024 (384 blocks) measured 47.8
+// -> 52.8 us in situ, so it and the O and down projections stay on 32-row
+// tiles. K is never split on this path.
 GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit) {
   const int NB = N / 16, G = (K + 127) / 128;
   GemmPlan p{};
+  if ((long long)((NB + 7) / 8) * ((M + 127) / 128) >= 512) {
+    p.mb = 8;
+    p.nbw = 2;
+    p.gx = (NB + 7) / 8;
+    p.gy = (M + 127) / 128;
+    p.S = 1;
+    p.gps = G;
+    p.blocks = ((p.gx + 7) / 8) * 8 * p.gy;
+    return p;
+  }
   p.mb = M <= 16 ? 1 : 2;
   p.gy = (M + 16 * p.mb - 1) / (16 * p.mb);
   auto splits = [&](int gx) {
@@ -761,6 +831,7 @@ hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& 
       return hipErrorInvalidValue;
   }
   pl.part = part;
+  if (pl.mb == 8) return gemm_launch<8, 2>(w, A, M, e, pl, s);
   if (pl.nbw == 2) return pl.mb == 2 ? gemm_launch<2, 2>(w, A, M, e, pl, s) : gemm_launch<1, 2>(w, A, M, e, pl, s);
   return pl.mb == 2 ? gemm_launch<2, 1>(w, A, M, e, pl, s) : gemm_launch<1, 1>(w, A, M, e, pl, s);
 }

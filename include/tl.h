@@ -347,6 +347,22 @@ tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* 
 size_t tl_w4_linear_ws_bytes(int32_t N, int32_t K, int32_t M);
 tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M,
                        float* d_C, void* d_ws, void* stream);
+/* Allocation-free variant of tl_w4_linear, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, kernels
+ * and results as tl_w4_linear, minus d_ws: split-K partials go to a static
+ * device buffer inside the library, one per GPU, of
+ * tl_w4_linear_noalloc_max_bytes() bytes (16 MiB), held until the process
+ * ends; its address on a device is looked up on the first call made on that
+ * device (make that call outside graph capture). Nothing in it has to start
+ * at zero: every call writes every partial it later sums. Calls on one GPU
+ * share the buffer, so calls that may overlap on one GPU (different streams
+ * without ordering) race; calls on one stream do not. Calls no
+ * hipMalloc/hipFree. Errors: as tl_w4_linear, plus TL_E_RANGE when
+ * tl_w4_linear_ws_bytes(N, K, M) exceeds the static buffer, TL_E_HIP. */
+size_t tl_w4_linear_noalloc_max_bytes(void);
+tl_status tl_w4_linear_noalloc(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M,
+                               float* d_C, void* stream);
 /* Per-row symmetric INT8 quantizer of the KV cache (bit-exact definition:
  * amax = max|x|; s = fp16(amax / 127) with a correctly rounded float32
  * division; q = clamp(rint_half_even(x / float(s)), -127, 127), 0 if s == 0).

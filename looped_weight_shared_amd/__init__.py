@@ -26,7 +26,8 @@ __all__ = [
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs", "tl_spec_decode", "TlSpecStats",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
     "tl_qlinear_packed_f16_bytes", "tl_qlinear_pack_f16",
-    "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
+    "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_w4_linear_noalloc_max_bytes",
+    "tl_w4_linear_noalloc", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
     "KERNEL_KINDS", "EXPORTED",
 ]
 
@@ -107,6 +108,8 @@ _SIGS = {
     "tl_qlinear_unpack": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_w4_linear_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "tl_w4_linear": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "tl_w4_linear_noalloc_max_bytes": (_sz, []),
+    "tl_w4_linear_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
     "tl_kv_quantize_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_profile_begin": (ctypes.c_int, [_vp, _i32]),
     "tl_profile_end": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]),
@@ -267,6 +270,14 @@ def tl_w4_linear_ws_bytes(N: int, K: int, M: int) -> int:
 
 def tl_w4_linear(packed, N: int, K: int, A, M: int, C, ws, stream=None) -> None:
     _check(lib.tl_w4_linear(_ptr(packed), N, K, _ptr(A), M, _ptr(C), _ptr(ws), _stream(stream)))
+
+
+def tl_w4_linear_noalloc_max_bytes() -> int:
+    return lib.tl_w4_linear_noalloc_max_bytes()
+
+
+def tl_w4_linear_noalloc(packed, N: int, K: int, A, M: int, C, stream=None) -> None:
+    _check(lib.tl_w4_linear_noalloc(_ptr(packed), N, K, _ptr(A), M, _ptr(C), _stream(stream)))
 
 
 def tl_kv_quantize_rows(x, rows: int, hd: int, q, s, stream=None) -> None:

@@ -16,6 +16,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1141,6 +1142,56 @@ tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_
   TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, part, s));
   if (S > 1) TL_HIP(tl::launch_reduce_partials(part, S, M, N, d_C, 0, s));
   return TL_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free W4 linear
+// Split-K partials of tl_w4_linear_noalloc live in this file-scope device
+// array (one copy per GPU, held until the process ends). Host code never
+// passes the array's name to a kernel: its per-device address comes from
+// hipGetSymbolAddress, taken once per device on the first call there.
+namespace {
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tl_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  TL_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TL_E_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    TL_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t tl_w4_linear_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+tl_status tl_w4_linear_noalloc(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M, float* d_C,
+                               void* stream) {
+  if (N < 16 || N % 16 || K < 8 || K % 8) return fail(TL_E_INVAL, "need N % 16 == 0 and K % 8 == 0");
+  if (M < 1) return fail(TL_E_RANGE, "M < 1");
+  if (!d_packed || !d_A || !d_C || !aligned(d_A, 16) || !aligned(d_C, 16)) return fail(TL_E_INVAL, "bad pointer");
+  const size_t need = tl_w4_linear_ws_bytes(N, K, M);
+  if (need > kNoallocScratchBytes)
+    return fail(TL_E_RANGE, "this shape needs " + std::to_string(need) + " bytes of split-K scratch, above the " +
+                                std::to_string(kNoallocScratchBytes) + "-byte static buffer");
+  void* ws = nullptr;
+  if (need > 0) {
+    const tl_status st = scratch_for_current_device(&ws);
+    if (st != TL_OK) return st;
+  }
+  return tl_w4_linear(d_packed, N, K, d_A, M, d_C, ws, stream);
 }
 
 tl_status tl_kv_quantize_rows(const uint16_t* d_x, int32_t rows, int32_t hd, int8_t* d_q, uint16_t* d_s,

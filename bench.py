@@ -220,7 +220,7 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
         algo = (wbytes * (s.n_pre + max(loops)) + s.vocab * s.d_model * 2
                 + sum(kv_per_tok * (s.n_pre + Lx) * (P + D // 2) for Lx in loops))
         roof_us = algo / (PEAK_HBM_GBS * 1e9) * 1e6
-        res[name] = {"ms_per_step": round(ms, 4), "lanes": nl, "loops": loops, "context": P + D,
+        res[name] = {"ms_per_step": round(ms, 4), "lanes": nl, "loops": loops, "context": P + D, "graph_replayed": False,
                      "algorithmic_bytes_per_step": int(algo), "hbm_roofline_us": round(roof_us, 1),
                      "frac": round(roof_us / (ms * 1e3), 4)}
         print(f"[bench] {name}: {ms:.4f} ms/step ({roof_us / (ms * 1e3):.1%} of the HBM roofline)",
@@ -388,6 +388,89 @@ def kernel_leg(s, tl, torch, stream):
     return res
 
 
+PMC_SHAPES = {"qkv": (6144, 2048), "o": (2048, 2048), "gate_up": (11264, 2048), "down": (2048, 5632)}
+
+
+def pmc_kernels(tl, torch):
+    """Eager launches for counter runs, each launch a dispatch of its own: per
+    loop-block linear shape, 4 W4A16 GEMMs at M = 1024 and 8 W4 GEMVs at M = 1
+    cycling through copies of the packed matrix that together exceed 320 MB
+    (cold weights); then 200 empty kernels and one plain 256 MiB device copy
+    (the calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+    for name, (N, K) in PMC_SHAPES.items():
+        qw = torch.randint(-2**31, 2**31 - 1, (N, K // 8), generator=g, dtype=torch.int32).cuda()
+        sc = (torch.rand((N, (K + 127) // 128), generator=g) * 0.002 + 0.002).half().cuda()
+        nb = tl.tl_qlinear_packed_bytes(N, K)
+        ncopy = -(-320 * 2**20 // nb)
+        packed = torch.empty((ncopy, -(-nb // 256) * 256), dtype=torch.uint8, device="cuda")
+        tl.tl_qlinear_pack(qw, sc, N, K, packed[0])
+        packed[1:].copy_(packed[0].expand(ncopy - 1, -1))
+        for M, reps in ((1024, 4), (1, 8)):
+            A = (torch.randn((M, K), generator=g) * 0.5).half().cuda()
+            C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(tl.tl_w4_linear_ws_bytes(N, K, M), 256), dtype=torch.uint8, device="cuda")
+            for i in range(reps):
+                tl.tl_w4_linear(packed[(i * 7) % ncopy], N, K, A, M, C, ws)
+            torch.cuda.synchronize()
+        print(f"[pmc] {name} N={N} K={K}: GEMM M=1024 x4, GEMV M=1 x8 over {ncopy} copies", file=sys.stderr,
+              flush=True)
+        del packed
+        torch.cuda.empty_cache()
+    tl.tl_launch_empty(200)
+    src = torch.ones(256 * 2**18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(dirs):
+    """Per kernel (name, grid) averages of every counter found in the given
+    rocprofv3 --pmc output directories (CSV), one line per kernel."""
+    import collections
+    import csv
+    import glob
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Kernel_Name"].split("(")[0][:60], int(r["Grid_Size"]))
+                    acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in acc.values() for c in v})
+    print("kernel".ljust(62) + "grid".rjust(9) + " n " + "".join(c[:24].rjust(26) for c in names))
+    for (k, grid), v in sorted(acc.items(), key=lambda kv: kv[0]):
+        n = max(len(x) for x in v.values())
+        print(k.ljust(62) + str(grid).rjust(9) + f"{n:3d}" +
+              "".join((f"{sum(v[c]) / len(v[c]):26.1f}" if v.get(c) else " " * 26) for c in names))
+
+
+def summarize_trace(csv_path):
+    """Per (kernel, grid) call count and average / median / min duration (us)
+    from a rocprofv3 --kernel-trace CSV, in descending total time."""
+    import collections
+    import csv
+    import statistics
+    d = collections.defaultdict(list)
+    meta = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0]
+            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+            wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 0)) or 0)
+            key = (name, grid)
+            d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            meta[key] = (wg, r.get("LDS_Block_Size", r.get("Lds_Size", "")), r.get("VGPR_Count", r.get("Arch_VGPR_Count", "")))
+    tot = sum(sum(v) for v in d.values())
+    print(" calls   avg_us   med_us   min_us   %time   blocks   wg  lds_B vgpr  kernel")
+    for key, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        wg, lds, vg = meta[key]
+        blocks = key[1] // wg if wg else key[1]
+        print(f"{len(v):6d} {sum(v) / len(v):8.2f} {statistics.median(v):8.2f} {min(v):8.2f} "
+              f"{100 * sum(v) / tot:7.2f} {blocks:8d} {wg:4d} {lds:>6} {vg:>4}  {key[0][:90]}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,9 +495,22 @@ def main():
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--pmc-kernels", action="store_true",
+                    help="only launch the single kernels for counter runs (GEMM M=1024, cold GEMV M=1, empty "
+                         "kernels) and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print per-kernel averages of the counters in rocprofv3 --pmc output dirs and exit (no GPU)")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace CSV and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mib or 256)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -432,6 +528,9 @@ def main():
     from looped_weight_shared_amd.model import Model
 
     torch.cuda.set_device(0)
+    if args.pmc_kernels:
+        pmc_kernels(tl, torch)
+        return
     s = synth.SHAPES["m407"]
     L, SEQ = 8, 128
     t0 = time.time()
@@ -511,20 +610,32 @@ def main():
             torch.cuda.synchronize()
             return ev[0].elapsed_time(ev[1])
 
+        def host_enqueue_ms():
+            # host time to enqueue one step (the calls return before the GPU is done)
+            m.reset(0)
+            m.prefill(ptoks, next_tok=bufs[0])
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            for t in range(D):
+                m.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            h = (time.perf_counter() - h0) * 1e3 / D
+            torch.cuda.synchronize()
+            return h
+
         decode_run(8, False)                       # warm-up
-        ms = decode_run(D, True)
-        ms_tok = ms / D
-        # host time to enqueue one step (the calls return before the GPU is done)
-        m.reset(0)
-        m.prefill(ptoks, next_tok=bufs[0])
-        torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        for t in range(D):
-            m.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
-        host_ms = (time.perf_counter() - h0) * 1e3 / D
-        torch.cuda.synchronize()
-        print(f"[bench] decode L={L} prompt {P} + {D} steps: {ms_tok:.4f} ms/token "
-              f"(host enqueue {host_ms:.4f} ms/step)", file=sys.stderr, flush=True)
+        ms_tok = decode_run(D, True) / D
+        host_ms = host_enqueue_ms()
+        # the same steps replayed from captured graphs (one per shape and
+        # token buffer; the part count changes every 128 keys): the host
+        # enqueues ~5x faster, the GPU time is a few percent higher
+        m.set_graphs(2)
+        decode_run(8, False)
+        ms_graph = decode_run(D, True) / D
+        host_graph = host_enqueue_ms()
+        m.set_graphs(0)
+        print(f"[bench] decode L={L} prompt {P} + {D} steps: {ms_tok:.4f} ms/token (host enqueue {host_ms:.4f} "
+              f"ms/step); graph-replayed {ms_graph:.4f} ms/token (host enqueue {host_graph:.4f} ms/step)",
+              file=sys.stderr, flush=True)
         # profiled pass
         m.reset(0)
         m.prefill(ptoks, next_tok=bufs[0])
@@ -548,6 +659,8 @@ def main():
                 + 2 * 2 * s.n_heads * s.head_dim * (s.n_pre + L) * (P + D / 2))
         out["decode"] = {"ms_per_token": round(ms_tok, 4), "prompt": P, "steps": D, "loops": L,
                          "kv": "fp16", "graph_replayed": False, "host_enqueue_ms_per_step": round(host_ms, 4),
+                         "graph_replayed_ms_per_token": round(ms_graph, 4),
+                         "graph_replayed_host_enqueue_ms_per_step": round(host_graph, 4),
                          "algorithmic_bytes_per_token": int(algo),
                          "hbm_roofline_ms_per_token": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
                          "frac_of_hbm_roofline": round(algo / (PEAK_HBM_GBS * 1e9) * 1e3 / ms_tok, 4),
@@ -660,6 +773,17 @@ def main():
     # ---------------------------------------------------------------- single kernels
     if not args.no_kernels:
         out["kernels"] = kernel_leg(s, tl, torch, stream)
+        # per-dispatch floor: back-to-back empty kernels, eager (event time / count)
+        tl.tl_launch_empty(100)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        tl.tl_launch_empty(2000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["dispatch_floor_us"] = round(e0.elapsed_time(e1) * 1e3 / 2000, 3)
+        print(f"[bench] empty kernels back to back: {out['dispatch_floor_us']} us each", file=sys.stderr,
+              flush=True)
 
     # ---------------------------------------------------------------- other workloads
     if not args.no_configs:

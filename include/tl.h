@@ -203,12 +203,23 @@ int32_t tl_length(const tl_ctx* ctx, int32_t lane);
 tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t n, float* d_hidden,
                      float* d_logits, int32_t* d_next, void* stream);
 
-/* Switches prefill graph capture/replay on (enable != 0) or off (the
- * default). Replay cuts the host's enqueue time per call (about 0.47 ->
- * 0.06 ms for the ~80 launches of a 10-layer prefill) but not the GPU
- * time, which the kernels and the per-dispatch gap set (it measured ~1.5%
- * higher than eager). Switching off frees the cached graph after its last
- * replay has finished. Errors: TL_E_INVAL (ctx NULL). */
+/* Graph capture/replay, off by default. enable is a bit mask: bit 0
+ * (value 1) prefill, bit 1 (value 2) decode steps. Replay cuts the host's
+ * enqueue time (about 0.47 -> 0.06 ms for the ~80 launches of a 10-layer
+ * prefill; decode steps, ~52 launches, likewise) but not the GPU time, which
+ * the kernels and the per-dispatch gap set.
+ * Decode: a step is captured once per (active lanes in order, their L, the
+ * decode attention's launch shape, which changes every 128 keys (256 beyond
+ * 1024), and the d_tokens/d_hidden/d_logits/d_next pointers) and replayed
+ * for later steps with the same key; up to 4 such graphs are kept (least
+ * recently replayed evicted). The lane positions are then read on the device
+ * from a copy in d_act_ws that each replay advances and that the call
+ * re-initialises (one small kernel) when prefill, reset, an eager step or a
+ * self-speculative round changed the lengths. Steps launch eagerly while a
+ * timing window or the safety check is on, for store-h caches, and inside
+ * tl_spec_decode's drafting. Results are bit-identical either way.
+ * Switching a kind off frees its graphs after their last replay finished.
+ * Errors: TL_E_INVAL (ctx NULL), TL_E_RANGE (enable outside 0..3). */
 tl_status tl_set_graphs(tl_ctx* ctx, int32_t enable);
 
 /* One cached decode step for every lane with h_active[lane] != 0 (h_active
@@ -306,6 +317,12 @@ tl_status tl_profile_begin(tl_ctx* ctx, int32_t max_launches);
 /* total_ms double[TL_K_COUNT], count int32[TL_K_COUNT] (host arrays).
  * Errors: TL_E_STATE if no window is open, TL_E_HIP. */
 tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count);
+
+/* Enqueues n empty kernels (one 64-thread block each) on `stream`: the
+ * per-dispatch floor of the stack, against which the short kernels of the
+ * forward pass are measured. Errors: TL_E_RANGE (n outside 0..1000000),
+ * TL_E_HIP. */
+tl_status tl_launch_empty(int32_t n, void* stream);
 
 /* ---- single kernels ----------------------------------------------------
  * The same kernels the forward pass runs, exposed for per-kernel parity

@@ -27,7 +27,7 @@ __all__ = [
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
     "tl_qlinear_packed_f16_bytes", "tl_qlinear_pack_f16",
     "tl_qlinear_unpack", "tl_w4_linear_ws_bytes", "tl_w4_linear", "tl_w4_linear_noalloc_max_bytes",
-    "tl_w4_linear_noalloc", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end",
+    "tl_w4_linear_noalloc", "tl_kv_quantize_rows", "tl_profile_begin", "tl_profile_end", "tl_launch_empty",
     "KERNEL_KINDS", "EXPORTED",
 ]
 
@@ -112,6 +112,7 @@ _SIGS = {
     "tl_w4_linear_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
     "tl_kv_quantize_rows": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "tl_profile_begin": (ctypes.c_int, [_vp, _i32]),
+    "tl_launch_empty": (ctypes.c_int, [_i32, _vp]),
     "tl_profile_end": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]),
 }
 EXPORTED = tuple(_SIGS)
@@ -199,8 +200,9 @@ def tl_safety_last(ctx):
     return it.value, row.value
 
 
-def tl_set_graphs(ctx, enable: bool) -> None:
-    _check(lib.tl_set_graphs(ctx, 1 if enable else 0))
+def tl_set_graphs(ctx, enable) -> None:
+    """enable: bit mask, 1 = prefill, 2 = decode steps (True = 1, False = 0)."""
+    _check(lib.tl_set_graphs(ctx, int(enable)))
 
 
 def tl_get_loops(ctx, lane: int) -> int:
@@ -286,6 +288,10 @@ def tl_kv_quantize_rows(x, rows: int, hd: int, q, s, stream=None) -> None:
 
 KERNEL_KINDS = ("embed", "norm", "qkv", "rope_kv", "attn", "o", "gate_up", "down", "head", "argmax", "copy",
                 "safety")
+
+
+def tl_launch_empty(n: int, stream=None) -> None:
+    _check(lib.tl_launch_empty(n, _stream(stream)))
 
 
 def tl_profile_begin(ctx, max_launches: int) -> None:

@@ -403,6 +403,21 @@ int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv) {
   return np;
 }
 
+void attn_decode_shape(int M, const RowMap& rm, const KvGeom& kv, int* out) {
+  int maxctx = 1, bw = 4;
+  for (int m = 0; m < M; ++m) {
+    const int ctx = rm.row_pos[m] + 1 - kv_first(kv, rm.row_pos[m]);
+    const int w = dec_part_waves(ctx);
+    maxctx = max(maxctx, ctx);
+    bw = max(bw, w);
+    out[3 + 2 * m] = w;
+    out[4 + 2 * m] = (ctx + kDecChunk * w - 1) / (kDecChunk * w);
+  }
+  out[0] = bw;
+  out[1] = (maxctx + bw * kDecChunk - 1) / (bw * kDecChunk);
+  out[2] = attn_decode_parts(M, rm, kv);
+}
+
 // BW waves per block (the largest part of the call's rows): a block covers
 // BW * 32 keys and writes BW / W parts of a row whose parts have W waves.
 template <int HD, bool I8, int BW>
@@ -416,7 +431,24 @@ __global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __res
   __shared__ float red_o[BW][64 / (HD / 8)][HD];  // per wave and key row of a pass
   __shared__ float red_m[BW], red_l[BW];
   const int bp = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
-  const int pos = rm.row_pos[m];
+  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
+  const int sub = ln % LPK, kg = ln / LPK, d0 = sub * 8;
+  const int d = kv.H * HD;
+  // ---- 1. projections of this row (8 dims + their RoPE partners): they do
+  // not depend on the position, so they are requested before it is known (a
+  // graph-replayed step reads the position from device memory)
+  const bool lo = d0 < HALF;
+  const int i0 = lo ? d0 : d0 - HALF;  // pair index of the first dim
+  const float* row = qkv + (size_t)m * 3 * d;
+  const float4_t* q1p = reinterpret_cast<const float4_t*>(row + h * HD + i0);
+  const float4_t* q2p = reinterpret_cast<const float4_t*>(row + h * HD + i0 + HALF);
+  const float4_t* k1p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0);
+  const float4_t* k2p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0 + HALF);
+  const float4_t* vp = reinterpret_cast<const float4_t*>(row + 2 * d + h * HD + d0);
+  float4_t q1[2] = {q1p[0], q1p[1]}, q2[2] = {q2p[0], q2p[1]};
+  float4_t k1[2] = {k1p[0], k1p[1]}, k2[2] = {k2p[0], k2p[1]};
+  float4_t vv[2] = {vp[0], vp[1]};
+  const int pos = rm.dpos ? rm.dpos[rm.row_lane[m]] : rm.row_pos[m];
   const int kbeg = kv_first(kv, pos);  // keys kbeg .. pos are visible
   const int ctx = pos + 1 - kbeg;
   const int W = BW == 4 ? 4 : dec_part_waves(ctx), ppb = BW / W;  // waves per part, parts per block
@@ -430,29 +462,14 @@ __global__ __launch_bounds__(BW * 64) void attn_decode_kernel(const float* __res
     }
     return;
   }
-  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
-  const int sub = ln % LPK, kg = ln / LPK, d0 = sub * 8;
-  const int d = kv.H * HD;
   const int lane_id = rm.row_lane[m];
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   const int rowb = I8 ? HD : 2 * HD;
   const int k0 = kbeg + (bp * BW + wave) * kDecChunk;
   const bool active = k0 <= pos;
-
-  // ---- 1. projections of this row (8 dims + their RoPE partners) and cos/sin
-  const bool lo = d0 < HALF;
-  const int i0 = lo ? d0 : d0 - HALF;  // pair index of the first dim
-  const float* row = qkv + (size_t)m * 3 * d;
-  const float4_t* q1p = reinterpret_cast<const float4_t*>(row + h * HD + i0);
-  const float4_t* q2p = reinterpret_cast<const float4_t*>(row + h * HD + i0 + HALF);
-  const float4_t* k1p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0);
-  const float4_t* k2p = reinterpret_cast<const float4_t*>(row + d + h * HD + i0 + HALF);
-  const float4_t* vp = reinterpret_cast<const float4_t*>(row + 2 * d + h * HD + d0);
+  // cos/sin of the position
   const float4_t* cp4 = reinterpret_cast<const float4_t*>(rope_cs + (size_t)pos * HALF + i0);
   const float4_t* sp4 = reinterpret_cast<const float4_t*>(rope_cs + (size_t)kv.S * HALF + (size_t)pos * HALF + i0);
-  float4_t q1[2] = {q1p[0], q1p[1]}, q2[2] = {q2p[0], q2p[1]};
-  float4_t k1[2] = {k1p[0], k1p[1]}, k2[2] = {k2p[0], k2p[1]};
-  float4_t vv[2] = {vp[0], vp[1]};
   float4_t cs[2] = {cp4[0], cp4[1]}, sn[2] = {sp4[0], sp4[1]};
 
   // ---- 2. the chunk's cached keys and values (positions < pos)

@@ -479,7 +479,8 @@ __global__ __launch_bounds__(256) void head_kernel(const float* __restrict__ x, 
 // largest logit, ties to the lowest index (a total order, so the result does
 // not depend on the scan order).
 __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ cval, const int* __restrict__ cidx,
-                                                     int nblk, RowMap rm, int32_t* __restrict__ next) {
+                                                     int nblk, RowMap rm, int32_t* __restrict__ next,
+                                                     int* __restrict__ advance) {
   __shared__ float bv_s[4];
   __shared__ int bi_s[4];
   const int m = blockIdx.x, tid = threadIdx.x;
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ c
         bi_s[0] = bi_s[w];
       }
     next[out_row(rm, m)] = bi_s[0] == 0x7fffffff ? 0 : bi_s[0];
+    if (advance) advance[rm.row_lane[m]] += 1;  // a graph-replayed decode step's last kernel
   }
 }
 
@@ -556,12 +558,13 @@ hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, 
   return hipGetLastError();
 }
 
-hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s) {
+hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s,
+                         int* advance) {
   if (M < 1 || M > 8) return hipErrorInvalidValue;
   const int nblk = (V + 15) / 16;
   const float* cval = static_cast<const float*>(scratch);
   const int* cidx = reinterpret_cast<const int*>(cval + (size_t)M * nblk);
-  launch(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next);
+  launch(argmax_kernel, dim3(M), dim3(256), 0, s, cval, cidx, nblk, rm, next, advance);
   return hipGetLastError();
 }
 
@@ -634,6 +637,29 @@ __global__ void scatter_rows_kernel(const float* __restrict__ src, int d, RowMap
 
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s) {
   launch(scatter_rows_kernel, dim3(M), dim3(256), 0, s, src, d, rm, dst);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decode positions
+__global__ void set_pos_kernel(int* __restrict__ dpos, PosArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.n) dpos[i] = a.v[i];
+}
+
+hipError_t launch_set_pos(int* dpos, const PosArgs& a, hipStream_t s) {
+  if (a.n < 0 || a.n > 8) return hipErrorInvalidValue;
+  launch(set_pos_kernel, dim3(1), dim3(64), 0, s, dpos, a);
+  return hipGetLastError();
+}
+
+__global__ void advance_pos_kernel(int* __restrict__ dpos, RowMap rm, int M) {
+  const int m = threadIdx.x;
+  if (m < M) dpos[rm.row_lane[m]] += 1;
+}
+
+hipError_t launch_advance_pos(int* dpos, const RowMap& rm, int M, hipStream_t s) {
+  if (M < 1 || M > 8) return hipErrorInvalidValue;
+  launch(advance_pos_kernel, dim3(1), dim3(64), 0, s, dpos, rm, M);
   return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ constexpr int kSpecMaxDraft = 7;
 int head_rows_cap(const tl_config* c) { return std::max(c->n_lanes, kSpecMaxDraft + 1); }
 
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, hkv, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, dpos, hkv, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -135,6 +135,7 @@ ActLayout act_layout(const tl_config* c) {
   // tokens and verifier argmaxes [kSpecMaxDraft + 1] each
   L.spec = off; off += al256(((size_t)(kSpecMaxDraft + 2) * c->n_lanes + 2 * (kSpecMaxDraft + 1)) * 4);
   L.safety = off; off += al256(4);  // first tripped (iteration, row) code of the safety check
+  L.dpos = off; off += al256(8 * 4);  // lane positions read by graph-replayed decode steps
   // store-h: K/V rebuilt for one layer, FP16 [lane][K|V][H][max_seq][hd]
   L.hkv = off;
   if (c->kv_dtype == TL_KV_H16) off += al256((size_t)c->n_lanes * 2 * c->max_seq * c->d_model * 2);
@@ -180,10 +181,23 @@ struct tl_ctx {
   int safety_iter = -1, safety_row = -1;  // last trip reported
   std::vector<int> len, loops, depth;  // depth: effective layers every cached token has
   int32_t spec_host[16];               // host side of the speculative token exchange
-  // optional: prefill launch sequences captured as a HIP graph and replayed
-  // when a later call has the same shape and pointers (cuts host enqueue
-  // time; the GPU time per step is not lower than eager launches)
-  bool graphs = false;
+  // optional: launch sequences captured as HIP graphs and replayed when a
+  // later call has the same shape and pointers (cuts host enqueue time):
+  // bit 0 prefill, bit 1 decode steps (tl_set_graphs)
+  int graph_mask = 0;
+  // decode graphs read the lane positions from here (device int32 [n_lanes]);
+  // dpos_synced: it equals len[] as of the stream's tail
+  int32_t* dpos = nullptr;
+  bool dpos_synced = false;
+  bool force_eager = false;  // self-speculative drafting: plain launches
+  struct DecodeGraph {
+    std::vector<long long> key;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;  // recorded after each replay
+    unsigned long long used = 0;
+  };
+  std::vector<DecodeGraph> dgraphs;
+  unsigned long long dgraph_clock = 0;
   bool h_ready = false;  // c->h holds the next linear's normalised input (fused embed + RMSNorm)
   // the first layer's rows are still the embedding rows of these tokens (the
   // first GEMV reads them directly and writes x); emb_rm maps row -> token
@@ -213,6 +227,7 @@ namespace {
 // Sets the kind under which the launches inside the scope are timed while a
 // timing window is open (each launch records its own event pair).
 void drop_prefill_graph(tl_ctx* ctx);
+void drop_decode_graphs(tl_ctx* ctx);
 
 struct KScope {
   KScope(tl_ctx* ctx, int kind, hipStream_t) {
@@ -625,6 +640,7 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->spec_ver = c->spec_chain + (size_t)(kSpecMaxDraft + 2) * cfg->n_lanes;
   c->spec_next = c->spec_ver + (kSpecMaxDraft + 1);
   c->safety_res = reinterpret_cast<int*>(ab + L.safety);
+  c->dpos = reinterpret_cast<int32_t*>(ab + L.dpos);
   c->pend = tl::Pending{nullptr, 1};
   c->len.assign(cfg->n_lanes, 0);
   c->loops.assign(cfg->n_lanes, 1);
@@ -637,6 +653,7 @@ tl_status tl_destroy(tl_ctx* ctx) {
   if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
   for (auto& e : ctx->prof_ev) (void)hipEventDestroy(e);
   drop_prefill_graph(ctx);
+  drop_decode_graphs(ctx);
   if (ctx->pg_done) (void)hipEventDestroy(ctx->pg_done);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   delete ctx;
@@ -671,6 +688,7 @@ tl_status tl_reset(tl_ctx* ctx, int32_t lane) {
     ctx->len[l] = 0;
     ctx->depth[l] = INT_MAX;
   }
+  ctx->dpos_synced = false;
   return TL_OK;
 }
 
@@ -774,6 +792,146 @@ void drop_prefill_graph(tl_ctx* ctx) {
   ctx->pg = tl_ctx::PrefillGraph{};
 }
 
+// The launches of one decode step over `rows` (the state update is the
+// caller's). replay: the step is being captured for graph replay, so the
+// decode attention reads the positions from ctx->dpos and a last kernel
+// advances them.
+tl_status enqueue_decode(tl_ctx* ctx, const std::vector<int>& rows, tl::RowMap rm, const int32_t* d_tokens,
+                         float* d_hidden, float* d_logits, int32_t* d_next, hipStream_t s, bool replay) {
+  const tl_config& C = ctx->cfg;
+  const int M = (int)rows.size(), d = C.d_model;
+  const bool safe = ctx->safety_max > 0.f;
+  if (replay) rm.dpos = ctx->dpos;
+  ctx->h_ready = false;
+  ctx->emb_tokens = nullptr;
+  ctx->pend = tl::Pending{nullptr, 1};  // nothing carries over from an earlier call
+  if (safe) {
+    KScope k(ctx, TL_K_SAFETY, s);
+    TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
+  }
+  const int Lmax = ctx->loops[rows[0]];
+  if (C.n_pre + Lmax > 0 && !ctx->hmode) {
+    ctx->emb_tokens = d_tokens;  // the first layer's QKV GEMV gathers the rows
+    ctx->emb_rm = rm;
+  } else {
+    KScope k(ctx, TL_K_EMBED, s);
+    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, C.vocab, ctx->x, s));
+  }
+  for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
+    int Ml = 0;
+    while (Ml < M && C.n_pre + ctx->loops[rows[Ml]] > layer) ++Ml;
+    const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
+    tl_status st = run_layer(ctx, B, layer, Ml, rm, true, s);
+    if (st != TL_OK) return st;
+    if (safe && layer >= C.n_pre) {
+      KScope k(ctx, TL_K_SAFETY, s);
+      TL_HIP(tl::launch_safety_check(ctx->x, ctx->pend, Ml, d, ctx->safety_max,
+                                     (layer - C.n_pre) << tl::kSafetyRowBits, ctx->safety_res, s));
+    }
+  }
+  if (d_logits || d_next) {
+    float* lg = d_logits ? d_logits : ctx->logits;
+    {
+      KScope k(ctx, TL_K_HEAD, s);
+      TL_HIP(tl::launch_head(ctx->x, M, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg, rm, ctx->hscr, s));
+    }
+  }
+  if (d_hidden) {
+    KScope k(ctx, TL_K_COPY, s);
+    TL_HIP(tl::launch_scatter_rows(ctx->x, M, d, rm, d_hidden, s));
+  }
+  // argmax last: a replayed step advances the device positions in it
+  if (d_next) {
+    KScope k(ctx, TL_K_ARGMAX, s);
+    TL_HIP(tl::launch_argmax(M, C.vocab, rm, ctx->hscr, d_next, s, replay ? ctx->dpos : nullptr));
+  } else if (replay) {
+    KScope k(ctx, TL_K_COPY, s);
+    TL_HIP(tl::launch_advance_pos(ctx->dpos, rm, M, s));
+  }
+  return TL_OK;
+}
+
+constexpr int kMaxDecodeGraphs = 4;  // e.g. alternating token buffers, or a few lane sets
+
+void drop_decode_graphs(tl_ctx* ctx) {
+  for (auto& g : ctx->dgraphs) {
+    if (g.done) (void)hipEventSynchronize(g.done);  // its last replay may still run
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.done) (void)hipEventDestroy(g.done);
+  }
+  ctx->dgraphs.clear();
+}
+
+// One decode step from a captured graph. The graph is keyed by everything
+// its launches depend on except the lane positions: the rows (lanes, in
+// order) and their L, the decode attention's launch shape (grid, block width
+// and parts per row, which change every 128 or 256 keys) and the caller's
+// pointers. The positions are read on the device from ctx->dpos, which the
+// host sets only when its own view changed since the last replay (prefill,
+// reset, eager steps); each replay advances them itself.
+tl_status decode_graph_launch(tl_ctx* ctx, const std::vector<int>& rows, const tl::RowMap& rm,
+                              const int32_t* d_tokens, float* d_hidden, float* d_logits, int32_t* d_next,
+                              hipStream_t s) {
+  const int M = (int)rows.size();
+  std::vector<long long> key;
+  key.push_back(M);
+  for (int m = 0; m < M; ++m) {
+    key.push_back(rows[m]);
+    key.push_back(ctx->loops[rows[m]]);
+  }
+  int shape[3 + 2 * 8];
+  tl::attn_decode_shape(M, rm, ctx->kv, shape);
+  key.insert(key.end(), shape, shape + 3 + 2 * M);
+  for (const void* p : {(const void*)d_tokens, (const void*)d_hidden, (const void*)d_logits, (const void*)d_next})
+    key.push_back((long long)reinterpret_cast<uintptr_t>(p));
+  if (!ctx->dpos_synced) {
+    tl::PosArgs a{};
+    a.n = ctx->cfg.n_lanes;
+    for (int l = 0; l < a.n; ++l) a.v[l] = ctx->len[l];
+    KScope k(ctx, TL_K_COPY, s);
+    TL_HIP(tl::launch_set_pos(ctx->dpos, a, s));
+    ctx->dpos_synced = true;
+  }
+  tl_ctx::DecodeGraph* g = nullptr;
+  for (auto& e : ctx->dgraphs)
+    if (e.key == key) g = &e;
+  if (!g) {
+    if (!ctx->cap_stream) TL_HIP(hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking));
+    hipGraph_t graph = nullptr;
+    TL_HIP(hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal));
+    tl_status st = enqueue_decode(ctx, rows, rm, d_tokens, d_hidden, d_logits, d_next, ctx->cap_stream, true);
+    const hipError_t ce = hipStreamEndCapture(ctx->cap_stream, &graph);
+    if (st != TL_OK || ce != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st != TL_OK ? st : fail(TL_E_HIP, std::string("decode graph capture: ") + hipGetErrorString(ce));
+    }
+    tl_ctx::DecodeGraph e;
+    const hipError_t ie = hipGraphInstantiate(&e.exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) return fail(TL_E_HIP, std::string("decode graph instantiate: ") + hipGetErrorString(ie));
+    const hipError_t ee = hipEventCreateWithFlags(&e.done, hipEventDisableTiming);
+    if (ee != hipSuccess) {
+      (void)hipGraphExecDestroy(e.exec);
+      return fail(TL_E_HIP, std::string("hipEventCreate: ") + hipGetErrorString(ee));
+    }
+    e.key = std::move(key);
+    if ((int)ctx->dgraphs.size() >= kMaxDecodeGraphs) {  // evict the least recently replayed
+      auto lru = std::min_element(ctx->dgraphs.begin(), ctx->dgraphs.end(),
+                                  [](const tl_ctx::DecodeGraph& a, const tl_ctx::DecodeGraph& b) { return a.used < b.used; });
+      (void)hipEventSynchronize(lru->done);
+      (void)hipGraphExecDestroy(lru->exec);
+      (void)hipEventDestroy(lru->done);
+      ctx->dgraphs.erase(lru);
+    }
+    ctx->dgraphs.push_back(std::move(e));
+    g = &ctx->dgraphs.back();
+  }
+  g->used = ++ctx->dgraph_clock;
+  TL_HIP(hipGraphLaunch(g->exec, s));
+  TL_HIP(hipEventRecord(g->done, s));
+  return TL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -790,7 +948,8 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
   const int L = ctx->loops[lane];
   if (p0 > 0 && C.n_pre + L > ctx->depth[lane]) return fail(TL_E_STATE, "lane's L is deeper than its cache");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!ctx->graphs || ctx->prof_on || ctx->safety_max > 0.f) {
+  ctx->dpos_synced = false;  // the lane's length changes
+  if (!(ctx->graph_mask & 1) || ctx->prof_on || ctx->safety_max > 0.f) {
     st = enqueue_prefill(ctx, lane, d_tokens, n, d_hidden, d_logits, d_next, p0, L, s);
     if (st != TL_OK) return st;
   } else {
@@ -851,8 +1010,10 @@ tl_status tl_safety_last(const tl_ctx* ctx, int32_t* iteration, int32_t* row) {
 
 tl_status tl_set_graphs(tl_ctx* ctx, int32_t enable) {
   if (!ctx) return fail(TL_E_INVAL, "ctx is NULL");
-  ctx->graphs = enable != 0;
-  if (!ctx->graphs) drop_prefill_graph(ctx);
+  if (enable < 0 || enable > 3) return fail(TL_E_RANGE, "enable must be 0..3 (bit 0 prefill, bit 1 decode)");
+  ctx->graph_mask = enable;
+  if (!(enable & 1)) drop_prefill_graph(ctx);
+  if (!(enable & 2)) drop_decode_graphs(ctx);
   return TL_OK;
 }
 
@@ -879,50 +1040,15 @@ tl_status tl_decode_step(tl_ctx* ctx, const int32_t* d_tokens, const uint8_t* h_
     rm.row_pos[m] = ctx->len[rows[m]];
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int d = C.d_model;
   const bool safe = ctx->safety_max > 0.f;
-  ctx->h_ready = false;
-  ctx->emb_tokens = nullptr;
-  ctx->pend = tl::Pending{nullptr, 1};  // nothing carries over from an earlier call
-  if (safe) {
-    KScope k(ctx, TL_K_SAFETY, s);
-    TL_HIP(tl::launch_safety_reset(ctx->safety_res, s));
-  }
-  const int Lmax = ctx->loops[rows[0]];
-  if (C.n_pre + Lmax > 0 && !ctx->hmode) {
-    ctx->emb_tokens = d_tokens;  // the first layer's QKV GEMV gathers the rows
-    ctx->emb_rm = rm;
-  } else {
-    KScope k(ctx, TL_K_EMBED, s);
-    TL_HIP(tl::launch_embed(ctx->embed, d_tokens, M, rm, d, C.vocab, ctx->x, s));
-  }
-  for (int layer = 0; layer < C.n_pre + Lmax; ++layer) {
-    int Ml = 0;
-    while (Ml < M && C.n_pre + ctx->loops[rows[Ml]] > layer) ++Ml;
-    const BlockW& B = ctx->blocks[std::min(layer, C.n_pre)];
-    tl_status st = run_layer(ctx, B, layer, Ml, rm, true, s);
-    if (st != TL_OK) return st;
-    if (safe && layer >= C.n_pre) {
-      KScope k(ctx, TL_K_SAFETY, s);
-      TL_HIP(tl::launch_safety_check(ctx->x, ctx->pend, Ml, d, ctx->safety_max,
-                                     (layer - C.n_pre) << tl::kSafetyRowBits, ctx->safety_res, s));
-    }
-  }
-  if (d_logits || d_next) {
-    float* lg = d_logits ? d_logits : ctx->logits;
-    {
-      KScope k(ctx, TL_K_HEAD, s);
-      TL_HIP(tl::launch_head(ctx->x, M, ctx->final_norm, C.rms_eps, ctx->head, C.vocab, d, lg, rm, ctx->hscr, s));
-    }
-    if (d_next) {
-      KScope k(ctx, TL_K_ARGMAX, s);
-      TL_HIP(tl::launch_argmax(M, C.vocab, rm, ctx->hscr, d_next, s));
-    }
-  }
-  if (d_hidden) {
-    KScope k(ctx, TL_K_COPY, s);
-    TL_HIP(tl::launch_scatter_rows(ctx->x, M, d, rm, d_hidden, s));
-  }
+  // graph replay (tl_set_graphs bit 1) unless a timing window or the safety
+  // check is on, the cache is store-h (its launch shapes change every step)
+  // or a self-speculative round is drafting
+  const bool replay = (ctx->graph_mask & 2) && !ctx->prof_on && !safe && !ctx->hmode && !ctx->force_eager;
+  tl_status st = replay ? decode_graph_launch(ctx, rows, rm, d_tokens, d_hidden, d_logits, d_next, s)
+                        : enqueue_decode(ctx, rows, rm, d_tokens, d_hidden, d_logits, d_next, s, false);
+  if (st != TL_OK) return st;
+  if (!replay) ctx->dpos_synced = false;  // eager steps do not advance the device positions
   for (int l : rows) {
     ctx->len[l] += 1;
     ctx->depth[l] = std::min(ctx->depth[l], C.n_pre + ctx->loops[l]);
@@ -970,11 +1096,14 @@ tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft
       break;
     }
     const int k = std::min(k_draft, C.max_seq - p - 1);  // positions p .. p+k must fit
-    // draft: k cached decode steps at draft_loops
+    // draft: k cached decode steps at draft_loops (plain launches: each step
+    // reads another row of the token chain, which a graph would key on)
     ctx->loops[lane] = draft_loops;
+    ctx->force_eager = true;
     for (int i = 0; i < k && st == TL_OK; ++i)
       st = tl_decode_step(ctx, chain + (size_t)i * nl, active.data(), nullptr, nullptr, chain + (size_t)(i + 1) * nl,
                           stream);
+    ctx->force_eager = false;
     ctx->loops[lane] = Lv;
     // verify: tokens t0..tk as one prefill at p with the head on every row
     // (after a failure: the drafted rows are dropped the same way)
@@ -1022,6 +1151,7 @@ tl_status tl_spec_decode(tl_ctx* ctx, int32_t lane, int32_t token, int32_t draft
   }
   ctx->loops[lane] = Lv;
   ctx->depth[lane] = depth0;
+  ctx->dpos_synced = false;  // the lane's length was set back and forth
   acc.emitted = emitted;
   if (stats) *stats = acc;
   return st;
@@ -1072,6 +1202,22 @@ tl_status tl_profile_end(tl_ctx* ctx, double* total_ms, int32_t* count) {
 }
 
 // ---------------------------------------------------------------- single kernels
+}  // extern "C"
+
+namespace {
+__global__ void empty_kernel() {}
+}  // namespace
+
+extern "C" {
+
+tl_status tl_launch_empty(int32_t n, void* stream) {
+  if (n < 0 || n > 1000000) return fail(TL_E_RANGE, "n outside 0..1000000");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+  TL_HIP(hipGetLastError());
+  return TL_OK;
+}
+
 size_t tl_qlinear_packed_bytes(int32_t N, int32_t K) {
   if (N < 16 || N % 16 || K < 8 || K % 8) return 0;
   return tl::packed_bytes(N, K);

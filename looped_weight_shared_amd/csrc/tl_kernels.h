@@ -186,7 +186,21 @@ struct RowMap {
   int lane, p0;
   int row_lane[8];
   int row_pos[8];
+  // Decode steps replayed from a graph read row m's position on the device,
+  // dpos[row_lane[m]] (advanced by launch_advance_pos at the end of each
+  // step), so one captured step serves every position with the same launch
+  // shape; row_pos keeps the host's values, which plan the launches.
+  const int* dpos = nullptr;
 };
+
+// Device copy of the lanes' positions for graph-replayed decode steps.
+struct PosArgs {
+  int v[8];
+  int n;
+};
+hipError_t launch_set_pos(int* dpos, const PosArgs& a, hipStream_t s);
+// dpos[row_lane[m]] += 1 for the M rows of a decode step.
+hipError_t launch_advance_pos(int* dpos, const RowMap& rm, int M, hipStream_t s);
 
 // RoPE on q and k of qkv fp32 [M][3d] (the sum of S split-K partials, each
 // [M][3d], in split order), fp16 Q out [M][d], K/V into cache layer.
@@ -208,6 +222,10 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
 // the O projection merges them (ASrc::att).
 size_t attn_decode_scratch_floats(int max_rows, int H, int hd, int S);
 int attn_decode_parts(int M, const RowMap& rm, const KvGeom& kv);  // parts written per (row, head) this call
+// Everything the decode attention's launch depends on besides the positions
+// themselves (grid, block width, parts per row): equal shapes let a captured
+// decode step be replayed at the next positions. Writes 3 + 2 * M ints.
+void attn_decode_shape(int M, const RowMap& rm, const KvGeom& kv, int* out);
 int attn_decode_np_max(int S);                  // part slots per (row, head)
 hipError_t launch_attn_decode(const float* qkv, int M, const RowMap& rm, const float* rope_cs, const KvGeom& kv,
                               int layer, float* part, uint16_t* o, hipStream_t s);
@@ -223,8 +241,11 @@ size_t head_scratch_bytes(int max_rows, int V);
 hipError_t launch_head(const float* x, int M, const uint16_t* gamma, float eps, const uint8_t* head_tiles, int V,
                        int d, float* logits, const RowMap& rm, void* scratch, hipStream_t s);
 // next[out_row(m)] = argmax of row m's logits, from the head's per-block
-// candidates in `scratch` (ties: lowest index).
-hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s);
+// candidates in `scratch` (ties: lowest index). advance (optional): also
+// advance[row_lane[m]] += 1 (the device positions of a graph-replayed decode
+// step, so that it needs no kernel of its own for them).
+hipError_t launch_argmax(int M, int V, const RowMap& rm, const void* scratch, int32_t* next, hipStream_t s,
+                         int* advance = nullptr);
 // dst[row_lane[m] * d] = src[m * d] for m < M (decode output rows by lane).
 hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm, float* dst, hipStream_t s);
 

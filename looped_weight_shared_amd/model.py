@@ -94,7 +94,8 @@ class Model:
     def safety_last(self):
         return tl_safety_last(self.ctx)
 
-    def set_graphs(self, enable: bool):
+    def set_graphs(self, enable):
+        """bit mask: 1 = prefill, 2 = decode steps (True = 1)."""
         tl_set_graphs(self.ctx, enable)
 
     def get_loops(self, lane):

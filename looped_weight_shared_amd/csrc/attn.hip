@@ -338,8 +338,249 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   }
 }
 
+// Short calls (M <= kShortMaxM rows: the 128-token benchmark step, chunked
+// prefill tails, speculative verification): one block per (16 queries, head),
+// so a 128-token call has 128 blocks instead of 32. Its 4 waves take the
+// block's visible keys in 32-key chunks round-robin, each with its own online
+// softmax, and need no block barrier until the final merge: a wave requests
+// its K rows straight from the cache in MFMA A-operand order (key row, 8
+// dims per lane), stages its V chunk in its own LDS slot (row-major, read back
+// with the transposing LDS read as in the tiled kernel) and keeps P in
+// registers; causally invisible chunks are never loaded. The 4 wave states
+// are merged in wave order at the end.
+constexpr int kShortQ = 16;       // queries per block
+constexpr int kShortChunk = 32;   // keys per wave step
+constexpr int kShortMaxM = 128;   // and at most 8 chunks (256 keys) visible to the call
+template <int HD, bool I8>
+__global__ __launch_bounds__(256) void attn_prefill_short_kernel(const uint16_t* __restrict__ q, int M, int lane_id,
+                                                                 int p0, KvGeom kv, int layer,
+                                                                 uint16_t* __restrict__ o) {
+  constexpr int KS = HD / 32;                  // k-steps of S^T = K Q^T
+  constexpr int DB = HD / 16;                  // 16-dim blocks of O
+  constexpr int LV = HD + 16;                  // LDS row stride of a wave's V chunk (halves)
+  constexpr int VCH = kShortChunk * HD / 8 / 64;  // 8-element V chunks per lane and key chunk
+  constexpr int RW = 4 + 4 * DB;               // floats per lane in the merge
+  static_assert(64 * RW * 4 <= kShortChunk * LV * 2, "merge state fits a wave's V slot");
+  using Raw = typename std::conditional<I8, uint2, u32x4_t>::type;
+  constexpr int ESZ = I8 ? 1 : 2;              // bytes per cached element
+  __shared__ __align__(16) _Float16 Vw[4][kShortChunk * LV];
+
+  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
+  const int l16 = ln & 15, lq = ln >> 4;
+  const int h = blockIdx.y;
+  const int q0 = blockIdx.x * kShortQ;
+  const int d = kv.H * HD;
+  const int kend = p0 + min(q0 + kShortQ, M);  // keys [kbeg, kend) can be visible to this block
+  const int kbeg = kv_first(kv, p0 + q0);
+  const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);  // log2 units: weights are 2^x
+  const int nch = (kend - kbeg + kShortChunk - 1) / kShortChunk;
+
+  // Q fragments (B operand): query q0 + l16, dims 32s + 8lq .. +7
+  half8_t qf[KS];
+  {
+    const int qr = q0 + l16, qc = min(qr, M - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(q + (size_t)qc * d + h * HD + 32 * s + 8 * lq);
+      qf[s] = qr < M ? __builtin_bit_cast(half8_t, v) : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  const int qpos = p0 + q0 + l16;
+  const int kfirst = kv_first(kv, qpos);
+  auto to_f16 = [&](const Raw& r) -> half8_t {
+    if constexpr (I8) {
+      half8_t hv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hv[j] = (_Float16)(float)(int8_t)((r.x >> (8 * j)) & 0xFF);
+        hv[4 + j] = (_Float16)(float)(int8_t)((r.y >> (8 * j)) & 0xFF);
+      }
+      return hv;
+    } else {
+      return __builtin_bit_cast(half8_t, r);
+    }
+  };
+
+  float mrow = -INFINITY, lrow = 0.f;
+  float4_t oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  _Float16* const vw = Vw[wave];
+
+  for (int c = wave; c < nch; c += 4) {
+    const int key0 = kbeg + c * kShortChunk;  // this chunk: keys key0 .. key0 + 31
+    // ---- requests: K fragments (key row key0 + 16kb + l16, dims 32s + 8lq ..),
+    // V rows (linear chunk e = ln + 64i: key e / (HD/8), dims 8 (e % (HD/8)) ..),
+    // INT8 scales of the keys this lane scores (16kb + 4lq + r)
+    Raw kr[2][KS], vr[VCH];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const size_t row = (size_t)kv_slot(kv, min(key0 + 16 * kb + l16, kend - 1)) * HD * ESZ;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kr[kb][s] = *reinterpret_cast<const Raw*>(cp.k + row + (32 * s + 8 * lq) * ESZ);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int e = ln + 64 * i, r = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
+      vr[i] = *reinterpret_cast<const Raw*>(cp.v + (size_t)kv_slot(kv, min(key0 + r, kend - 1)) * HD * ESZ + d0 * ESZ);
+    }
+    uint32_t ksr[I8 ? 8 : 1], vsr[I8 ? 8 : 1];
+    if constexpr (I8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int slot = kv_slot(kv, min(key0 + 16 * kb + 4 * lq + r, kend - 1));
+          ksr[4 * kb + r] = cp.ks[slot];
+          vsr[4 * kb + r] = cp.vs[slot];
+        }
+    }
+    // ---- the V chunk into this wave's LDS slot (fp16; INT8 codes are exact in fp16)
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int e = ln + 64 * i, r = e / (HD / 8), d0 = (e % (HD / 8)) * 8;
+      *reinterpret_cast<half8_t*>(&vw[r * LV + d0]) = to_f16(vr[i]);
+    }
+    // ---- S^T = K Q^T (lane: keys 16kb + 4lq + r of query l16)
+    float sv[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) t = mfma16(to_f16(kr[kb][s]), qf[s], t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 16 * kb + 4 * lq + r;
+        float ks = scale;
+        if constexpr (I8) ks *= h2f((uint16_t)ksr[4 * kb + r]);
+        sv[kb][r] = (key < kend && key <= qpos && key >= kfirst) ? t[r] * ks : -INFINITY;
+      }
+    }
+    // ---- online softmax of the lane's query (its 32 keys are spread over the
+    // lanes n, n+16, n+32, n+48)
+    {
+      float mx = sv[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow, mx);
+      // no visible key so far (a window starting later, or keys beyond the
+      // query): subtract 0, so the weights are exp(-inf) = 0, not NaN
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(sv[kb][r] - mref);
+          ps += pr;
+          sv[kb][r] = pr;
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lrow = lrow * alpha + ps;
+      mrow = mnew;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[b][r] *= alpha;
+    }
+    // ---- O^T += V^T P^T over the chunk's 32 keys (one k-step; P in two fp16
+    // parts, value scales folded in), V^T from this wave's slot
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's V writes land before its reads
+    {
+      half8_t ph, pl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = sv[kb][r];
+          if constexpr (I8) x *= h2f((uint16_t)vsr[4 * kb + r]);
+          const _Float16 hi = (_Float16)x;
+          ph[4 * kb + r] = hi;
+          pl[4 * kb + r] = (_Float16)(x - (float)hi);
+        }
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const _Float16* vp = &vw[(4 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
+        const half8_t vf = lds_read_tr16x8(vp, vp + 16 * LV);
+        oacc[b] = mfma16(vf, ph, oacc[b]);
+        oacc[b] = mfma16(vf, pl, oacc[b]);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next chunk's writes
+  }
+
+  // ---- merge the 4 waves' states in wave order (waves 1..3 through their own
+  // LDS slot), normalise and store query q0 + l16, dims 16b + 4lq .. +3
+  if (wave > 0) {
+    float* dst = reinterpret_cast<float*>(vw) + ln * RW;
+    dst[0] = mrow;
+    dst[1] = lrow;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) *reinterpret_cast<float4_t*>(dst + 4 + 4 * b) = oacc[b];
+  }
+  attn_lds_barrier();
+  if (wave > 0) return;
+  float mw[4], lw[4];
+  mw[0] = mrow;
+  lw[0] = lrow;
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const float* src = reinterpret_cast<const float*>(Vw[w]) + ln * RW;
+    mw[w] = src[0];
+    lw[w] = src[1];
+  }
+  float m = mw[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) m = fmaxf(m, mw[w]);
+  const float mref = m == -INFINITY ? 0.f : m;
+  float a[4], den = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    a[w] = __builtin_amdgcn_exp2f(mw[w] - mref);
+    den += lw[w] * a[w];
+  }
+  const float inv = 1.0f / den;
+  const int qr = q0 + l16;
+  if (qr >= M) return;
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    float4_t acc = oacc[b] * a[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      acc += *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(Vw[w]) + ln * RW + 4 + 4 * b) * a[w];
+    uint2 wv;
+    wv.x = (uint32_t)f2h(acc[0] * inv) | ((uint32_t)f2h(acc[1] * inv) << 16);
+    wv.y = (uint32_t)f2h(acc[2] * inv) | ((uint32_t)f2h(acc[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(o + (size_t)qr * d + h * HD + b * 16 + 4 * lq) = wv;
+  }
+}
+
 hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const KvGeom& kv, int layer,
                                uint16_t* o, hipStream_t s) {
+  // short calls over a short visible span (each wave walks at most 2 chunks;
+  // a long context reached by a short call is better served by the tiled
+  // kernel, which requests the next key tile during the current one)
+  if (M <= kShortMaxM && p0 + M - kv_first(kv, p0) <= 8 * kShortChunk) {
+    const dim3 g((M + kShortQ - 1) / kShortQ, kv.H);
+    if (kv.hd == 128 && kv.int8)
+      launch(attn_prefill_short_kernel<128, true>, g, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    else if (kv.hd == 128)
+      launch(attn_prefill_short_kernel<128, false>, g, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    else if (kv.hd == 64 && kv.int8)
+      launch(attn_prefill_short_kernel<64, true>, g, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    else if (kv.hd == 64)
+      launch(attn_prefill_short_kernel<64, false>, g, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   dim3 grid((M + 63) / 64, kv.H);
   if (kv.hd == 128 && kv.int8)
     launch(attn_prefill_kernel<128, true>, grid, dim3(kAttnThreads), 0, s, q, M, lane, p0, kv, layer, o);

@@ -425,9 +425,24 @@ def pmc_kernels(tl, torch):
     torch.cuda.synchronize()
 
 
-def summarize_pmc(dirs):
+def _kernel_name(full):
+    """Kernel name without its argument list (and without an anonymous
+    namespace's parenthesised prefix)."""
+    full = full.replace("(anonymous namespace)::", "")
+    return full.split("(")[0]
+
+
+def _dims(r, field):
+    """Total threads of a grid or workgroup from per-axis (or total) CSV columns."""
+    if field + "_X" in r:
+        return int(r[field + "_X"]) * int(r.get(field + "_Y") or 1) * int(r.get(field + "_Z") or 1)
+    return int(r.get(field) or 0)
+
+
+def summarize_pmc(dirs, until=None, since=None):
     """Per kernel (name, grid) averages of every counter found in the given
-    rocprofv3 --pmc output directories (CSV), one line per kernel."""
+    rocprofv3 --pmc output directories (CSV), one line per kernel. `until` and
+    `since` window each run's dispatches as in summarize_trace."""
     import collections
     import csv
     import glob
@@ -435,34 +450,48 @@ def summarize_pmc(dirs):
     for d in dirs:
         for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(fn) as f:
-                for r in csv.DictReader(f):
-                    key = (r["Kernel_Name"].split("(")[0][:60], int(r["Grid_Size"]))
+                rows = list(csv.DictReader(f))
+            mark = until or since
+            if mark:
+                cut = min((int(r["Dispatch_Id"]) for r in rows if mark in r["Kernel_Name"]), default=1 << 62)
+                rows = [r for r in rows if (int(r["Dispatch_Id"]) < cut) == bool(until)]
+            if rows:
+                for r in rows:
+                    key = (_kernel_name(r["Kernel_Name"])[:60], int(r["Grid_Size"]))
                     acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
     names = sorted({c for v in acc.values() for c in v})
-    print("kernel".ljust(62) + "grid".rjust(9) + " n " + "".join(c[:24].rjust(26) for c in names))
+    print("kernel".ljust(62) + "grid".rjust(10) + "    n" + "".join(c[:24].rjust(26) for c in names))
     for (k, grid), v in sorted(acc.items(), key=lambda kv: kv[0]):
         n = max(len(x) for x in v.values())
-        print(k.ljust(62) + str(grid).rjust(9) + f"{n:3d}" +
+        print(k.ljust(62) + str(grid).rjust(10) + f"{n:5d}" +
               "".join((f"{sum(v[c]) / len(v[c]):26.1f}" if v.get(c) else " " * 26) for c in names))
 
 
-def summarize_trace(csv_path):
+def summarize_trace(csv_path, until=None, since=None):
     """Per (kernel, grid) call count and average / median / min duration (us)
-    from a rocprofv3 --kernel-trace CSV, in descending total time."""
+    from a rocprofv3 --kernel-trace CSV, in descending total time. With
+    `until` (`since`), only the dispatches that start before (at or after) the
+    first dispatch whose kernel name contains that text are counted."""
     import collections
     import csv
     import statistics
     d = collections.defaultdict(list)
     meta = {}
     with open(csv_path) as f:
-        for r in csv.DictReader(f):
-            name = r["Kernel_Name"].split("(")[0]
-            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
-            wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 0)) or 0)
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    mark = until or since
+    if mark:
+        cut = next((i for i, r in enumerate(rows) if mark in r["Kernel_Name"]), len(rows))
+        rows = rows[:cut] if until else rows[cut:]
+    if rows:
+        for r in rows:
+            name = _kernel_name(r["Kernel_Name"])
+            grid = _dims(r, "Grid_Size")
+            wg = _dims(r, "Workgroup_Size")
             key = (name, grid)
             d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             meta[key] = (wg, r.get("LDS_Block_Size", r.get("Lds_Size", "")), r.get("VGPR_Count", r.get("Arch_VGPR_Count", "")))
-    tot = sum(sum(v) for v in d.values())
+    tot = sum(sum(v) for v in d.values()) or 1.0
     print(" calls   avg_us   med_us   min_us   %time   blocks   wg  lds_B vgpr  kernel")
     for key, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
         wg, lds, vg = meta[key]
@@ -502,15 +531,21 @@ def main():
                     help="print per-kernel averages of the counters in rocprofv3 --pmc output dirs and exit (no GPU)")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel durations from a rocprofv3 --kernel-trace CSV and exit (no GPU)")
+    ap.add_argument("--trace-until", metavar="NAME",
+                    help="with --summarize-trace/--summarize-pmc: only dispatches before the first one of a "
+                         "kernel whose name contains NAME")
+    ap.add_argument("--trace-since", metavar="NAME",
+                    help="with --summarize-trace/--summarize-pmc: only dispatches from the first one of a "
+                         "kernel whose name contains NAME on")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.trace_until, args.trace_since)
         return
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mib or 256)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+        summarize_pmc(args.summarize_pmc, args.trace_until, args.trace_since)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "

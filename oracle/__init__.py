@@ -22,13 +22,16 @@ Sources (the TinyLoop documentation pages):
     matched VRAM": per-token per-head symmetric INT8 with one FP16 scale;
     section "Key Runtime Switches" (TINYLOOP_DISABLE_KV_CACHE): the uncached
     recompute is the parity reference for cached decode.
+  * "Current Status" page, KV-cache table: store-h (the cache keeps the
+    block's normed input h, FP16 or INT8 per 128-element group, and K, V are
+    rebuilt from it): Cache(store_h=..., h_int8=...), kvquant.h_quantize.
   * Self-speculative decode ("Introduction" page, "What Makes It Different";
     "Current Status" page, speculative decode table): speculative.py.
   * Per-iteration residual-norm safety check ("Current Status" page,
     architecture-unique features table): safety.py.
 """
 from .int4 import pack_int4, unpack_int4, dequantize
-from .kvquant import kv_quantize, kv_dequantize, kv_cache_bytes
+from .kvquant import kv_quantize, kv_dequantize, kv_cache_bytes, h_quantize, h_dequantize, store_h_bytes
 from .model import (OracleModel, Cache, rmsnorm, rope_cos_sin, apply_rope, attention,
                     silu, fp16, forward, decode_step, generate_greedy, forward_uncached,
                     head_logits)
@@ -36,6 +39,6 @@ from .speculative import speculative_greedy
 from .safety import safety_trip
 
 __all__ = ["pack_int4", "unpack_int4", "dequantize", "kv_quantize", "kv_dequantize",
-           "kv_cache_bytes", "OracleModel", "Cache", "rmsnorm", "rope_cos_sin", "apply_rope",
+           "kv_cache_bytes", "h_quantize", "h_dequantize", "store_h_bytes", "OracleModel", "Cache", "rmsnorm", "rope_cos_sin", "apply_rope",
            "attention", "silu", "fp16", "forward", "decode_step", "generate_greedy",
            "forward_uncached", "head_logits", "speculative_greedy", "safety_trip"]

@@ -33,7 +33,7 @@ import math
 import numpy as np
 
 from .int4 import dequantize
-from .kvquant import kv_quantize, kv_dequantize
+from .kvquant import kv_quantize, kv_dequantize, h_quantize, h_dequantize, H_GROUP
 
 _LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
@@ -144,17 +144,22 @@ class Cache:
     depth[t] is the number of effective layers token t was computed through.
     """
 
-    def __init__(self, shape, max_seq, kv_int8=False, window=0, store_h=False):
+    def __init__(self, shape, max_seq, kv_int8=False, window=0, store_h=False, h_int8=False):
         self.shape = shape
         self.max_seq = max_seq
         self.kv_int8 = kv_int8
         self.window = window  # cache_window: > 0 keeps only the last `window` tokens visible
         # store-h: keep the block's normed input h per position instead of K/V
         # and rebuild K, V from it with the block's own W_k, W_v when read
-        self.store_h = store_h
-        if store_h and kv_int8:
-            raise ValueError("store-h keeps FP16 h rows; INT8 K/V does not apply")
+        self.store_h = store_h or h_int8
+        if self.store_h and kv_int8:
+            raise ValueError("store-h keeps h rows; INT8 K/V does not apply")
+        # store-h INT8: h kept as per-128-group INT8 codes and FP16 scales
+        # (kvquant.h_quantize); self.h then holds the rows K and V are rebuilt
+        # from, fp16(q * s)
+        self.h_int8 = h_int8
         self.h = {}
+        self.hq, self.hs = {}, {}
         self.length = 0
         self.k, self.v = {}, {}
         self.kq, self.ks, self.vq, self.vs = {}, {}, {}, {}
@@ -183,6 +188,14 @@ class Cache:
     def write_h(self, layer, pos, h):
         if layer not in self.h:
             self.h[layer] = np.zeros((self.max_seq, self.shape.d_model), dtype=np.float64)
+        if self.h_int8:
+            d = self.shape.d_model
+            if layer not in self.hq:
+                self.hq[layer] = np.zeros((self.max_seq, d), dtype=np.int8)
+                self.hs[layer] = np.zeros((self.max_seq, d // H_GROUP), dtype=np.float16)
+            q, s = h_quantize(np.atleast_2d(h).astype(np.float16))
+            self.hq[layer][pos], self.hs[layer][pos] = q, s
+            h = h_dequantize(q, s)
         self.h[layer][pos] = h
 
 
@@ -205,7 +218,11 @@ def _block_forward(x, B, cache, layer, positions, s, casts, rec=None):
     if cache.store_h:
         # store-h ("Current Status" page, KV-cache table; "Claims & Data
         # Sources": h-mode KV reconstruction from the shared W_k / W_v): the
-        # cache keeps h; K and V of every visible position are rebuilt from it
+        # cache keeps h (FP16, or INT8 codes whose fp16(q * s) it reads back);
+        # K and V of every visible position, the new ones included, are
+        # rebuilt from what the cache holds; Q comes from h itself
+        if cache.h_int8 and not casts:
+            raise ValueError("INT8 store-h quantizes FP16 rows; it needs the FP16 cast points")
         upto = int(positions[-1]) + 1
         cache.write_h(layer, positions, h)
         hall = cache.h[layer][:upto]
@@ -254,7 +271,7 @@ def head_logits(model, x_rows, casts=True, rec=None):
 
 
 def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False,
-            max_seq=None, kv_int8=False, window=0, store_h=False, sites=None):
+            max_seq=None, kv_int8=False, window=0, store_h=False, h_int8=False, sites=None):
     """Append `tokens` to a lane at its current length and run all n_pre + L layers.
 
     Returns a dict with the final residual rows 'hidden' [n][d] (before the
@@ -270,7 +287,8 @@ def forward(model, tokens, L, cache=None, casts=True, logits="last", trace=False
     if L < 1:
         raise ValueError("L must be >= 1")
     if cache is None:
-        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8, window=window, store_h=store_h)
+        cache = Cache(s, max_seq or max(n, 1), kv_int8=kv_int8, window=window, store_h=store_h,
+                      h_int8=h_int8)
     p0 = cache.length
     if p0 + n > cache.max_seq:
         raise ValueError("sequence exceeds max_seq")

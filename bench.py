@@ -511,7 +511,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative decode leg")
-    ap.add_argument("--no-storeh", action="store_true", help="skip the store-h (TL_KV_H16) leg")
+    ap.add_argument("--no-storeh", action="store_true", help="skip the store-h legs (TL_KV_H16, TL_KV_H8)")
     ap.add_argument("--no-fp16body", action="store_true", help="skip the FP16-body leg")
     ap.add_argument("--no-kernels", action="store_true",
                     help="skip the single-kernel leg (cold W4 GEMV and M=1024 GEMM at the loop block's shapes)")
@@ -725,42 +725,47 @@ def main():
             print(f"[bench] spec decode draft L=2 verify L={L} k={kd}: {dt * 1e3 / D:.4f} ms/token, "
                   f"accepted {st.accepted}/{st.drafted}", file=sys.stderr, flush=True)
         # ------------------------------------------------------------ store-h cache
-        # same prompt/steps with h kept per position and K/V rebuilt per layer
+        # same prompt/steps with h kept per position (FP16, or INT8 per
+        # 128-element group) and K/V rebuilt per layer
         if not args.no_storeh:
-            mh = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=tl.TL_KV_H16,
-                       max_tokens=max(SEQ, args.prompt))
-            mh.set_loops(0, L)
-
-            def prefill_h():
-                mh.reset(0)
-                mh.prefill(toks)
-            for _ in range(3):
-                prefill_h()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(10):
-                prefill_h()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms_pre_h = e0.elapsed_time(e1) / 10
-            mh.reset(0)
-            mh.prefill(ptoks, next_tok=bufs[0])
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for t in range(D):
-                mh.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms_tok_h = e0.elapsed_time(e1) / D
             kvb = {k: tl.tl_kv_layer_bytes(mod.make_config(s, 2048, L, kv_dtype=v))
-                   for k, v in (("fp16", tl.TL_KV_FP16), ("h16", tl.TL_KV_H16))}
-            mh.close()
-            out["store_h"] = {"kv_bytes_per_lane_layer": kvb, "kv_saving": round(1 - kvb["h16"] / kvb["fp16"], 3),
-                              "prefill_ms_seq128": round(ms_pre_h, 4), "decode_ms_per_token": round(ms_tok_h, 4),
-                              "note": "prefill bit-identical to FP16 K/V; decode rebuilds K/V of the context every layer"}
-            print(f"[bench] store-h: prefill {ms_pre_h:.3f} ms/step, decode {ms_tok_h:.4f} ms/token, "
-                  f"KV bytes {kvb['h16']} vs {kvb['fp16']}", file=sys.stderr, flush=True)
+                   for k, v in (("fp16", tl.TL_KV_FP16), ("h16", tl.TL_KV_H16), ("h8", tl.TL_KV_H8))}
+            out["store_h"] = {"kv_bytes_per_lane_layer": kvb,
+                              "note": "h16 prefill bit-identical to FP16 K/V; decode rebuilds K/V of the "
+                                      "context every layer (h8: from fp16(q*s) of the INT8 rows)"}
+            for name, kvd in (("h16", tl.TL_KV_H16), ("h8", tl.TL_KV_H8)):
+                mh = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=kvd,
+                           max_tokens=max(SEQ, args.prompt))
+                mh.set_loops(0, L)
+
+                def prefill_h():
+                    mh.reset(0)
+                    mh.prefill(toks)
+                for _ in range(3):
+                    prefill_h()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(10):
+                    prefill_h()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms_pre_h = e0.elapsed_time(e1) / 10
+                mh.reset(0)
+                mh.prefill(ptoks, next_tok=bufs[0])
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for t in range(D):
+                    mh.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms_tok_h = e0.elapsed_time(e1) / D
+                mh.close()
+                out["store_h"][name] = {"kv_saving": round(1 - kvb[name] / kvb["fp16"], 3),
+                                        "prefill_ms_seq128": round(ms_pre_h, 4),
+                                        "decode_ms_per_token": round(ms_tok_h, 4)}
+                print(f"[bench] store-h {name}: prefill {ms_pre_h:.3f} ms/step, decode {ms_tok_h:.4f} ms/token, "
+                      f"KV bytes {kvb[name]} vs {kvb['fp16']}", file=sys.stderr, flush=True)
 
         # ------------------------------------------------------------ FP16 body
         # the same steps with the block weights dequantized once to fp16

@@ -64,7 +64,15 @@ typedef enum {
  * GEMM arithmetic produces K and V either way); decode differs from it only
  * in rounding (its stored K/V rows come from the decode GEMV there). Not
  * combinable with cache_window. */
-typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1, TL_KV_H16 = 2 } tl_kv_dtype;
+/* TL_KV_H8 (store-h INT8, the same table's Store-h INT8 row: 66-75% less
+ * memory than FP16 K/V): as TL_KV_H16, but each 128-element group of an h
+ * row is kept as INT8 codes with one fp16 scale, quantized with the INT8 K/V
+ * rule (scale fp16(amax / 127), codes rint(x / scale) clamped to +-127), and
+ * K, V of every visible position, the call's new rows included, are rebuilt
+ * from fp16(code * scale); Q comes from h itself. 74.6% less than FP16 K/V at
+ * d_model = 2048. Needs d_model % 128 == 0; not combinable with
+ * cache_window. */
+typedef enum { TL_KV_FP16 = 0, TL_KV_INT8 = 1, TL_KV_H16 = 2, TL_KV_H8 = 3 } tl_kv_dtype;
 
 /* Model shape and runtime limits. */
 typedef struct {
@@ -136,6 +144,9 @@ size_t tl_weights_ws_bytes(const tl_config* cfg);
  *         and head, "Performance and Memory" page, INT8-KV; equal to
  *         2 * R * n_heads * (head_dim + 2) when R * n_heads % 128 == 0).
  *   H16:  max_seq * d_model * 2               (h rows [max_seq][d_model]).
+ *   H8:   A(max_seq * d_model) + A(max_seq * d_model / 128 * 2): codes int8
+ *         [max_seq][d_model] at offset 0, then the fp16 scale of each
+ *         128-element group [max_seq][d_model / 128].
  * Layout per layer: K then V planes [n_heads][R][head_dim]; INT8: K codes
  * int8 [n_heads][R][head_dim] at offset 0, K scales fp16 [n_heads][R] at
  * A(codes), V codes at A(codes) + A(scales), V scales after them, every

@@ -21,7 +21,7 @@ __all__ = [
     "TLError", "TlConfig", "TlQLinear", "TlBlock", "TlWeights", "lib", "LIB_PATH",
     "TL_OK", "TL_E_INVAL", "TL_E_RANGE", "TL_E_STATE", "TL_E_HIP", "TL_E_UNSUPPORTED", "TL_E_SAFETY",
     "tl_set_safety", "tl_safety_last",
-    "TL_KV_FP16", "TL_KV_INT8", "TL_KV_H16",
+    "TL_KV_FP16", "TL_KV_INT8", "TL_KV_H16", "TL_KV_H8",
     "tl_weights_ws_bytes", "tl_kv_layer_bytes", "tl_kv_bytes", "tl_act_ws_bytes", "tl_create",
     "tl_destroy", "tl_set_loops", "tl_get_loops", "tl_reset", "tl_length", "tl_prefill", "tl_set_graphs", "tl_spec_decode", "TlSpecStats",
     "tl_decode_step", "tl_last_error", "tl_qlinear_packed_bytes", "tl_qlinear_pack",
@@ -50,7 +50,7 @@ if len(_hip_runtimes()) > 1:
                       + ", ".join(_hip_runtimes()))
 
 TL_OK, TL_E_INVAL, TL_E_RANGE, TL_E_STATE, TL_E_HIP, TL_E_UNSUPPORTED, TL_E_SAFETY = range(7)
-TL_KV_FP16, TL_KV_INT8, TL_KV_H16 = 0, 1, 2
+TL_KV_FP16, TL_KV_INT8, TL_KV_H16, TL_KV_H8 = 0, 1, 2, 3
 
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 

@@ -587,6 +587,77 @@ hipError_t launch_store_h(const uint16_t* h, int M, int d, const RowMap& rm, uin
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ INT8 store-h rows
+// One wave per 128-element group of an h row ("Current Status" page, KV-cache
+// table: Store-h INT8): amax over the group (fp32, exact), scale fp16(amax /
+// 127) and codes clamp(rint(x / s), -127, 127), the same decisions as the
+// INT8 K/V quantizer per (token, head) (kv_scale, kv_code); lane l holds
+// elements 2l and 2l + 1 of the group.
+__global__ __launch_bounds__(256) void store_h8_kernel(const uint16_t* __restrict__ h, int d, int G, RowMap rm,
+                                                       uint8_t* __restrict__ base, size_t hs_off,
+                                                       size_t layer_bytes, int n_layers, int layer,
+                                                       uint16_t* __restrict__ hhat) {
+  const int m = blockIdx.x, g = blockIdx.y * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (g >= G) return;
+  const uint32_t two = *reinterpret_cast<const uint32_t*>(h + (size_t)m * d + g * 128 + 2 * l);
+  const float x0 = h2f((uint16_t)(two & 0xffffu)), x1 = h2f((uint16_t)(two >> 16));
+  float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const _Float16 sc = kv_scale(amax);
+  const float sf = (float)sc;
+  const int q0 = kv_code(x0, sf), q1 = kv_code(x1, sf);
+  const int pos = row_pos(rm, m);
+  uint8_t* lb = base + ((size_t)row_lane(rm, m) * n_layers + layer) * layer_bytes;
+  *reinterpret_cast<uint16_t*>(lb + (size_t)pos * d + g * 128 + 2 * l) =
+      (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
+  if (l == 0) *reinterpret_cast<_Float16*>(lb + hs_off + ((size_t)pos * G + g) * 2) = sc;
+  if (hhat) {
+    const _Float16 y0 = (_Float16)((float)q0 * sf), y1 = (_Float16)((float)q1 * sf);
+    *reinterpret_cast<uint32_t*>(hhat + (size_t)m * d + g * 128 + 2 * l) =
+        (uint32_t)__builtin_bit_cast(uint16_t, y0) | ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
+  }
+}
+
+hipError_t launch_store_h8(const uint16_t* h, int M, int d, int S, const RowMap& rm, uint8_t* base,
+                           size_t layer_bytes, int n_layers, int layer, uint16_t* hhat, hipStream_t s) {
+  if (d % 128 || M < 1) return hipErrorInvalidValue;
+  const int G = d / 128;
+  launch(store_h8_kernel, dim3(M, (G + 3) / 4), dim3(256), 0, s, h, d, G, rm, base, h8_planes(S, d).hs,
+         layer_bytes, n_layers, layer, hhat);
+  return hipGetLastError();
+}
+
+// fp16(q * s) of rows 0 .. rows-1: 8 consecutive elements (one group's) per thread.
+__global__ __launch_bounds__(256) void dequant_h8_kernel(const uint8_t* __restrict__ lb, size_t hs_off, int rows,
+                                                         int d, uint16_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // index of an 8-element run
+  if (i >= (size_t)rows * d / 8) return;
+  const size_t e0 = i * 8;
+  const size_t r = e0 / d, c = e0 - r * d;
+  const float sf = (float)*reinterpret_cast<const _Float16*>(lb + hs_off + (r * (d / 128) + c / 128) * 2);
+  const uint2 q8 = *reinterpret_cast<const uint2*>(lb + e0);
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t src = k < 2 ? q8.x : q8.y;
+    const int sh = (k & 1) * 16;
+    const int qa = (int)(int8_t)((src >> sh) & 0xff), qb = (int)(int8_t)((src >> (sh + 8)) & 0xff);
+    const _Float16 ya = (_Float16)((float)qa * sf), yb = (_Float16)((float)qb * sf);
+    w[k] = (uint32_t)__builtin_bit_cast(uint16_t, ya) | ((uint32_t)__builtin_bit_cast(uint16_t, yb) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+hipError_t launch_dequant_h8(const uint8_t* layer_base, int rows, int d, int S, uint16_t* out, hipStream_t s) {
+  if (d % 128 || rows < 0 || rows > S) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  const size_t runs = (size_t)rows * d / 8;
+  launch(dequant_h8_kernel, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, s, layer_base, h8_planes(S, d).hs,
+         rows, d, out);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ safety check
 // Residual L2 norm of each row (x plus any pending split partials, x itself
 // untouched); a row whose norm is not <= max_norm (NaN included) records

@@ -56,8 +56,11 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->d_model > 2048) return *why = "d_model must be <= 2048 (one residual row per 256 threads in registers)", false;
   if (c->group_size != 128) return *why = "group_size must be 128", false;
   if (c->vocab < 1 || c->n_pre < 0) return *why = "vocab < 1 or n_pre < 0", false;
-  if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8 && c->kv_dtype != TL_KV_H16)
+  if (c->kv_dtype != TL_KV_FP16 && c->kv_dtype != TL_KV_INT8 && c->kv_dtype != TL_KV_H16 &&
+      c->kv_dtype != TL_KV_H8)
     return *why = "bad kv_dtype", false;
+  if (c->kv_dtype == TL_KV_H8 && c->d_model % 128)
+    return *why = "store-h INT8 (TL_KV_H8) needs d_model % 128 == 0 (128-element groups)", false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return *why = "bad rms_eps or rope_base", false;
   *st = TL_E_RANGE;
   if (c->max_loops < 1 || c->max_loops > 64) return *why = "max_loops must be in 1..64", false;
@@ -65,9 +68,9 @@ bool check_cfg(const tl_config* c, tl_status* st, std::string* why) {
   if (c->max_seq < 1 || c->max_tokens < 1) return *why = "max_seq and max_tokens must be >= 1", false;
   if (c->cache_window < 0) return *why = "cache_window must be >= 0", false;
   if (c->fp16_body != 0 && c->fp16_body != 1) return *why = "fp16_body must be 0 or 1", false;
-  if (c->kv_dtype == TL_KV_H16 && c->cache_window > 0) {
+  if ((c->kv_dtype == TL_KV_H16 || c->kv_dtype == TL_KV_H8) && c->cache_window > 0) {
     *st = TL_E_UNSUPPORTED;
-    return *why = "store-h (TL_KV_H16) does not combine with cache_window", false;
+    return *why = "store-h (TL_KV_H16, TL_KV_H8) does not combine with cache_window", false;
   }
   *st = TL_OK;
   return true;
@@ -115,7 +118,7 @@ constexpr int kSpecMaxDraft = 7;
 int head_rows_cap(const tl_config* c) { return std::max(c->n_lanes, kSpecMaxDraft + 1); }
 
 struct ActLayout {
-  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, dpos, hkv, total;
+  size_t x, h, qkv, q, o, a, part, logits, gpart, hscr, spec, safety, dpos, hkv, hdq, total;
 };
 ActLayout act_layout(const tl_config* c) {
   const size_t T = (size_t)tokens_cap(c), d = c->d_model, f = c->ffn_dim;
@@ -137,8 +140,12 @@ ActLayout act_layout(const tl_config* c) {
   L.safety = off; off += al256(4);  // first tripped (iteration, row) code of the safety check
   L.dpos = off; off += al256(8 * 4);  // lane positions read by graph-replayed decode steps
   // store-h: K/V rebuilt for one layer, FP16 [lane][K|V][H][max_seq][hd]
+  const bool hmode = c->kv_dtype == TL_KV_H16 || c->kv_dtype == TL_KV_H8;
   L.hkv = off;
-  if (c->kv_dtype == TL_KV_H16) off += al256((size_t)c->n_lanes * 2 * c->max_seq * c->d_model * 2);
+  if (hmode) off += al256((size_t)c->n_lanes * 2 * c->max_seq * c->d_model * 2);
+  // store-h INT8: fp16(q * s) rows of one lane's h cache for the rebuild, FP16 [max_seq][d]
+  L.hdq = off;
+  if (c->kv_dtype == TL_KV_H8) off += al256((size_t)c->max_seq * c->d_model * 2);
   L.total = off;
   return L;
 }
@@ -169,8 +176,12 @@ struct tl_ctx {
   int32_t* spec_chain;  // [kSpecMaxDraft + 2][n_lanes]
   int32_t* spec_ver;    // [kSpecMaxDraft + 1]
   int32_t* spec_next;   // [kSpecMaxDraft + 1]
-  // store-h: h cache [lane][layer][max_seq][d] (in d_kv); kv then describes the scratch
+  // store-h: h cache [lane][layer][max_seq][d] (in d_kv); kv then describes the scratch.
+  // h8: the cache holds INT8 codes and per-128-group fp16 scales (tl::h8_planes)
+  // and hdq the fp16(q * s) rows a rebuild reads
   bool hmode = false;
+  bool h8 = false;
+  uint16_t* hdq = nullptr;
   uint8_t* hc_base = nullptr;
   size_t hc_layer_bytes = 0;
   int hc_layers = 0;
@@ -298,11 +309,13 @@ tl_status linear(tl_ctx* c, int kind, const tl::Packed& w, const tl::ASrc& src, 
 
 // One effective layer over M rows (prefill rows of one lane, or the first M
 // decode rows).
-// Store-h attention input of one layer (TL_KV_H16; "Current Status" page,
-// KV-cache table: Store-h; "Claims & Data Sources": h-mode KV reconstruction
-// from the shared W_k / W_v):
+// Store-h attention input of one layer (TL_KV_H16, TL_KV_H8; "Current
+// Status" page, KV-cache table: Store-h FP16 and INT8; "Claims & Data
+// Sources": h-mode KV reconstruction from the shared W_k / W_v):
 //   1. h = fp16(RMSNorm(x)) (pending split partials summed), each row also
-//      stored at its position in its lane's h cache for this layer;
+//      stored at its position in its lane's h cache for this layer (H8: as
+//      INT8 codes with one fp16 scale per 128-element group, and K, V are
+//      rebuilt from fp16(q * s), the new rows' included);
 //   2. prefill: Q = fp16(RoPE(h W_q^T)) by the Q section of the packed QKV
 //      (GEMM, RoPE epilogue); decode: q, k, v of the new rows (GEMV) for the
 //      decode attention, which rotates them itself;
@@ -319,7 +332,11 @@ tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   }
   {
     KScope k(c, TL_K_COPY, s);
-    TL_HIP(tl::launch_store_h(c->h, M, d, rm, c->hc_base, c->hc_layer_bytes, c->hc_layers, layer, s));
+    if (c->h8)  // decode: the new rows' fp16(q * s) also go to hdq for their K/V
+      TL_HIP(tl::launch_store_h8(c->h, M, d, c->cfg.max_seq, rm, c->hc_base, c->hc_layer_bytes, c->hc_layers, layer,
+                                 decode ? c->hdq : nullptr, s));
+    else
+      TL_HIP(tl::launch_store_h(c->h, M, d, rm, c->hc_base, c->hc_layer_bytes, c->hc_layers, layer, s));
   }
   const int nbd = d / 16;  // n-blocks per section
   const size_t tb = B.qkv.f16 ? 4096 : 1024;  // tile bytes
@@ -333,7 +350,17 @@ tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
   er.qout = c->q;
   er.kv = c->kv;
   er.layer = 0;
-  if (decode) {
+  if (decode && c->h8) {
+    // q from h; k, v of the new rows from the fp16(q * s) rows the cache will
+    // give back, as for every cached position
+    tl::Epi eq{tl::EPI_STORE, c->qkv, nullptr, 3 * d};
+    eq.perm_hd = hd;
+    tl::Epi ekv{tl::EPI_STORE, c->qkv + d, nullptr, 3 * d};
+    ekv.perm_hd = hd;
+    KScope k(c, TL_K_QKV, s);
+    TL_HIP(tl::launch_w4_gemv(qsec, tl::ASrc{c->h, nullptr, nullptr, 0.f}, M, eq, s));
+    TL_HIP(tl::launch_w4_gemv(kvsec, tl::ASrc{c->hdq, nullptr, nullptr, 0.f}, M, ekv, s));
+  } else if (decode) {
     tl::Epi eq{tl::EPI_STORE, c->qkv, nullptr, 3 * d};
     eq.perm_hd = hd;
     KScope k(c, TL_K_QKV, s);
@@ -353,8 +380,13 @@ tl_status hmode_qkv(tl_ctx* c, const BlockW& B, int layer, int M, const tl::RowM
     const int end = decode ? rm.row_pos[m] : rm.p0 + M;
     if (end < 1) continue;
     er.lane = lane;
-    const uint16_t* hrows =
-        reinterpret_cast<const uint16_t*>(c->hc_base + ((size_t)lane * c->hc_layers + layer) * c->hc_layer_bytes);
+    const uint8_t* lb = c->hc_base + ((size_t)lane * c->hc_layers + layer) * c->hc_layer_bytes;
+    const uint16_t* hrows = reinterpret_cast<const uint16_t*>(lb);
+    if (c->h8) {
+      KScope k(c, TL_K_COPY, s);
+      TL_HIP(tl::launch_dequant_h8(lb, end, d, c->cfg.max_seq, c->hdq, s));
+      hrows = c->hdq;
+    }
     KScope k(c, TL_K_ROPE_KV, s);
     TL_HIP(tl::launch_w4_gemm(kvsec, hrows, end, er, c->gpart, s));
   }
@@ -488,6 +520,7 @@ size_t tl_kv_layer_bytes(const tl_config* cfg) {
   const size_t rows = (size_t)kv_rows(cfg) * cfg->n_heads;
   if (cfg->kv_dtype == TL_KV_INT8) return tl::int8_planes(cfg->n_heads, kv_rows(cfg), cfg->head_dim).bytes;
   if (cfg->kv_dtype == TL_KV_H16) return (size_t)cfg->max_seq * cfg->d_model * 2;
+  if (cfg->kv_dtype == TL_KV_H8) return tl::h8_planes(cfg->max_seq, cfg->d_model).bytes;
   return 2 * rows * cfg->head_dim * 2;
 }
 
@@ -606,7 +639,8 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
       return fail(TL_E_HIP, std::string("rope table upload: ") + hipGetErrorString(e));
     }
   }
-  c->hmode = cfg->kv_dtype == TL_KV_H16;
+  c->hmode = cfg->kv_dtype == TL_KV_H16 || cfg->kv_dtype == TL_KV_H8;
+  c->h8 = cfg->kv_dtype == TL_KV_H8;
   c->kv.base = static_cast<uint8_t*>(d_kv);
   c->kv.layer_bytes = tl_kv_layer_bytes(cfg);
   c->kv.n_layers = cfg->n_pre + cfg->max_loops;
@@ -636,6 +670,7 @@ tl_status tl_create(const tl_config* cfg, const tl_weights* w, void* d_weights_w
   c->logits = reinterpret_cast<float*>(ab + L.logits);
   c->gpart = reinterpret_cast<float*>(ab + L.gpart);
   c->hscr = ab + L.hscr;
+  c->hdq = c->h8 ? reinterpret_cast<uint16_t*>(ab + L.hdq) : nullptr;
   c->spec_chain = reinterpret_cast<int32_t*>(ab + L.spec);
   c->spec_ver = c->spec_chain + (size_t)(kSpecMaxDraft + 2) * cfg->n_lanes;
   c->spec_next = c->spec_ver + (kSpecMaxDraft + 1);

@@ -91,6 +91,19 @@ __host__ __device__ inline Int8Planes int8_planes(int H, int cap, int hd) {
   return p;
 }
 
+// One layer of an INT8 store-h cache (TL_KV_H8): codes int8 [S][d] at 0, then
+// the fp16 scale of each 128-element group, [S][d / 128], both planes
+// 256-byte aligned.
+struct H8Planes {
+  size_t hs, bytes;
+};
+__host__ __device__ inline H8Planes h8_planes(int S, int d) {
+  H8Planes p;
+  p.hs = kv_al256((size_t)S * d);
+  p.bytes = p.hs + kv_al256((size_t)S * (d / 128) * 2);
+  return p;
+}
+
 // Cache row of position pos (a ring when windowed) and the first position
 // a query at pos sees.
 __host__ __device__ inline int kv_slot(const KvGeom& kv, int pos) { return kv.window ? pos % kv.cap : pos; }
@@ -253,6 +266,13 @@ hipError_t launch_scatter_rows(const float* src, int M, int d, const RowMap& rm,
 // lane and position.
 hipError_t launch_store_h(const uint16_t* h, int M, int d, const RowMap& rm, uint8_t* base, size_t layer_bytes,
                           int n_layers, int layer, hipStream_t s);
+// INT8 store-h rows: h row m (fp16 [d]) -> codes and per-128-group scales at
+// its position in its lane's cache layer (h8_planes with S = max_seq); with
+// hhat, fp16(q * s) of the row is also written to hhat[m][d].
+hipError_t launch_store_h8(const uint16_t* h, int M, int d, int S, const RowMap& rm, uint8_t* base,
+                           size_t layer_bytes, int n_layers, int layer, uint16_t* hhat, hipStream_t s);
+// fp16(q * s) of positions 0 .. rows-1 of one INT8 store-h cache layer -> out [rows][d].
+hipError_t launch_dequant_h8(const uint8_t* layer_base, int rows, int d, int S, uint16_t* out, hipStream_t s);
 
 // Per-iteration residual-norm check: result = min(result, code_base + m) for
 // each row m of x (+ pending partials) whose L2 norm is not <= max_norm.

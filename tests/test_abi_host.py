@@ -66,7 +66,8 @@ def test_packed_bytes():
 
 def test_bad_configs_are_rejected_without_a_gpu():
     bad = [dict(head_dim=96), dict(d_model=1000), dict(max_loops=0), dict(max_loops=65),
-           dict(n_lanes=9), dict(group_size=64), dict(kv_dtype=3), dict(max_seq=0)]
+           dict(n_lanes=9), dict(group_size=64), dict(kv_dtype=4), dict(max_seq=0),
+           dict(kv_dtype=3, n_heads=3, head_dim=64, d_model=192)]
     for kw in bad:
         c = _cfg()
         for k, v in kw.items():
@@ -118,3 +119,24 @@ def test_store_h_halves_kv_memory():
     h16 = tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H16))
     assert 2 * h16 == fp16 and h16 == 2048 * 2048 * 2
     assert tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H16, cache_window=64)) == 0
+
+
+def test_store_h_int8_layer_bytes():
+    """TL_KV_H8 keeps d_model codes and d_model / 128 fp16 scales per position,
+    each plane 256-byte aligned ("Current Status" page, KV-cache table: Store-h
+    INT8, 66-75% less than FP16 K/V); needs 128-element groups; no window."""
+    import oracle
+    import synth
+    from looped_weight_shared_amd.model import make_config
+    s = synth.SHAPES["m407"]
+    fp16 = tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_FP16))
+    h8 = tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H8))
+    assert h8 == 2048 * 2048 + 2048 * 16 * 2
+    assert h8 * 10 == oracle.store_h_bytes(10, 2048, 2048, True)
+    assert 0.66 <= 1 - h8 / fp16 <= 0.75
+    odd = make_config(s, 100, 8, kv_dtype=tl.TL_KV_H8)
+    assert tl.tl_kv_layer_bytes(odd) == -(-100 * 2048 // 256) * 256 + -(-100 * 16 * 2 // 256) * 256
+    assert tl.tl_kv_layer_bytes(make_config(s, 2048, 8, kv_dtype=tl.TL_KV_H8, cache_window=64)) == 0
+    t = synth.SHAPES["tiny"]
+    if t.d_model % 128:
+        assert tl.tl_kv_layer_bytes(make_config(t, 64, 2, kv_dtype=tl.TL_KV_H8)) == 0

@@ -18,8 +18,17 @@ Also reported (same JSON line):
               (M = 1024) alone, at the loop block's four linear shapes.
   cpu_baseline -- the CPU oracle timed on this host on a bounded sample of
               the same prefill step (reported, not a target).
+  decode graph replay, host enqueue time, self-speculative decode, store-h
+              (FP16 and INT8 h), the FP16-body comparator, the empty-kernel
+              dispatch floor, and the other 407M workloads (prefill seq 1024
+              at L = 16 / 32; INT8-KV decode at context 2048, one lane and
+              three lanes at L = 4 / 16 / 32), each skippable (--no-*).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Profiling helpers (no timed step): --pmc-kernels (single-kernel launches for
+counter runs), --summarize-trace CSV / --summarize-pmc DIR... (per-kernel
+tables, windowed with --trace-until / --trace-since), --ingest-pmc FETCH WRITE
+(writes profiles/traffic.json), --cpu-configs (oracle on the other workloads).
 """
 from __future__ import annotations
 

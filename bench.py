@@ -79,6 +79,12 @@ def _traffic(kernel_key, src_files, launches_bytes_expected=None):
     return ent.get("bytes_per_launch")
 
 
+def _traffic_sum(keys):
+    """Sum of the counters' bytes per launch over several kernels (None unless all are current)."""
+    v = [_traffic(k, ["w4mm.hip", "tl_device.h"]) for k in keys]
+    return None if any(x is None for x in v) else sum(v)
+
+
 def _pmc_dispatches(d, counter):
     """(kernel name, grid size, value) per dispatch from a rocprofv3 --pmc CSV directory."""
     import csv
@@ -92,14 +98,64 @@ def _pmc_dispatches(d, counter):
     return out
 
 
-def ingest_pmc(fetch_dir, write_dir, copy_mib):
+def ingest_pmc(fetch_dir, write_dir, copy_mib, kfetch_dir=None, kwrite_dir=None):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --decode-steps 4 --copy-mib <copy_mib>`, one with
-    FETCH_SIZE, one with WRITE_SIZE (KiB per dispatch). Each counter is scaled by what it reads
-    for the plain device copy of copy_mib MiB in the same run (copy_mib MiB read and written)."""
+    `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --no-configs
+    --decode-steps 4 --copy-mib <copy_mib>`, one with FETCH_SIZE, one with WRITE_SIZE (KiB per
+    dispatch), and optionally two of `bench.py --pmc-kernels` (the cold M = 1 GEMVs). Each counter
+    is scaled by what it reads for the plain device copy of copy_mib MiB in the same run."""
+    copy_bytes = copy_mib * 2**20
+    data = _ingest_runs(fetch_dir, write_dir, copy_bytes, _forward_kernels())
+    run = ("bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --no-configs "
+           "--decode-steps 4 --copy-mib %d" % copy_mib)
+    cmds = ["export TMPDIR=/tmp; timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -d %s -o run -f csv -- python -u %s"
+            % (fetch_dir, run),
+            "export TMPDIR=/tmp; timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -d %s -o run -f csv -- python -u %s"
+            % (write_dir, run)]
+    ing = "python bench.py --ingest-pmc %s %s --copy-mib %d" % (fetch_dir, write_dir, copy_mib)
+    if kfetch_dir and kwrite_dir:
+        data.update(_ingest_runs(kfetch_dir, kwrite_dir, 256 * 2**20, _cold_gemv_kernels()))
+        cmds += ["export TMPDIR=/tmp; timeout -s KILL 150 rocprofv3 --pmc %s -d %s -o run -f csv -- python -u "
+                 "bench.py --pmc-kernels" % (c, d) for c, d in (("FETCH_SIZE", kfetch_dir), ("WRITE_SIZE", kwrite_dir))]
+        ing += " --ingest-pmc-kernels %s %s" % (kfetch_dir, kwrite_dir)
+    out = {"commands": cmds + [ing],
+           "note": "per-dispatch KiB counters x 1024 x (copy bytes / the counter's reading for the plain device copy "
+                   "of the same run); bytes_per_launch = scaled FETCH_SIZE + scaled WRITE_SIZE, averaged over the "
+                   "kernel's dispatches"}
+    out.update(data)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fo:
+        json.dump(out, fo, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def _forward_kernels():
+    d, f = 2048, 5632
+    return {
+        # dominant prefill kernel: the gate/up GEMM at M=128, 32x128 tiles: 88 column blocks x 4
+        # row tiles = 352 blocks of 256 threads (the 256-token prompt's instance has 704)
+        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2, false, 2>" in n and g == 352 * 256,
+                         tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
+        # decode gate/up GEMV: the only two-n-block GEMV (fused RMSNorm, one row)
+        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1, false>" in n,
+                         tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
+    }
+
+
+def _cold_gemv_kernels():
+    """The M = 1 GEMVs of `bench.py --pmc-kernels` (fp16 A row in, fp32 C row out), one entry per
+    loop-block linear, told apart by template and grid (512 threads, N / 16 blocks)."""
+    out = {}
+    for name, (N, K) in PMC_SHAPES.items():
+        tmpl = "w4_gemv_kernel<1, 0, 1, 8, 2, false>" if K > 2048 else "w4_gemv_kernel<1, 0, 1, 2, 1, false>"
+        out["gemv_cold_" + name] = ((lambda t, g0: (lambda n, g: t in n and g == g0))(tmpl, (N // 16) * 512),
+                                    tl_packed_bytes(N, K) + K * 2 + N * 4)
+    return out
+
+
+def _ingest_runs(fetch_dir, write_dir, copy_bytes, kernels):
     fetch = _pmc_dispatches(fetch_dir, "FETCH_SIZE")
     write = _pmc_dispatches(write_dir, "WRITE_SIZE")
-    copy_bytes = copy_mib * 2**20
 
     def pick(rows, pred):
         v = [x[2] * 1024 for x in rows if pred(x[0], x[1])]
@@ -112,24 +168,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
     if not cf or not cw:
         raise SystemExit("no copy-kernel dispatch found in the counter runs")
     kf, kw = copy_bytes / cf, copy_bytes / cw
-    d, f = 2048, 5632
-    kernels = {
-        # dominant prefill kernel: the gate/up GEMM at M=128, 32x128 tiles: 88 column blocks x 4
-        # row tiles = 352 blocks of 256 threads (the 256-token prompt's instance has 704)
-        "gemm_gate_up": (lambda n, g: "w4_gemm_kernel<2, 2, false, 2>" in n and g == 352 * 256,
-                         tl_packed_bytes(2 * f, d) + 128 * d * 2 + 128 * f * 2),
-        # decode gate/up GEMV: the only two-n-block GEMV (fused RMSNorm, one row)
-        "gemv_gate_up": (lambda n, g: "w4_gemv_kernel<2, 1, 1, 2, 1, false>" in n,
-                         tl_packed_bytes(2 * f, d) + d * 4 + f * 2),
-    }
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    run = "bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --decode-steps 4 --copy-mib %d" % copy_mib
-    data = {"commands": [
-        "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -f csv -- python -u " + run,
-        "export TMPDIR=/tmp; timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -f csv -- python -u " + run,
-        "python bench.py --ingest-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write --copy-mib %d" % copy_mib],
-        "note": "per-dispatch KiB counters x 1024 x (copy bytes / the counter's reading for the plain device copy); "
-                "bytes_per_launch = scaled FETCH_SIZE + scaled WRITE_SIZE, averaged over the kernel's dispatches"}
+    data = {}
     for key, (pred, algo) in kernels.items():
         fb, nf = pick(fetch, pred)
         wb, nw = pick(write, pred)
@@ -141,9 +180,7 @@ def ingest_pmc(fetch_dir, write_dir, copy_mib):
                      "algorithmic_bytes_per_launch": algo, "dispatches": [nf, nw],
                      "copy_calibration": {"bytes": copy_bytes, "fetch_factor": round(kf, 4),
                                           "write_factor": round(kw, 4)}}
-    with open(path, "w") as fo:
-        json.dump(data, fo, indent=1)
-    print(json.dumps(data, indent=1))
+    return data
 
 
 def tl_packed_bytes(N, K):
@@ -533,6 +570,8 @@ def main():
                     help="finish with one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--ingest-pmc-kernels", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="with --ingest-pmc: also the cold M = 1 GEMVs from two --pmc-kernels counter runs")
     ap.add_argument("--pmc-kernels", action="store_true",
                     help="only launch the single kernels for counter runs (GEMM M=1024, cold GEMV M=1, empty "
                          "kernels) and exit")
@@ -551,7 +590,8 @@ def main():
         summarize_trace(args.summarize_trace, args.trace_until, args.trace_since)
         return
     if args.ingest_pmc:
-        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mib or 256)
+        kp = args.ingest_pmc_kernels or (None, None)
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.copy_mib or 256, kp[0], kp[1])
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.trace_until, args.trace_since)
@@ -851,7 +891,7 @@ def main():
             agg = byts / us / 1e3
             out["roofline_decode"] = {
                 "bound": "hbm", "achieved": round(agg, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(agg / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(agg / PEAK_HBM_GBS, 4), "traffic": _traffic_sum(["gemv_cold_" + k for k in kl]),
                 "kernel": "w4_gemv_kernel, M=1, cold weights: QKV + O + gate/up + down of the loop block "
                           "(bytes summed over summed launch times)",
                 "bytes_per_launch": {k: kl[k]["gemv_m1"]["algorithmic_bytes"] for k in kl},

@@ -1302,7 +1302,7 @@ tl_status tl_qlinear_unpack(const void* d_packed, int32_t N, int32_t K, int8_t* 
 
 size_t tl_w4_linear_ws_bytes(int32_t N, int32_t K, int32_t M) {
   if (N < 16 || N % 16 || K < 8 || K % 8 || M < 1) return 0;
-  return al256(tl::w4_gemm_scratch_bytes(N, K, M, false));
+  return al256(tl::w4_gemm_scratch_bytes(N, K, M, false, false));
 }
 
 tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_t* d_A, int32_t M, float* d_C,
@@ -1317,10 +1317,10 @@ tl_status tl_w4_linear(const void* d_packed, int32_t N, int32_t K, const uint16_
     TL_HIP(tl::launch_w4_gemv(p, tl::ASrc{d_A, nullptr, nullptr, 0.f}, M, e, s));
     return TL_OK;
   }
-  const int S = tl::plan_w4_gemm(N, K, M, false).S;
+  const int S = tl::plan_w4_gemm(N, K, M, false, false, false).S;
   if (S > 1 && (!d_ws || !aligned(d_ws, 256))) return fail(TL_E_INVAL, "this shape needs d_ws");
   float* part = static_cast<float*>(d_ws);
-  TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, part, s));
+  TL_HIP(tl::launch_w4_gemm(p, d_A, M, e, part, s, false));
   if (S > 1) TL_HIP(tl::launch_reduce_partials(part, S, M, N, d_C, 0, s));
   return TL_OK;
 }

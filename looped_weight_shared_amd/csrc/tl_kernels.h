@@ -168,12 +168,15 @@ struct GemmPlan {
 };
 constexpr int kMaxSplitK = 16;  // consumers sum at most this many partials
 // swiglu: gate/up pairs per wave and no K split; unsplit: no K split
-GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit = false);
-size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu);
+// folded: the caller sums split-K partials within a pass it makes anyway
+// (false: the standalone linear, which needs an extra reduction pass)
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit = false, bool folded = true);
+size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu, bool folded = true);
 // C = A * W^T for any M (prefill GEMM shape); A fp16 [M][K]. When the plan
 // splits K (S > 1, never for SwiGLU) the kernel writes the S partials to
 // `part` instead of running the epilogue; the caller passes them on.
-hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s);
+hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s,
+                          bool folded = true);
 // out (= or +=) sum of S partials [S][M][N], in split order.
 hipError_t launch_reduce_partials(const float* part, int S, int M, int N, float* out, int accumulate, hipStream_t s);
 

@@ -741,7 +741,14 @@ __global__ __launch_bounds__(256, MB > 2 ? 2 : 1) void w4_gemm_kernel(const uint
 // tile leaves CUs unevenly loaded: QKV at M = 1024 (384 blocks) measured 47.8
 // -> 52.8 us in situ, so it and the O and down projections stay on 32-row
 // tiles. K is never split on this path.
-GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit) {
+//
+// From M = 512 the other linears take 64-row tiles (kernel <4, 2>, 64 x 128
+// blocks, the large-M code path): half the dequantization per output of the
+// 32-row tiles. At M = 1024 (seq-1024 forward, one box, two alternations)
+// QKV 47.7 -> 42.5 us, down 42.6 -> 36.9 (now split-K 2), O 18.9 -> 17.6,
+// the step 3.58-3.60 -> 3.52-3.54 ms; unsplit O and down on 256 such blocks
+// were slower (21, 46 us).
+GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit, bool folded) {
   const int NB = N / 16, G = (K + 127) / 128;
   GemmPlan p{};
   if ((long long)((NB + 7) / 8) * ((M + 127) / 128) >= 512) {
@@ -754,30 +761,40 @@ GemmPlan plan_w4_gemm(int N, int K, int M, bool swiglu, bool unsplit) {
     p.blocks = ((p.gx + 7) / 8) * 8 * p.gy;
     return p;
   }
-  p.mb = M <= 16 ? 1 : 2;
-  p.gy = (M + 16 * p.mb - 1) / (16 * p.mb);
-  auto splits = [&](int gx) {
-    int S = 1;
-    if (!swiglu && !unsplit)
-      while (S < kMaxSplitK && gx * p.gy * S < 384 && G / (2 * S) >= 4) S *= 2;
-    return S;
+  auto tiles = [&](int mb) {
+    GemmPlan q{};
+    q.mb = mb;
+    q.gy = (M + 16 * mb - 1) / (16 * mb);
+    auto splits = [&](int gx) {
+      int S = 1;
+      if (!swiglu && !unsplit)
+        while (S < kMaxSplitK && gx * q.gy * S < 384 && G / (2 * S) >= 4) S *= 2;
+      return S;
+    };
+    q.nbw = 2;
+    q.gx = (NB + 4 * q.nbw - 1) / (4 * q.nbw);
+    int S = splits(q.gx);
+    if (!swiglu && mb <= 2 && q.gx * q.gy * S < 256) {
+      q.nbw = 1;
+      q.gx = (NB + 3) / 4;
+      S = splits(q.gx);
+    }
+    q.gps = (G + S - 1) / S;
+    q.S = (G + q.gps - 1) / q.gps;
+    q.blocks = ((q.gx + 7) / 8) * 8 * q.gy * q.S;
+    return q;
   };
-  p.nbw = 2;
-  p.gx = (NB + 4 * p.nbw - 1) / (4 * p.nbw);
-  int S = splits(p.gx);
-  if (!swiglu && p.gx * p.gy * S < 256) {
-    p.nbw = 1;
-    p.gx = (NB + 3) / 4;
-    S = splits(p.gx);
+  // 64-row tiles from M = 512, unless they would split K for a caller that
+  // must sum the partials in a pass of its own (the standalone linear)
+  if (M >= 512) {
+    const GemmPlan q = tiles(4);
+    if (folded || q.S == 1) return q;
   }
-  p.gps = (G + S - 1) / S;
-  p.S = (G + p.gps - 1) / p.gps;
-  p.blocks = ((p.gx + 7) / 8) * 8 * p.gy * p.S;
-  return p;
+  return tiles(M <= 16 ? 1 : 2);
 }
 
-size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu) {
-  const GemmPlan p = plan_w4_gemm(N, K, M, swiglu, false);
+size_t w4_gemm_scratch_bytes(int N, int K, int M, bool swiglu, bool folded) {
+  const GemmPlan p = plan_w4_gemm(N, K, M, swiglu, false, folded);
   if (p.S == 1) return 0;
   return (size_t)p.S * M * N * 4;
 }
@@ -821,9 +838,10 @@ static hipError_t gemm_launch(const Packed& w, const uint16_t* A, int M, const E
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s) {
+hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& e, float* part, hipStream_t s,
+                          bool folded) {
   if (M < 1) return hipErrorInvalidValue;
-  GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU, e.mode == EPI_QKV_ROPE);
+  GemmPlan pl = plan_w4_gemm(w.N, w.K, M, e.mode == EPI_SWIGLU, e.mode == EPI_QKV_ROPE, folded);
   if (pl.S > 1 && !part) return hipErrorInvalidValue;
   if (e.mode == EPI_QKV_ROPE) {
     const int d = e.kv.H * e.kv.hd;
@@ -832,6 +850,7 @@ hipError_t launch_w4_gemm(const Packed& w, const uint16_t* A, int M, const Epi& 
   }
   pl.part = part;
   if (pl.mb == 8) return gemm_launch<8, 2>(w, A, M, e, pl, s);
+  if (pl.mb == 4) return gemm_launch<4, 2>(w, A, M, e, pl, s);
   if (pl.nbw == 2) return pl.mb == 2 ? gemm_launch<2, 2>(w, A, M, e, pl, s) : gemm_launch<1, 2>(w, A, M, e, pl, s);
   return pl.mb == 2 ? gemm_launch<2, 1>(w, A, M, e, pl, s) : gemm_launch<1, 1>(w, A, M, e, pl, s);
 }

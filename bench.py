@@ -228,9 +228,14 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
         ms = timed(step, 5)
         flop = _layer_flops(s, M) * (s.n_pre + Lx)
         roof_us = flop / (PEAK_F16_TFLOPS * 1e12) * 1e6
+        tl.tl_profile_begin(mx.ctx, 100000)
+        for _ in range(2):
+            step()
+        prof = tl.tl_profile_end(mx.ctx)
         res[f"prefill_seq{M}_L{Lx}"] = {"ms_per_step": round(ms, 3), "tokens_per_s": round(M / ms * 1e3, 1),
                                         "gflop": round(flop / 1e9, 1), "mfma_roofline_us": round(roof_us, 1),
-                                        "frac": round(roof_us / (ms * 1e3), 4)}
+                                        "frac": round(roof_us / (ms * 1e3), 4),
+                                        "kernels_us": {k: round(v / n * 1e3, 2) for k, (n, v) in prof.items() if n}}
         print(f"[bench] prefill seq {M} L={Lx}: {ms:.3f} ms/step, {M / ms * 1e3:,.0f} tok/s "
               f"({roof_us / (ms * 1e3):.1%} of the MFMA roofline)", file=sys.stderr, flush=True)
         mx.close()
@@ -266,9 +271,15 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
         algo = (wbytes * (s.n_pre + max(loops)) + s.vocab * s.d_model * 2
                 + sum(kv_per_tok * (s.n_pre + Lx) * (P + D // 2) for Lx in loops))
         roof_us = algo / (PEAK_HBM_GBS * 1e9) * 1e6
+        prime()
+        tl.tl_profile_begin(mi.ctx, 100000)
+        for t in range(32):
+            mi.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+        prof = tl.tl_profile_end(mi.ctx)
         res[name] = {"ms_per_step": round(ms, 4), "lanes": nl, "loops": loops, "context": P + D, "graph_replayed": False,
                      "algorithmic_bytes_per_step": int(algo), "hbm_roofline_us": round(roof_us, 1),
-                     "frac": round(roof_us / (ms * 1e3), 4)}
+                     "frac": round(roof_us / (ms * 1e3), 4),
+                     "kernels_us": {k: round(v / n * 1e3, 2) for k, (n, v) in prof.items() if n}}
         print(f"[bench] {name}: {ms:.4f} ms/step ({roof_us / (ms * 1e3):.1%} of the HBM roofline)",
               file=sys.stderr, flush=True)
         mi.close()

@@ -58,7 +58,7 @@ def _check(w, om16, s, P, steps, L, kv, max_tokens):
     hid, lgs = _run(m, s, toks, P, steps)
     m.close()
     ro = oracle.forward(om16, toks, L, logits=None, max_seq=P + steps + 8, kv_int8=kv == tl.TL_KV_INT8,
-                        store_h=kv == tl.TL_KV_H16)
+                        store_h=kv == tl.TL_KV_H16, h_int8=kv == tl.TL_KV_H8)
     ref_l = oracle.head_logits(om16, ro["hidden"][P - 1:])
     e_h, e_l = rel_rows(hid, ro["hidden"]), rel_rows(lgs, ref_l)
     print(f"fp16 body P={P} L={L} kv={kv}: hidden {e_h:.2e} logits {e_l:.2e}")
@@ -72,7 +72,7 @@ def tiny():
     return s, w, oracle.OracleModel(w, fp16_body=True)
 
 
-@pytest.mark.parametrize("P,L,kv", [(5, 3, 0), (40, 3, 0), (130, 2, 0), (40, 3, 2)])
+@pytest.mark.parametrize("P,L,kv", [(5, 3, 0), (40, 3, 0), (130, 2, 0), (40, 3, 2), (40, 3, 3)])
 def test_tiny_fp16_body(tiny, P, L, kv):
     s, w, om16 = tiny
     _check(w, om16, s, P, 6, L, kv, max_tokens=P)

@@ -196,7 +196,7 @@ def _layer_flops(s, M):
     return gemm + 4 * s.n_heads * s.head_dim * M * (M + 1) // 2
 
 
-def other_configs(s, w, tl, Model, torch, synth, stream):
+def other_configs(s, w, tl, Model, torch, synth, stream, only=None):
     """The 407M workloads besides the headline one: seq-1024 prefill at L=16
     and 32 (tokens/s against the MFMA roofline), and cached greedy decode at
     context 2048 with an INT8 KV cache (prompt 1920 + 128 steps), one lane at
@@ -217,6 +217,8 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
     M = 1024
     t1024 = torch.from_numpy(synth.make_tokens(s.vocab, M, seed=0)).cuda()
     for Lx in (16, 32):
+        if only and f"prefill_seq{M}_L{Lx}" not in only:
+            continue
         mx = Model(w, max_seq=2048, max_loops=Lx, n_lanes=1, kv_dtype=tl.TL_KV_FP16, max_tokens=M)
         mx.set_loops(0, Lx)
 
@@ -246,6 +248,8 @@ def other_configs(s, w, tl, Model, torch, synth, stream):
               + tl.tl_qlinear_packed_bytes(s.d_model, s.ffn_dim))
     kv_per_tok = 2 * s.n_heads * (s.head_dim + 2)  # INT8 K and V rows plus their fp16 scales, one layer
     for name, loops in (("decode_int8_ctx2048_L8", [8]), ("decode_int8_ctx2048_3lanes_L4_16_32", [4, 16, 32])):
+        if only and name not in only:
+            continue
         nl = len(loops)
         mi = Model(w, max_seq=2048, max_loops=max(loops), n_lanes=nl, kv_dtype=tl.TL_KV_INT8, max_tokens=P)
         bufs = [torch.zeros(nl, dtype=torch.int32, device="cuda") for _ in range(2)]
@@ -575,6 +579,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
                          "context 2048, one lane at L=8 and three lanes at L=4/16/32)")
+    ap.add_argument("--configs", metavar="NAMES",
+                    help="comma-separated subset of the other workloads (prefill_seq1024_L16, prefill_seq1024_L32, "
+                         "decode_int8_ctx2048_L8, decode_int8_ctx2048_3lanes_L4_16_32)")
     ap.add_argument("--cpu-configs", action="store_true",
                     help="also time the CPU oracle on those workloads (bounded samples; about two minutes)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -887,7 +894,8 @@ def main():
 
     # ---------------------------------------------------------------- other workloads
     if not args.no_configs:
-        out["other_configs"] = other_configs(s, w, tl, Model, torch, synth, stream)
+        out["other_configs"] = other_configs(s, w, tl, Model, torch, synth, stream,
+                                             args.configs.split(",") if args.configs else None)
 
     # ---------------------------------------------------------------- decode roofline
     # headline: the four loop-block GEMVs with cold weights (kernel leg), their

@@ -45,7 +45,10 @@ def source_hash() -> str:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
-    h.update(" ".join([ARCH] + FLAGS).encode())
+    # the flags with the include directories relative to the repository, so
+    # that a copy of the tree at another path keeps the same stamp
+    flags = [f.replace(ROOT, ".") for f in FLAGS]
+    h.update(" ".join([ARCH] + flags).encode())
     return h.hexdigest()
 
 

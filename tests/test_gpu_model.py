@@ -152,6 +152,24 @@ def test_407m_prefill_seq128_L8_full_size(m407):
     m.close()
 
 
+@pytest.mark.parametrize("n", [512, 600])
+def test_407m_prefill_64_row_tiles(m407, n):
+    """From 512 rows the QKV (RoPE epilogue), gate/up (SwiGLU epilogue), O and
+    down (split-K partials summed by the next RMSNorm) GEMMs run 64-row tiles;
+    below 641 rows gate/up has not yet switched to the 128-row tile. Every
+    position against the oracle at L=2."""
+    w, om = m407
+    prompt = synth.make_tokens(w["shape"].vocab, n, seed=3)
+    m = _model(w, max_seq=1024, max_loops=2, max_tokens=n)
+    m.set_loops(0, 2)
+    hid, lg, nx = GpuRun(m).prefill(prompt)
+    ro = oracle.forward(om, prompt, 2)
+    e_h, e_l = rel_rows(hid, ro["hidden"]), rel_rows(lg, ro["logits"])
+    print(f"407M n={n} L2: hidden {e_h:.2e} logits {e_l:.2e}")
+    assert e_h < TOL and e_l < TOL
+    m.close()
+
+
 @pytest.mark.parametrize("L", [8, 32])
 @pytest.mark.parametrize("kv_int8", [False, True])
 def test_407m_prefill_and_decode(m407, L, kv_int8):

@@ -74,7 +74,8 @@ def test_repack_is_bit_exact(N, K):
 LIN_CASES = [(6144, 2048, m) for m in (1, 3, 8, 16, 17, 128, 130, 512, 700, 1024, 1400)] + \
             [(2048, 5632, m) for m in (1, 2, 64, 100, 1024)] + [(2048, 2048, 128), (2048, 2048, 1024)] + \
             [(256, 704, m) for m in (1, 5, 32, 33)] + [(11264, 2048, m) for m in (1, 100, 256, 600, 1000, 1024)] + \
-            [(2048, 2048, 512)]
+            [(2048, 2048, 512)] + \
+            [(1040, 2048, 600), (1040, 704, 130), (1040, 2048, 17), (16, 128, 40)]  # n-blocks not a multiple of the tile
 
 
 @pytest.mark.parametrize("N,K,M", LIN_CASES)

@@ -30,12 +30,8 @@
 namespace tl {
 
 // ---------------------------------------------------------------- epilogue
-__device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float v) {
-  if (e.perm_hd) n = qkv_natural_col(n, e.perm_hd);
-  if (e.mode == EPI_RESID)
-    e.out_f32[(size_t)m * e.ldo + n] += v;
-  else
-    e.out_f32[(size_t)m * e.ldo + n] = v;
+__device__ __forceinline__ size_t epi_index(const Epi& e, int m, int n) {
+  return (size_t)m * e.ldo + (e.perm_hd ? qkv_natural_col(n, e.perm_hd) : n);
 }
 __device__ __forceinline__ void epi_swiglu(const Epi& e, int m, int c, float g, float u) {
   e.out_f16[(size_t)m * e.ldo + c] = f2h(silu(g) * u);
@@ -154,6 +150,18 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
         sc[it][j] = scales[tile * 16 + l16];
       }
     }
+  }
+  // the residual values the epilogue adds to (EPI_RESID), requested last: the
+  // epilogue thread (row em, column ecol of each n-block) owns them, so they
+  // need no wait until the end and no dependent load remains there
+  const int eln = tid >> 2, er = tid & 3;
+  const int em = 4 * (eln >> 4) + er, ecol = eln & 15;
+  const bool eout = tid < 256 && em < M;
+  float rx[NBB];
+#pragma unroll
+  for (int j = 0; j < NBB; ++j) {
+    rx[j] = 0.f;
+    if (e.mode == EPI_RESID && eout) rx[j] = e.out_f32[epi_index(e, em, (nb0 + j) * 16 + ecol)];
   }
   asm volatile("" ::: "memory");
   if constexpr (NORM) {
@@ -283,23 +291,20 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[((wave * NBB + j) * 64 + lane) * 4 + r] = acc[j][r];
   __syncthreads();
-  if (tid < 256) {
-    const int ln = tid >> 2, r = tid & 3;
-    const int m = 4 * (ln >> 4) + r, col = ln & 15;
-    if (m < M) {
-      float v[NBB];
+  if (eout) {
+    float v[NBB];
 #pragma unroll
-      for (int j = 0; j < NBB; ++j) {
-        float t = 0.f;
-        for (int w = 0; w < WK; ++w) t += red[((w * NBB + j) * 64 + ln) * 4 + r];
-        v[j] = t;
-      }
-      if (e.mode == EPI_SWIGLU) {
-        if constexpr (NBB == 2) epi_swiglu(e, m, blockIdx.x * 16 + col, v[0], v[1]);
-      } else {
+    for (int j = 0; j < NBB; ++j) {
+      float t = 0.f;
+      for (int w = 0; w < WK; ++w) t += red[((w * NBB + j) * 64 + eln) * 4 + er];
+      v[j] = t;
+    }
+    if (e.mode == EPI_SWIGLU) {
+      if constexpr (NBB == 2) epi_swiglu(e, em, blockIdx.x * 16 + ecol, v[0], v[1]);
+    } else {
 #pragma unroll
-        for (int j = 0; j < NBB; ++j) epi_store(e, m, (nb0 + j) * 16 + col, v[j]);
-      }
+      for (int j = 0; j < NBB; ++j)
+        e.out_f32[epi_index(e, em, (nb0 + j) * 16 + ecol)] = e.mode == EPI_RESID ? rx[j] + v[j] : v[j];
     }
   }
 }

@@ -579,12 +579,38 @@ __global__ __launch_bounds__(256, MB > 2 ? 2 : 1) void w4_gemm_kernel(const uint
     }
   };
 
+  // QKV epilogue of the small tiles: the RoPE cos/sin of every output this
+  // lane writes, requested with the first groups rather than after the loop
+  // (they depend on nothing the loop computes)
+  constexpr bool kRopePre = EP == GEP_QKV && !kBig;
+  float rcs[kRopePre ? NBW : 1][kRopePre ? MB : 1][4][2];
+  auto rope_at = [&](int j, int i, int rr) {
+    const int half = e.kv.hd / 2;
+    const int n = min(nbw0 + j, NB - 1) * 16 + l16, p = n % e.kv.hd;
+    const int t = 8 * (p >> 4) + (p & 7);
+    const int pos = e.p0 + min(m0 + i * 16 + 4 * lq + rr, M - 1);
+    return (size_t)pos * half + t;
+  };
+
   if constexpr (DA == D) {
     // prologue: groups kg0 .. kg0+D-1 requested; group kg0's activations staged
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       load_a(ar[k], kg0 + k);
       load_b(br[k], bs[k], kg0 + k);
+    }
+    if constexpr (kRopePre) {
+      const size_t sin_off = (size_t)e.kv.S * (e.kv.hd / 2);
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const size_t o = rope_at(j, i, rr);
+            rcs[j][i][rr][0] = e.rope[o];
+            rcs[j][i][rr][1] = e.rope[sin_off + o];
+          }
     }
     store_a(ar[0], 0);
     lds_barrier();
@@ -689,8 +715,14 @@ __global__ __launch_bounds__(256, MB > 2 ? 2 : 1) void w4_gemm_kernel(const uint
           const float other = dpp_mov<kDppRor8>(v);  // the pair partner, 8 lanes away
           float y = v;
           if (sec < 2) {
-            const float c = e.rope[(size_t)pos * half + t];
-            const float sn = e.rope[(size_t)e.kv.S * half + (size_t)pos * half + t];
+            float c, sn;
+            if constexpr (kRopePre) {
+              c = rcs[j][i][rr][0];
+              sn = rcs[j][i][rr][1];
+            } else {
+              c = e.rope[(size_t)pos * half + t];
+              sn = e.rope[(size_t)e.kv.S * half + (size_t)pos * half + t];
+            }
             _Float16 y1, y2;
             rope_pair(first ? v : other, first ? other : v, c, sn, &y1, &y2);
             y = (float)(first ? y1 : y2);

@@ -278,7 +278,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
     // (lq, n) addressing key row +4lq + n/4 at dims 16b + 4(n%4) .. +3), so
     // both operands enumerate k in the same order. P (value scale folded in)
     // enters as an fp16 high part and the fp16 rounding of the remainder: the
-    // two MFMAs apply it with about 22 significant bits instead of 11.
+    // two MFMAs apply it with about 22 significant bits instead of 11. (INT8:
+    // a weight near 1 is then the fp16 scale itself, held exactly; weights
+    // far below it fall into fp16's subnormal range and keep fewer bits, on
+    // terms that carry little of O.)
 #pragma unroll
     for (int j = 0; j < PS; ++j) {
       half8_t ph, pl;

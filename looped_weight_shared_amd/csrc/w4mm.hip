@@ -215,22 +215,29 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const uint8_t* __
     // merge each row's parts in part order (attn_merge_step), as the merge kernel does
     const bool kin = k4 < K;
     for (int m = 0; m < M; ++m) {
+      // row m's parts are pairs q0 .. q1-1 (row-major); one weight and one
+      // sum per part, shared by the thread's 4 columns (the merge kernel's
+      // per-element arithmetic, attn_merge_step, in the same order)
+      const int q0 = m * a.att_np, q1 = min(q0 + a.att_np, npairs);
       float gm = -INFINITY;
 #pragma unroll
       for (int q = 0; q < APT; ++q)
-        if (q < npairs && q / a.att_np == m) gm = fmaxf(gm, ml[q].x);
-      float num[4] = {0.f, 0.f, 0.f, 0.f}, den[4] = {0.f, 0.f, 0.f, 0.f};
+        if (q >= q0 && q < q1) gm = fmaxf(gm, ml[q].x);
+      float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
 #pragma unroll
       for (int q = 0; q < APT; ++q)
-        if (q < npairs && q / a.att_np == m)
+        if (q >= q0 && q < q1 && ml[q].x != -INFINITY) {
+          const float w = __builtin_amdgcn_exp2f(ml[q].x - gm);
+          den = fmaf(w, ml[q].y, den);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) attn_merge_step(gm, ml[q].x, ml[q].y, xv[q][c], num[c], den[c]);
+          for (int c = 0; c < 4; ++c) num[c] = fmaf(w, xv[q][c], num[c]);
+        }
       if (k4 < Kp) {
         half2_t h01, h23;
-        h01.x = (_Float16)(num[0] / den[0]);
-        h01.y = (_Float16)(num[1] / den[1]);
-        h23.x = (_Float16)(num[2] / den[2]);
-        h23.y = (_Float16)(num[3] / den[3]);
+        h01.x = (_Float16)(num[0] / den);
+        h01.y = (_Float16)(num[1] / den);
+        h23.x = (_Float16)(num[2] / den);
+        h23.y = (_Float16)(num[3] / den);
         const half2_t z2 = {0, 0};
         *reinterpret_cast<half2_t*>(As + m * lda + k4) = kin ? h01 : z2;
         *reinterpret_cast<half2_t*>(As + m * lda + k4 + 2) = kin ? h23 : z2;

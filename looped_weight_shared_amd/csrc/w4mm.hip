@@ -62,7 +62,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// GI: groups requested per wave (ceil(G / 8) rounded up to 2 or 8; a wave
+// GI: groups requested per wave (ceil(G / 8) rounded up to 2, 6 or 8; a wave
 // with fewer groups re-requests its last one and skips it in the math). APT:
 // fp16 activation chunks per thread (fp16 input). All requests are
 // unconditional with clamped addresses, so the code between them is
@@ -395,7 +395,8 @@ hipError_t launch_w4_gemv(const Packed& w, const ASrc& a, int M, const Epi& e, h
                                                        : gemv_norm_rows<1>(w, a, M, e, s);
   if (e.mode == EPI_SWIGLU) return hipErrorInvalidValue;
   if (a.att) return gemv_att(w, a, M, e, s);
-  return w.G <= 2 * kGemvWaves ? gemv_a16<2>(w, a, M, e, s) : gemv_a16<8>(w, a, M, e, s);
+  if (w.G <= 2 * kGemvWaves) return gemv_a16<2>(w, a, M, e, s);
+  return w.G <= 6 * kGemvWaves ? gemv_a16<6>(w, a, M, e, s) : gemv_a16<8>(w, a, M, e, s);
 }
 
 // ---------------------------------------------------------------- GEMM

@@ -142,12 +142,22 @@ def _forward_kernels():
     }
 
 
+def _gemv_a16_template(K, M=1):
+    """Template of the fp16-input W4 GEMV the library launches for K (groups requested per wave:
+    2, 6 or 8 for up to 16, 48 or 64 groups; fp16 chunks per thread rounded up to a power of 2)."""
+    G = (K + 127) // 128
+    gi = 2 if G <= 16 else (6 if G <= 48 else 8)
+    apt_raw = -(-(M * (K // 8)) // 512)
+    apt = next(a for a in (1, 2, 4, 8, 16) if apt_raw <= a)
+    return f"w4_gemv_kernel<1, 0, 1, {gi}, {apt}, false>"
+
+
 def _cold_gemv_kernels():
     """The M = 1 GEMVs of `bench.py --pmc-kernels` (fp16 A row in, fp32 C row out), one entry per
     loop-block linear, told apart by template and grid (512 threads, N / 16 blocks)."""
     out = {}
     for name, (N, K) in PMC_SHAPES.items():
-        tmpl = "w4_gemv_kernel<1, 0, 1, 8, 2, false>" if K > 2048 else "w4_gemv_kernel<1, 0, 1, 2, 1, false>"
+        tmpl = _gemv_a16_template(K)
         out["gemv_cold_" + name] = ((lambda t, g0: (lambda n, g: t in n and g == g0))(tmpl, (N // 16) * 512),
                                     tl_packed_bytes(N, K) + K * 2 + N * 4)
     return out

@@ -92,3 +92,14 @@ def test_pmc_summary_windows_by_dispatch(tmp_path):
     assert len(before) == 2 and float(before[1].split()[-1]) == 100.0
     vals = {l.split("(")[0].strip()[:30]: float(l.split()[-1]) for l in after[1:]}
     assert sorted(vals.values()) == [300.0, 900.0]
+
+
+def test_gemv_a16_template_follows_the_library_dispatch():
+    """The counter ingest finds the M = 1 fp16-input GEMV by template: 2, 6 or 8 groups per wave
+    for up to 16, 48 or 64 K groups, fp16 chunks per thread rounded up to a power of 2."""
+    t = bench._gemv_a16_template
+    assert t(2048) == "w4_gemv_kernel<1, 0, 1, 2, 1, false>"    # QKV / O / gate-up shapes
+    assert t(5632) == "w4_gemv_kernel<1, 0, 1, 6, 2, false>"    # down projection, 44 groups
+    assert t(6144) == "w4_gemv_kernel<1, 0, 1, 6, 2, false>"    # 48 groups: the last with 6
+    assert t(6272) == "w4_gemv_kernel<1, 0, 1, 8, 2, false>"    # 49 groups
+    assert t(704) == "w4_gemv_kernel<1, 0, 1, 2, 1, false>"     # tiny shape's down projection

@@ -216,7 +216,7 @@ tl_status tl_prefill(tl_ctx* ctx, int32_t lane, const int32_t* d_tokens, int32_t
 
 /* Graph capture/replay, off by default. enable is a bit mask: bit 0
  * (value 1) prefill, bit 1 (value 2) decode steps. Replay cuts the host's
- * enqueue time (about 0.47 -> 0.06 ms for the ~80 launches of a 10-layer
+ * enqueue time (about 0.2-0.5 -> 0.06 ms for the ~80 launches of a 10-layer
  * prefill; decode steps, ~52 launches, likewise) but not the GPU time, which
  * the kernels and the per-dispatch gap set.
  * Decode: a step is captured once per (active lanes in order, their L, the

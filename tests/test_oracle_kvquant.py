@@ -91,3 +91,14 @@ def test_kv_bytes_match_printed_page_numbers():
     per_token_int8 = int8 // g["max_seq"]
     assert fp16 // per_token_int8 == g["int8_context_printed"]
     assert fp16 // (fp16 // g["max_seq"]) == g["fp16_context_printed"]
+
+
+def test_dequantize_worked_rows():
+    """Hand-worked values: each row's codes times that row's scale (not another row's), exactly,
+    including a subnormal fp16 scale."""
+    q = np.array([[127, -127, 1, 0], [3, -2, 0, 64]], dtype=np.int8)
+    s = np.array([0.5, 2.0 ** -20], dtype=np.float16)
+    d = oracle.kv_dequantize(q, s)
+    assert d.dtype == np.float64
+    assert d[0].tolist() == [63.5, -63.5, 0.5, 0.0]
+    assert d[1].tolist() == [3 * 2.0 ** -20, -2 * 2.0 ** -20, 0.0, 64 * 2.0 ** -20]

@@ -25,6 +25,16 @@
 
 namespace tl {
 
+// Workgroups go to the 8 XCDs round-robin by linear index and each XCD has
+// its own L2. Renumbering block b of an n-block grid so that the blocks one
+// XCD receives are consecutive indices lets a (head, query tile) grid put
+// whole heads on one XCD: a head's K/V rows then enter one L2 instead of all
+// eight. A bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int x = b & 7, per = n >> 3, extra = n & 7;
+  return x * per + min(x, extra) + (b >> 3);
+}
+
 struct CachePtrs {
   const uint8_t* k;   // fp16 [S][hd] or int8 [S][hd] of this head
   const uint8_t* v;
@@ -123,8 +133,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int qg = wave & 3, kh = wave >> 2;  // query group, key half
   const int l16 = ln & 15, lq = ln >> 4;
-  const int h = blockIdx.y;
-  const int q0 = blockIdx.x * 64;
+  // 1-D grid of H x nq blocks, head-major per XCD; within a head the last
+  // (causally longest) query tile is dispatched first
+  const int nq = (M + 63) / 64;
+  const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int h = id / nq;
+  const int q0 = (nq - 1 - (id - h * nq)) * 64;
   const int d = kv.H * HD;
   const int kend = p0 + min(q0 + 64, M);  // keys [kbeg, kend) can be visible to this block
   const int kbeg = kv_first(kv, p0 + q0);  // the window of the block's first query
@@ -370,8 +384,10 @@ __global__ __launch_bounds__(256) void attn_prefill_short_kernel(const uint16_t*
 
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int l16 = ln & 15, lq = ln >> 4;
-  const int h = blockIdx.y;
-  const int q0 = blockIdx.x * kShortQ;
+  const int nq = (M + kShortQ - 1) / kShortQ;  // 1-D grid of H x nq blocks, as in the tiled kernel
+  const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int h = id / nq;
+  const int q0 = (nq - 1 - (id - h * nq)) * kShortQ;
   const int d = kv.H * HD;
   const int kend = p0 + min(q0 + kShortQ, M);  // keys [kbeg, kend) can be visible to this block
   const int kbeg = kv_first(kv, p0 + q0);
@@ -571,7 +587,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
   // a long context reached by a short call is better served by the tiled
   // kernel, which requests the next key tile during the current one)
   if (M <= kShortMaxM && p0 + M - kv_first(kv, p0) <= 8 * kShortChunk) {
-    const dim3 g((M + kShortQ - 1) / kShortQ, kv.H);
+    const dim3 g((M + kShortQ - 1) / kShortQ * kv.H);
     if (kv.hd == 128 && kv.int8)
       launch(attn_prefill_short_kernel<128, true>, g, dim3(256), 0, s, q, M, lane, p0, kv, layer, o);
     else if (kv.hd == 128)
@@ -584,7 +600,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  dim3 grid((M + 63) / 64, kv.H);
+  const dim3 grid((M + 63) / 64 * kv.H);
   if (kv.hd == 128 && kv.int8)
     launch(attn_prefill_kernel<128, true>, grid, dim3(kAttnThreads), 0, s, q, M, lane, p0, kv, layer, o);
   else if (kv.hd == 128)

@@ -180,25 +180,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       return __builtin_bit_cast(half8_t, r);
     }
   };
+  // Rows outside [kbeg, kend) hold the clamped edge row, a finite cache row:
+  // their scores are masked to -inf, so their weights are exactly 0.
   auto store_tile = [&](int kt) {
-    const half8_t hz = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + kAttnThreads * i;
       const int kr = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-      const bool ok = kt * KT + kr < kend && kt * KT + kr >= kbeg;
-      *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = ok ? to_f16(kreg[i]) : hz;
-      *reinterpret_cast<half8_t*>(&Vs[kr * LV + d0]) = ok ? to_f16(vreg[i]) : hz;
+      *reinterpret_cast<half8_t*>(&Ks[kr * LK + d0]) = to_f16(kreg[i]);
+      *reinterpret_cast<half8_t*>(&Vs[kr * LV + d0]) = to_f16(vreg[i]);
     }
-    if (tid < KT) {
-      const bool ok = kt * KT + tid < kend && kt * KT + tid >= kbeg;
-      float a = 1.f, b = 1.f;
-      if constexpr (I8) {
-        a = ok ? h2f((uint16_t)kscr) : 0.f;
-        b = ok ? h2f((uint16_t)vscr) : 0.f;
+    if constexpr (I8) {  // an FP16 cache takes the softmax scale as a constant
+      if (tid < KT) {
+        ksc[tid] = h2f((uint16_t)kscr) * scale;
+        vsc[tid] = h2f((uint16_t)vscr);
       }
-      ksc[tid] = a * scale;
-      vsc[tid] = b;
     }
   };
 
@@ -226,6 +222,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
   const int qpos = p0 + q0 + 16 * qg + l16;
   const int kfirst = kv_first(kv, qpos);
+  // a key part in [kfull0, kfull1] is visible to all 16 queries of the group
+  const int kfull0 = kv_first(kv, p0 + q0 + 16 * qg + 15), kfull1 = p0 + q0 + 16 * qg;
 
   for (int kt = kt0; kt < nkt; ++kt) {
     const int key0 = kt * KT + kh * KH;  // this wave's keys key0 .. key0 + KH - 1
@@ -236,6 +234,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
 
     // ---- S^T = K Q^T for KH keys x 16 queries (lane: keys 16kb + 4lq + r, query n)
     float sv[KB][4];
+    float4_t st[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       float4_t t = {0.f, 0.f, 0.f, 0.f};
@@ -244,12 +243,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
         const half8_t kf = *reinterpret_cast<const half8_t*>(&Ks[(kh * KH + kb * 16 + l16) * LK + 32 * s + 8 * lq]);
         t = mfma16(kf, qf[s], t);
       }
-      const float4_t ks = *reinterpret_cast<const float4_t*>(&ksc[kh * KH + kb * 16 + 4 * lq]);
+      const float4_t ks = I8 ? *reinterpret_cast<const float4_t*>(&ksc[kh * KH + kb * 16 + 4 * lq])
+                             : (float4_t){scale, scale, scale, scale};
+      st[kb] = t * ks;
+    }
+    if (key0 >= kfull0 && key0 + KH - 1 <= kfull1) {  // wave-uniform: no key of the part is masked
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + kb * 16 + 4 * lq + r;
-        sv[kb][r] = (key <= qpos && key >= kfirst) ? t[r] * ks[r] : -INFINITY;
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[kb][r] = st[kb][r];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + kb * 16 + 4 * lq + r;
+          sv[kb][r] = (key <= qpos && key >= kfirst) ? st[kb][r] : -INFINITY;
+        }
     }
     // ---- online softmax of the lane's query (its keys are spread over the
     // lanes n, n+16, n+32, n+48)
@@ -302,10 +312,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
 #pragma unroll
       for (int hblk = 0; hblk < 2; ++hblk) {
         const int kb = 2 * j + hblk;
-        const float4_t vs = *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq]);
+        const float4_t vs = I8 ? *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq])
+                               : (float4_t){1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float x = sv[kb][r] * vs[r];
+          const float x = I8 ? sv[kb][r] * vs[r] : sv[kb][r];
           const _Float16 hi = (_Float16)x;
           ph[4 * hblk + r] = hi;
           pl[4 * hblk + r] = (_Float16)(x - (float)hi);

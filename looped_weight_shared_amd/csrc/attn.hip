@@ -269,8 +269,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows4_max(mx);
       const float mnew = fmaxf(mrow, mx);
       // a query with no visible key so far (a sliding window that starts in a
       // later tile, or a key half beyond the query) keeps mnew = -inf:
@@ -286,8 +285,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
           ps += pr;
           sv[kb][r] = pr;
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = rows4_sum(ps);
       lrow = lrow * alpha + ps;
       mrow = mnew;
 #pragma unroll
@@ -495,8 +493,7 @@ __global__ __launch_bounds__(256) void attn_prefill_short_kernel(const uint16_t*
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows4_max(mx);
       const float mnew = fmaxf(mrow, mx);
       // no visible key so far (a window starting later, or keys beyond the
       // query): subtract 0, so the weights are exp(-inf) = 0, not NaN
@@ -511,8 +508,7 @@ __global__ __launch_bounds__(256) void attn_prefill_short_kernel(const uint16_t*
           ps += pr;
           sv[kb][r] = pr;
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = rows4_sum(ps);
       lrow = lrow * alpha + ps;
       mrow = mnew;
 #pragma unroll

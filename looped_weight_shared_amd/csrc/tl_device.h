@@ -94,6 +94,25 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_mov<kDppMirror>(v));
   return v;
 }
+// Max and sum over the four rows' copies of a lane's value (lanes n, n + 16,
+// n + 32, n + 48), on gfx950's row swaps instead of LDS permutes:
+// v_permlane16_swap with both operands holding x leaves rows (0, 0, 2, 2) in
+// the one and (1, 1, 3, 3) in the other, so their elementwise max (sum) is
+// the xor-16 butterfly step in every lane; v_permlane32_swap does the same
+// for the halves. Both operands of every step are the same two values in
+// each lane of a query, so all four lanes end with the same bits.
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 // The same over aligned groups of N = 8 or 16 lanes.
 template <int N>
 __device__ __forceinline__ float lanes_sum(float v) {

@@ -7,8 +7,9 @@
 // read back as q * s in the prefill too (cached and uncached paths agree).
 //
 // Prefill: a block takes 64 queries of one head (8 waves: 4 groups of 16
-// rows x 2 halves of each key tile) and walks 128-key tiles up to its causal
-// limit: K and V tiles staged row-major in LDS (V's MFMA fragments read back
+// rows x 2 halves of each key tile; without a sliding window the rows are two
+// mirrored 32-row tiles, which evens the causal work of the blocks) and walks
+// 128-key tiles up to its causal limit: K and V tiles staged row-major in LDS (V's MFMA fragments read back
 // with gfx950's transposing LDS read), S^T = K Q^T and O^T += V^T P^T on
 // v_mfma_f32_16x16x32_f16 (the transposed score tile is already in the PV
 // MFMA's operand layout, so P stays in registers), online softmax in
@@ -97,6 +98,15 @@ __device__ __forceinline__ void attn_lds_barrier() {
 // rows. Splitting the keys halves each wave's dependent MFMA/softmax chain and
 // puts two waves on every SIMD (9.1 -> 8.6 us per layer at 128 tokens, where
 // a block sees a single tile; longer calls walk more tiles per wave).
+// Blocks per head of the tiled prefill kernel. Without a window (fold) a
+// block takes two 32-row query tiles, j and its mirror nq - 1 - j, as query
+// groups 0-1 and 2-3: every pair has about the same causal work, so the
+// blocks end together instead of the last tile's block walking twice the
+// average number of key tiles (a group whose queries all precede a key part
+// skips it). With a window a block takes 64 consecutive rows.
+__host__ __device__ inline int attn_prefill_blocks(int M, bool fold) {
+  return fold ? ((M + 31) / 32 + 1) / 2 : (M + 63) / 64;
+}
 constexpr int kAttnKT = 128;
 constexpr int kAttnKSplit = 2;
 constexpr int kAttnThreads = 256 * kAttnKSplit;
@@ -133,15 +143,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
   const int qg = wave & 3, kh = wave >> 2;  // query group, key half
   const int l16 = ln & 15, lq = ln >> 4;
-  // 1-D grid of H x nq blocks, head-major per XCD; within a head the last
-  // (causally longest) query tile is dispatched first
-  const int nq = (M + 63) / 64;
+  // 1-D grid of H x nqb blocks, head-major per XCD (attn_prefill_blocks).
+  // r0: first row of this wave's query group (M: the group has no rows).
+  const bool fold = kv.window == 0;
+  const int nqb = attn_prefill_blocks(M, fold);
   const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int h = id / nq;
-  const int q0 = (nq - 1 - (id - h * nq)) * 64;
+  const int h = id / nqb;
+  const int j = id - h * nqb;
+  int r0, rlo, rhi;  // rows [rlo, rhi) bound the block's queries
+  if (fold) {
+    const int nq = (M + 31) / 32, ta = j, tb = nq - 1 - j;
+    r0 = qg < 2 ? 32 * ta + 16 * qg : (tb > ta ? 32 * tb + 16 * (qg - 2) : M);
+    rlo = 32 * ta;
+    rhi = min(32 * max(ta, tb) + 32, M);
+  } else {
+    rlo = (nqb - 1 - j) * 64;  // the causally longest tile first
+    r0 = rlo + 16 * qg;
+    rhi = min(rlo + 64, M);
+  }
   const int d = kv.H * HD;
-  const int kend = p0 + min(q0 + 64, M);  // keys [kbeg, kend) can be visible to this block
-  const int kbeg = kv_first(kv, p0 + q0);  // the window of the block's first query
+  const int kend = p0 + rhi;               // keys [kbeg, kend) can be visible to this block
+  const int kbeg = kv_first(kv, p0 + rlo);  // the window of the block's first query
   const CachePtrs cp = cache_ptrs(kv, lane_id, layer, h);
   // scores in log2 units (softmax scale times log2 e folded into the key
   // scales), so every weight is one v_exp_f32: exp(x) = 2^(x log2 e)
@@ -199,10 +221,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   };
 
   load_tile(kt0);
-  // Q fragments (A operand of S): row q0 + 16*qg + l16, dims 32s + 8lq .. +7
+  // Q fragments (A operand of S): row r0 + l16, dims 32s + 8lq .. +7
   half8_t qf[KS];
   {
-    const int qr = q0 + 16 * qg + l16;
+    const int qr = r0 + l16;
     const int qc = min(qr, M - 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -220,10 +242,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   float4_t oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  const int qpos = p0 + q0 + 16 * qg + l16;
+  const int qpos = p0 + r0 + l16;
   const int kfirst = kv_first(kv, qpos);
-  // a key part in [kfull0, kfull1] is visible to all 16 queries of the group
-  const int kfull0 = kv_first(kv, p0 + q0 + 16 * qg + 15), kfull1 = p0 + q0 + 16 * qg;
+  // a key part in [kfull0, kfull1] is visible to all 16 queries of the group;
+  // one that starts after kvis (or a group without rows) is visible to none
+  const int kfull0 = kv_first(kv, p0 + r0 + 15), kfull1 = p0 + r0;
+  const int kvis = r0 < M ? p0 + r0 + 15 : -1;
 
   for (int kt = kt0; kt < nkt; ++kt) {
     const int key0 = kt * KT + kh * KH;  // this wave's keys key0 .. key0 + KH - 1
@@ -231,101 +255,103 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
     attn_lds_barrier();
     if (kt + 1 < nkt) load_tile(kt + 1);  // the next tile is in flight during this tile's math
     asm volatile("" ::: "memory");
+    if (key0 <= kvis) {  // wave-uniform: otherwise the group's state would not change
 
-    // ---- S^T = K Q^T for KH keys x 16 queries (lane: keys 16kb + 4lq + r, query n)
-    float sv[KB][4];
-    float4_t st[KB];
+      // ---- S^T = K Q^T for KH keys x 16 queries (lane: keys 16kb + 4lq + r, query n)
+      float sv[KB][4];
+      float4_t st[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      float4_t t = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < KB; ++kb) {
+        float4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const half8_t kf = *reinterpret_cast<const half8_t*>(&Ks[(kh * KH + kb * 16 + l16) * LK + 32 * s + 8 * lq]);
-        t = mfma16(kf, qf[s], t);
+        for (int s = 0; s < KS; ++s) {
+          const half8_t kf = *reinterpret_cast<const half8_t*>(&Ks[(kh * KH + kb * 16 + l16) * LK + 32 * s + 8 * lq]);
+          t = mfma16(kf, qf[s], t);
+        }
+        const float4_t ks = I8 ? *reinterpret_cast<const float4_t*>(&ksc[kh * KH + kb * 16 + 4 * lq])
+                               : (float4_t){scale, scale, scale, scale};
+        st[kb] = t * ks;
       }
-      const float4_t ks = I8 ? *reinterpret_cast<const float4_t*>(&ksc[kh * KH + kb * 16 + 4 * lq])
-                             : (float4_t){scale, scale, scale, scale};
-      st[kb] = t * ks;
-    }
-    if (key0 >= kfull0 && key0 + KH - 1 <= kfull1) {  // wave-uniform: no key of the part is masked
+      if (key0 >= kfull0 && key0 + KH - 1 <= kfull1) {  // wave-uniform: no key of the part is masked
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[kb][r] = st[kb][r];
-    } else {
+          for (int r = 0; r < 4; ++r) sv[kb][r] = st[kb][r];
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kb * 16 + 4 * lq + r;
-          sv[kb][r] = (key <= qpos && key >= kfirst) ? st[kb][r] : -INFINITY;
-        }
-    }
-    // ---- online softmax of the lane's query (its keys are spread over the
-    // lanes n, n+16, n+32, n+48)
-    {
-      float mx = sv[0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
-      mx = rows4_max(mx);
-      const float mnew = fmaxf(mrow, mx);
-      // a query with no visible key so far (a sliding window that starts in a
-      // later tile, or a key half beyond the query) keeps mnew = -inf:
-      // subtract 0 instead, so its weights are exp(-inf) = 0 rather than NaN
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);  // 0 while mrow = -inf
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(sv[kb][r] - mref);
-          ps += pr;
-          sv[kb][r] = pr;
-        }
-      ps = rows4_sum(ps);
-      lrow = lrow * alpha + ps;
-      mrow = mnew;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[b][r] *= alpha;
-    }
-    // ---- O^T += V^T P^T over this wave's keys, 32 keys per MFMA. A k-step
-    // pairs key blocks 2j and 2j+1: lane (lq, n) holds P^T for keys
-    // 32j + 4lq + (0..3) and 32j + 16 + 4lq + (0..3) of query n, and reads V^T
-    // for the same 8 keys of dim 16b + n with two transposing reads (lane
-    // (lq, n) addressing key row +4lq + n/4 at dims 16b + 4(n%4) .. +3), so
-    // both operands enumerate k in the same order. P (value scale folded in)
-    // enters as an fp16 high part and the fp16 rounding of the remainder: the
-    // two MFMAs apply it with about 22 significant bits instead of 11. (INT8:
-    // a weight near 1 is then the fp16 scale itself, held exactly; weights
-    // far below it fall into fp16's subnormal range and keep fewer bits, on
-    // terms that carry little of O.)
-#pragma unroll
-    for (int j = 0; j < PS; ++j) {
-      half8_t ph, pl;
-#pragma unroll
-      for (int hblk = 0; hblk < 2; ++hblk) {
-        const int kb = 2 * j + hblk;
-        const float4_t vs = I8 ? *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq])
-                               : (float4_t){1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = I8 ? sv[kb][r] * vs[r] : sv[kb][r];
-          const _Float16 hi = (_Float16)x;
-          ph[4 * hblk + r] = hi;
-          pl[4 * hblk + r] = (_Float16)(x - (float)hi);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int key = key0 + kb * 16 + 4 * lq + r;
+            sv[kb][r] = (key <= qpos && key >= kfirst) ? st[kb][r] : -INFINITY;
+          }
       }
+      // ---- online softmax of the lane's query (its keys are spread over the
+      // lanes n, n+16, n+32, n+48)
+      {
+        float mx = sv[0][0];
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const _Float16* vp = &Vs[(kh * KH + 32 * j + 4 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
-        const half8_t vf = lds_read_tr16x8(vp, vp + 16 * LV);
-        oacc[b] = mfma16(vf, ph, oacc[b]);
-        oacc[b] = mfma16(vf, pl, oacc[b]);
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
+        mx = rows4_max(mx);
+        const float mnew = fmaxf(mrow, mx);
+        // a query with no visible key so far (a sliding window that starts in a
+        // later tile, or a key half beyond the query) keeps mnew = -inf:
+        // subtract 0 instead, so its weights are exp(-inf) = 0 rather than NaN
+        const float mref = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(mrow - mref);  // 0 while mrow = -inf
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(sv[kb][r] - mref);
+            ps += pr;
+            sv[kb][r] = pr;
+          }
+        ps = rows4_sum(ps);
+        lrow = lrow * alpha + ps;
+        mrow = mnew;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[b][r] *= alpha;
+      }
+      // ---- O^T += V^T P^T over this wave's keys, 32 keys per MFMA. A k-step
+      // pairs key blocks 2j and 2j+1: lane (lq, n) holds P^T for keys
+      // 32j + 4lq + (0..3) and 32j + 16 + 4lq + (0..3) of query n, and reads V^T
+      // for the same 8 keys of dim 16b + n with two transposing reads (lane
+      // (lq, n) addressing key row +4lq + n/4 at dims 16b + 4(n%4) .. +3), so
+      // both operands enumerate k in the same order. P (value scale folded in)
+      // enters as an fp16 high part and the fp16 rounding of the remainder: the
+      // two MFMAs apply it with about 22 significant bits instead of 11. (INT8:
+      // a weight near 1 is then the fp16 scale itself, held exactly; weights
+      // far below it fall into fp16's subnormal range and keep fewer bits, on
+      // terms that carry little of O.)
+#pragma unroll
+      for (int j = 0; j < PS; ++j) {
+        half8_t ph, pl;
+#pragma unroll
+        for (int hblk = 0; hblk < 2; ++hblk) {
+          const int kb = 2 * j + hblk;
+          const float4_t vs = I8 ? *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq])
+                                 : (float4_t){1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = I8 ? sv[kb][r] * vs[r] : sv[kb][r];
+            const _Float16 hi = (_Float16)x;
+            ph[4 * hblk + r] = hi;
+            pl[4 * hblk + r] = (_Float16)(x - (float)hi);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const _Float16* vp = &Vs[(kh * KH + 32 * j + 4 * lq + (l16 >> 2)) * LV + b * 16 + 4 * (l16 & 3)];
+          const half8_t vf = lds_read_tr16x8(vp, vp + 16 * LV);
+          oacc[b] = mfma16(vf, ph, oacc[b]);
+          oacc[b] = mfma16(vf, pl, oacc[b]);
+        }
       }
     }
     attn_lds_barrier();  // every wave is done with this K/V tile before the next is written
@@ -346,13 +372,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
   attn_lds_barrier();
   if (kh == 1) return;
   const float* src = mb + (size_t)(qg * 64 + ln) * RW;
-  // ---- normalise and store query q0 + 16*qg + n, dims 16b + 4lq .. +3
+  // ---- normalise and store query r0 + n, dims 16b + 4lq .. +3
   const float m2 = src[0], l2 = src[1];
   const float m = fmaxf(mrow, m2);
   const float mref = m == -INFINITY ? 0.f : m;
   const float a1 = __builtin_amdgcn_exp2f(mrow - mref), a2 = __builtin_amdgcn_exp2f(m2 - mref);
   const float inv = 1.0f / (lrow * a1 + l2 * a2);
-  const int qr = q0 + 16 * qg + l16;
+  const int qr = r0 + l16;
   if (qr >= M) return;
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
@@ -607,7 +633,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int M, int lane, int p0, const
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  const dim3 grid((M + 63) / 64 * kv.H);
+  const dim3 grid(attn_prefill_blocks(M, kv.window == 0) * kv.H);
   if (kv.hd == 128 && kv.int8)
     launch(attn_prefill_kernel<128, true>, grid, dim3(kAttnThreads), 0, s, q, M, lane, p0, kv, layer, o);
   else if (kv.hd == 128)

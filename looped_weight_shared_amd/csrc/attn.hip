@@ -26,6 +26,8 @@
 
 namespace tl {
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
 // Workgroups go to the 8 XCDs round-robin by linear index and each XCD has
 // its own L2. Renumbering block b of an n-block grid so that the blocks one
 // XCD receives are consecutive indices lets a (head, query tile) grid put
@@ -338,11 +340,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(const uint16
           const float4_t vs = I8 ? *reinterpret_cast<const float4_t*>(&vsc[kh * KH + kb * 16 + 4 * lq])
                                  : (float4_t){1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = I8 ? sv[kb][r] * vs[r] : sv[kb][r];
-            const _Float16 hi = (_Float16)x;
-            ph[4 * hblk + r] = hi;
-            pl[4 * hblk + r] = (_Float16)(x - (float)hi);
+          for (int r = 0; r < 4; r += 2) {  // pairs: one packed conversion per part
+            float2_t x = {sv[kb][r], sv[kb][r + 1]};
+            if constexpr (I8) x *= (float2_t){vs[r], vs[r + 1]};
+            const half2_t hi = __builtin_convertvector(x, half2_t);
+            const half2_t lo = __builtin_convertvector(x - __builtin_convertvector(hi, float2_t), half2_t);
+            ph[4 * hblk + r] = hi[0];
+            ph[4 * hblk + r + 1] = hi[1];
+            pl[4 * hblk + r] = lo[0];
+            pl[4 * hblk + r + 1] = lo[1];
           }
         }
 #pragma unroll
@@ -550,12 +556,15 @@ __global__ __launch_bounds__(256) void attn_prefill_short_kernel(const uint16_t*
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sv[kb][r];
-          if constexpr (I8) x *= h2f((uint16_t)vsr[4 * kb + r]);
-          const _Float16 hi = (_Float16)x;
-          ph[4 * kb + r] = hi;
-          pl[4 * kb + r] = (_Float16)(x - (float)hi);
+        for (int r = 0; r < 4; r += 2) {  // pairs: one packed conversion per part
+          float2_t x = {sv[kb][r], sv[kb][r + 1]};
+          if constexpr (I8) x *= (float2_t){h2f((uint16_t)vsr[4 * kb + r]), h2f((uint16_t)vsr[4 * kb + r + 1])};
+          const half2_t hi = __builtin_convertvector(x, half2_t);
+          const half2_t lo = __builtin_convertvector(x - __builtin_convertvector(hi, float2_t), half2_t);
+          ph[4 * kb + r] = hi[0];
+          ph[4 * kb + r + 1] = hi[1];
+          pl[4 * kb + r] = lo[0];
+          pl[4 * kb + r + 1] = lo[1];
         }
 #pragma unroll
       for (int b = 0; b < DB; ++b) {

@@ -22,7 +22,10 @@ Also reported (same JSON line):
               (FP16 and INT8 h), the FP16-body comparator, the empty-kernel
               dispatch floor, and the other 407M workloads (prefill seq 1024
               at L = 16 / 32; INT8-KV decode at context 2048, one lane and
-              three lanes at L = 4 / 16 / 32), each skippable (--no-*).
+              three lanes at L = 4 / 16 / 32), and the page's two comparison
+              tables at L = 8 (W4 against FP16-body prefill at seq 128-1024;
+              FP16 against INT8 KV decode at context 256 / 1024 / 2048), each
+              skippable (--no-*).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Profiling helpers (no timed step): --pmc-kernels (single-kernel launches for
@@ -297,6 +300,82 @@ def other_configs(s, w, tl, Model, torch, synth, stream, only=None):
         print(f"[bench] {name}: {ms:.4f} ms/step ({roof_us / (ms * 1e3):.1%} of the HBM roofline)",
               file=sys.stderr, flush=True)
         mi.close()
+    return res
+
+
+def pages_tables(s, w, tl, Model, torch, synth, stream):
+    """The two comparisons the "Performance and Memory" page tabulates, at
+    L = 8 on the 407M shape: (1) prefill of the INT4 loop block against the
+    FP16 body (block weights dequantized once to fp16) at seq 128, 256, 512
+    and 1024, no logits ("FP16 body cache" table); (2) cached decode with an
+    FP16 KV cache against INT8 KV at contexts 256, 1024 and 2048 ("KV cache
+    INT8" table): a prompt of N - 32 tokens, then 32 timed greedy steps up to
+    context N. Synthetic weights and ids; the pages' rows are H100 numbers
+    of a trained checkpoint, context only."""
+    res = {"prefill_w4_vs_fp16_body_L8": {}, "decode_fp16_vs_int8_kv_L8": {}}
+    L = 8
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    mods = {body: Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=tl.TL_KV_FP16, max_tokens=1024,
+                        fp16_body=(body == "fp16_body")) for body in ("w4", "fp16_body")}
+    for mx in mods.values():
+        mx.set_loops(0, L)
+    for n in (128, 256, 512, 1024):
+        toks = torch.from_numpy(synth.make_tokens(s.vocab, n, seed=0)).cuda()
+        row = {}
+        for body, mx in mods.items():
+            def step():
+                mx.reset(0)
+                mx.prefill(toks)
+            for _ in range(2):
+                step()
+            ms = timed(step, 5)
+            row[f"{body}_ms"] = round(ms, 4)
+            row[f"{body}_tok_s"] = round(n / ms * 1e3, 1)
+        row["w4_speedup_over_fp16_body"] = round(row["fp16_body_ms"] / row["w4_ms"], 3)
+        res["prefill_w4_vs_fp16_body_L8"][f"seq{n}"] = row
+        print(f"[bench] prefill seq {n} L=8: W4 {row['w4_ms']:.3f} ms, FP16 body {row['fp16_body_ms']:.3f} ms",
+              file=sys.stderr, flush=True)
+    for mx in mods.values():
+        mx.close()
+
+    D = 32
+    for kvname, kvd in (("fp16", tl.TL_KV_FP16), ("int8", tl.TL_KV_INT8)):
+        mk = Model(w, max_seq=2048, max_loops=L, n_lanes=1, kv_dtype=kvd, max_tokens=2048 - D)
+        mk.set_loops(0, L)
+        bufs = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+        for n in (256, 1024, 2048):
+            pt = torch.from_numpy(synth.make_tokens(s.vocab, n - D, seed=0)).cuda()
+
+            def prime():
+                mk.reset(0)
+                mk.prefill(pt, next_tok=bufs[0])
+            prime()
+            for t in range(4):
+                mk.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            prime()
+            it = iter(range(D))
+
+            def dstep():
+                t = next(it)
+                mk.decode_step(bufs[t % 2], next_tok=bufs[(t + 1) % 2])
+            ms = timed(dstep, D)
+            res["decode_fp16_vs_int8_kv_L8"].setdefault(f"ctx{n}", {})[f"{kvname}_kv_ms_per_token"] = round(ms, 4)
+        mk.close()
+    for n in (256, 1024, 2048):
+        row = res["decode_fp16_vs_int8_kv_L8"][f"ctx{n}"]
+        row["int8_over_fp16"] = round(row["int8_kv_ms_per_token"] / row["fp16_kv_ms_per_token"], 3)
+        print(f"[bench] decode to context {n} L=8: FP16 KV {row['fp16_kv_ms_per_token']:.4f}, "
+              f"INT8 KV {row['int8_kv_ms_per_token']:.4f} ms/token", file=sys.stderr, flush=True)
     return res
 
 
@@ -589,6 +668,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other 407M workloads (seq-1024 prefill at L=16/32; INT8 KV decode at "
                          "context 2048, one lane at L=8 and three lanes at L=4/16/32)")
+    ap.add_argument("--no-tables", action="store_true",
+                    help="skip the pages' comparison tables (W4 vs FP16-body prefill at seq 128-1024; FP16 vs "
+                         "INT8 KV decode at context 256/1024/2048)")
     ap.add_argument("--configs", metavar="NAMES",
                     help="comma-separated subset of the other workloads (prefill_seq1024_L16, prefill_seq1024_L32, "
                          "decode_int8_ctx2048_L8, decode_int8_ctx2048_3lanes_L4_16_32)")
@@ -906,6 +988,9 @@ def main():
     if not args.no_configs:
         out["other_configs"] = other_configs(s, w, tl, Model, torch, synth, stream,
                                              args.configs.split(",") if args.configs else None)
+
+    if not args.no_tables:
+        out["pages_tables"] = pages_tables(s, w, tl, Model, torch, synth, stream)
 
     # ---------------------------------------------------------------- decode roofline
     # headline: the four loop-block GEMVs with cold weights (kernel leg), their

@@ -707,7 +707,7 @@ def main():
         summarize_pmc(args.summarize_pmc, args.trace_until, args.trace_since)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
               "multi-GPU path; the forward pass would shard across GPUs by lanes (data parallel).",
               file=sys.stderr)
         sys.exit(2)

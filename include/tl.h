@@ -50,7 +50,7 @@ typedef enum {
   TL_E_RANGE = 2,        /* L, token count or sequence length out of range */
   TL_E_STATE = 3,        /* call not valid in the lane's current state */
   TL_E_HIP = 4,          /* a HIP runtime call failed */
-  TL_E_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  TL_E_UNSUPPORTED = 5,  /* valid request the library does not implement */
   TL_E_SAFETY = 6        /* the residual-norm safety check tripped (tl_set_safety) */
 } tl_status;
 

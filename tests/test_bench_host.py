@@ -103,3 +103,15 @@ def test_gemv_a16_template_follows_the_library_dispatch():
     assert t(6144) == "w4_gemv_kernel<1, 0, 1, 6, 2, false>"    # 48 groups: the last with 6
     assert t(6272) == "w4_gemv_kernel<1, 0, 1, 8, 2, false>"    # 49 groups
     assert t(704) == "w4_gemv_kernel<1, 0, 1, 2, 1, false>"     # tiny shape's down projection
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU; asked for more it says so and exits 2
+    before touching a device (this host has none)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""

@@ -51,21 +51,40 @@ PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
-def _ensure_built():
-    """Builds libtl.so when it is missing or older than its sources."""
+def _build_mod():
+    """looped_weight_shared_amd/build.py, loaded without importing the package."""
     spec = importlib.util.spec_from_file_location(
         "_tl_build", os.path.join(ROOT, "looped_weight_shared_amd", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    mod.ensure_current()
+    return mod
+
+
+def _ensure_built():
+    """Builds libtl.so when it is missing or older than its sources."""
+    _build_mod().ensure_current()
 
 
 def _src_hash(*names):
+    """Hash of the named kernel sources and of the per-source compiler flags
+    they are built with (a counter entry is only current for both)."""
+    dev_flags = _build_mod().DEVICE_FLAGS
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "looped_weight_shared_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        if n in dev_flags:
+            h.update(" ".join(dev_flags[n]).encode())
     return h.hexdigest()[:16]
+
+
+GEMM_SRC = ["w4mm.hip", "w4_epi.h", "tl_device.h"]
+GEMV_SRC = ["w4gemv.hip", "w4_epi.h", "tl_device.h"]
+
+
+def _kernel_src(kernel_key):
+    """The sources a counter entry was taken on: the prefill GEMM's or the decode GEMV's."""
+    return GEMV_SRC if kernel_key.startswith("gemv") else GEMM_SRC
 
 
 def _traffic(kernel_key, src_files, launches_bytes_expected=None):
@@ -84,7 +103,7 @@ def _traffic(kernel_key, src_files, launches_bytes_expected=None):
 
 def _traffic_sum(keys):
     """Sum of the counters' bytes per launch over several kernels (None unless all are current)."""
-    v = [_traffic(k, ["w4mm.hip", "tl_device.h"]) for k in keys]
+    v = [_traffic(k, GEMV_SRC) for k in keys]
     return None if any(x is None for x in v) else sum(v)
 
 
@@ -187,7 +206,7 @@ def _ingest_runs(fetch_dir, write_dir, copy_bytes, kernels):
         wb, nw = pick(write, pred)
         if fb is None or wb is None:
             continue
-        data[key] = {"source_hash": _src_hash("w4mm.hip", "tl_device.h"),
+        data[key] = {"source_hash": _src_hash(*_kernel_src(key)),
                      "bytes_per_launch": round(fb * kf + wb * kw),
                      "fetch_bytes_per_launch": round(fb * kf), "write_bytes_per_launch": round(wb * kw),
                      "algorithmic_bytes_per_launch": algo, "dispatches": [nf, nw],
@@ -770,7 +789,7 @@ def main():
     achieved = flops[dom] / (avg_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                "traffic": _traffic("gemm_" + dom, ["w4mm.hip", "tl_device.h"]),
+                "traffic": _traffic("gemm_" + dom, GEMM_SRC),
                 "kernel": f"w4_gemm_kernel ({dom}: M={SEQ} N={2 * f if dom == 'gate_up' else (3 * d if dom == 'qkv' else d)} "
                           f"K={f if dom == 'down' else d})",
                 "flop_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3)}
@@ -844,7 +863,7 @@ def main():
         dk = "gate_up"
         rd = {"bound": "hbm", "achieved": round(gb[dk], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(gb[dk] / PEAK_HBM_GBS, 4),
-              "traffic": _traffic("gemv_" + dk, ["w4mm.hip", "tl_device.h"]),
+              "traffic": _traffic("gemv_" + dk, GEMV_SRC),
               "kernel": "w4_gemv_kernel (gate_up: M=1 N=11264 K=2048)",
               "bytes_per_launch": wbytes[dk], "avg_launch_us": round(kern_dec[dk][1], 3),
               "note": "weights of the loop block are re-read every iteration; iterations after the "

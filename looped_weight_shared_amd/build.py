@@ -26,6 +26,11 @@ ARCH = "gfx950"
 # Packed-FP32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
+# Per-source device-only flags. The decode GEMV takes LLVM's memory-clause
+# machine scheduler (same instructions, reordered so each wave's weight
+# requests leave together): decode steps measured 1.1-1.5% faster with it,
+# while the prefill GEMM measured slower under it and keeps the default.
+DEVICE_FLAGS = {"w4gemv.hip": ["-Xarch_device", "-mllvm=-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def _run(cmd):
@@ -49,6 +54,8 @@ def source_hash() -> str:
     # that a copy of the tree at another path keeps the same stamp
     flags = [f.replace(ROOT, ".") for f in FLAGS]
     h.update(" ".join([ARCH] + flags).encode())
+    for name in sorted(DEVICE_FLAGS):
+        h.update((name + ":" + " ".join(DEVICE_FLAGS[name])).encode())
     return h.hexdigest()
 
 
@@ -74,7 +81,7 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        results = list(ex.map(lambda so: _run([HIPCC, *FLAGS, *DEVICE_FLAGS.get(os.path.basename(so[0]), []), "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
     for (rc, out), src in zip(results, srcs):
         if verbose and out.strip():
             print(out)

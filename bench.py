@@ -123,13 +123,13 @@ def _pmc_dispatches(d, counter):
 def ingest_pmc(fetch_dir, write_dir, copy_mib, kfetch_dir=None, kwrite_dir=None):
     """Writes profiles/traffic.json from two rocprofv3 --pmc runs of
     `bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --no-configs
-    --decode-steps 4 --copy-mib <copy_mib>`, one with FETCH_SIZE, one with WRITE_SIZE (KiB per
+    --no-tables --decode-steps 4 --copy-mib <copy_mib>`, one with FETCH_SIZE, one with WRITE_SIZE (KiB per
     dispatch), and optionally two of `bench.py --pmc-kernels` (the cold M = 1 GEMVs). Each counter
     is scaled by what it reads for the plain device copy of copy_mib MiB in the same run."""
     copy_bytes = copy_mib * 2**20
     data = _ingest_runs(fetch_dir, write_dir, copy_bytes, _forward_kernels())
     run = ("bench.py --steps 3 --warmup 1 --no-cpu --no-spec --no-storeh --no-fp16body --no-kernels --no-configs "
-           "--decode-steps 4 --copy-mib %d" % copy_mib)
+           "--no-tables --decode-steps 4 --copy-mib %d" % copy_mib)
     cmds = ["export TMPDIR=/tmp; timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -d %s -o run -f csv -- python -u %s"
             % (fetch_dir, run),
             "export TMPDIR=/tmp; timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -d %s -o run -f csv -- python -u %s"
